@@ -1,0 +1,122 @@
+"""Plain float64 CPU oracle for the Video Delta Attention (VDA) forward pass.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or run
+this module: only the tests, the smoke check and the benchmark's CPU-baseline
+leg use it, to decide whether the GPU library is right and to time a baseline.
+It shares no code with the GPU library.
+
+What it computes (sources: the VDN-MiniMax-H3 pages -- the aiezz page, section 03
+"technical principles", bullets "Video Delta Attention" and "dual text injection";
+the laicaila page, section "technical principles", the same two bullets; the
+comfyui-wiki page, section "how Video DeltaNet speeds up H3"; the model card's
+introduction, bullet "hybrid architecture"):
+
+* The linear branch keeps a recurrent state per head.  Per frame, all spatial
+  tokens of that frame update the state together through the normal equations of
+  a least-squares problem -- the frame-wise form of the token-wise delta rule.
+  The pages give no formula.  The reading taken here is the regularised
+  frame-level least squares
+
+      X_f = argmin_X ||K_f X - V_f||_F^2 + lam ||X - X_prev||_F^2
+          = (lam I + K_f^T K_f)^{-1} (lam X_prev + K_f^T V_f),
+
+  with the state stored as X = S^T (d x dv), keys K_f (n x d), values V_f (n x dv).
+* The text is written once into the state, at initialisation: the same update
+  applied to a zero state with all T text tokens as one "frame".
+* The state is bidirectional: a forward scan over frames 1..F and a backward scan
+  over F..1, both starting from the text state.
+* Each frame reads the state out with its queries.  Reading: inclusive states
+  (after frame f's own update) and the mean of the two directions,
+  O_f = Q_f (X_fwd_f + X_bwd_f) / 2.
+* No feature map, no 1/sqrt(d) scaling, no decay and no gate inside the op.
+
+Every function works on float64 arrays and uses library linear algebra
+(``numpy.linalg.solve``) for the solves, with no blocking or reordering beyond
+the definition above.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "frame_statistics", "normal_equation_update", "text_state", "scan_from",
+    "head_states", "readout", "vda_forward_head", "vda_forward",
+]
+
+
+def frame_statistics(K_f: np.ndarray, V_f: np.ndarray):
+    """Normal-equation statistics of one frame: G = K_f^T K_f (d x d), B = K_f^T V_f (d x dv).
+    All tokens of the frame enter together (the frame-wise joint solve of the
+    "Video Delta Attention" bullet)."""
+    K_f = np.asarray(K_f, dtype=np.float64)
+    V_f = np.asarray(V_f, dtype=np.float64)
+    return K_f.T @ K_f, K_f.T @ V_f
+
+
+def normal_equation_update(X_prev: np.ndarray, K_f: np.ndarray, V_f: np.ndarray, lam: float):
+    """One frame of the state update: solve (lam I + K_f^T K_f) X = lam X_prev + K_f^T V_f."""
+    if not lam > 0:
+        raise ValueError("lam must be > 0")
+    G, Bm = frame_statistics(K_f, V_f)
+    d = G.shape[0]
+    A = lam * np.eye(d) + G
+    R = lam * np.asarray(X_prev, dtype=np.float64) + Bm
+    return np.linalg.solve(A, R)
+
+
+def text_state(text_k: np.ndarray, text_v: np.ndarray, lam: float, d: int, dv: int):
+    """The text written once into the state: the update applied to a zero state, with
+    all text tokens as one frame ("dual text injection" bullet).  T = 0 gives zero."""
+    text_k = np.asarray(text_k, dtype=np.float64).reshape(-1, d)
+    text_v = np.asarray(text_v, dtype=np.float64).reshape(-1, dv)
+    return normal_equation_update(np.zeros((d, dv)), text_k, text_v, lam)
+
+
+def scan_from(X0: np.ndarray, K: np.ndarray, V: np.ndarray, lam: float):
+    """Run the recurrence over frames in the order given.  K: [F,n,d], V: [F,n,dv].
+    Returns the inclusive states [F,d,dv]: entry i is the state after frame i."""
+    X = np.asarray(X0, dtype=np.float64)
+    out = np.empty((K.shape[0],) + X.shape)
+    for i in range(K.shape[0]):
+        X = normal_equation_update(X, K[i], V[i], lam)
+        out[i] = X
+    return out
+
+
+def head_states(k, v, text_k, text_v, lam):
+    """Text state and both directional state sequences of one head.
+    Returns (X_text [d,dv], X_fwd [F,d,dv], X_bwd [F,d,dv]); X_bwd[f] is the backward
+    state after frame f (the backward scan runs f = F-1 .. 0)."""
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    d, dv = k.shape[-1], v.shape[-1]
+    X_text = text_state(text_k, text_v, lam, d, dv)
+    X_fwd = scan_from(X_text, k, v, lam)
+    X_bwd = scan_from(X_text, k[::-1], v[::-1], lam)[::-1]
+    return X_text, X_fwd, X_bwd
+
+
+def readout(q, X_fwd, X_bwd):
+    """O_f = Q_f (X_fwd_f + X_bwd_f) / 2 for every frame.  q: [F,n,d] -> [F,n,dv]."""
+    q = np.asarray(q, dtype=np.float64)
+    W = 0.5 * (X_fwd + X_bwd)
+    return np.stack([q[f] @ W[f] for f in range(q.shape[0])]) if q.shape[0] else \
+        np.zeros((0, q.shape[1], X_fwd.shape[-1]))
+
+
+def vda_forward_head(q, k, v, text_k, text_v, lam):
+    """VDA forward for one (batch, head): q,k [F,n,d], v [F,n,dv], text_k [T,d], text_v [T,dv]."""
+    _, X_fwd, X_bwd = head_states(k, v, text_k, text_v, lam)
+    return readout(q, X_fwd, X_bwd)
+
+
+def vda_forward(q, k, v, text_k, text_v, lam):
+    """VDA forward over [B,H,...] arrays; heads and batch entries are independent.
+    Returns out [B,H,F,n,dv] in float64."""
+    q = np.asarray(q, dtype=np.float64)
+    Bsz, H = q.shape[:2]
+    out = np.empty(q.shape[:-1] + (np.asarray(v).shape[-1],))
+    for b in range(Bsz):
+        for h in range(H):
+            out[b, h] = vda_forward_head(q[b, h], k[b, h], v[b, h], text_k[b, h], text_v[b, h], lam)
+    return out

@@ -1,0 +1,350 @@
+"""Pins of the float64 oracle against facts other than itself (CPU only).
+
+Each pin ties the oracle to something it does not compute the same way: values
+worked by hand, a different least-squares route (QR/SVD via lstsq), the textbook
+token-wise delta rule, the contraction bound, fixed points, limits, symmetries.
+``test_mutants_are_caught`` plants plausible mistakes into the oracle (on the
+CPU) and checks that at least one pin fails for each.
+"""
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import vda_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+RTOL = 1e-10
+
+
+def _load_golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        g = json.load(f)
+    conv = lambda a: np.vectorize(lambda s: float(Fraction(s)))(np.array(a, dtype=object)).astype(np.float64)
+    out = {k: conv(g[k]) for k in ("text_k", "text_v", "k", "v", "q", "x_text", "x_fwd", "x_bwd", "out")}
+    out["lam"] = float(Fraction(g["lam"]))
+    return out
+
+
+def _rand(rng, *shape):
+    return rng.standard_normal(shape)
+
+
+def _rownorm(x):
+    return x / np.linalg.norm(x, axis=-1, keepdims=True)
+
+
+def _tiny_head(seed=0, F=4, n=5, d=3, dv=2, T=3):
+    rng = np.random.default_rng(seed)
+    return dict(q=_rand(rng, F, n, d), k=_rownorm(_rand(rng, F, n, d)), v=_rand(rng, F, n, dv),
+                text_k=_rownorm(_rand(rng, T, d)), text_v=_rand(rng, T, dv))
+
+
+# ---------------------------------------------------------------------------
+# pin predicates (return True when the pin holds) -- reused by the mutant test
+# ---------------------------------------------------------------------------
+
+def pin_golden():
+    ok = True
+    for name in ("scalar_two_frames_lam1.json", "scalar_two_frames_lam_half.json"):
+        g = _load_golden(name)
+        xt, xf, xb = oracle.head_states(g["k"], g["v"], g["text_k"], g["text_v"], g["lam"])
+        out = oracle.vda_forward_head(g["q"], g["k"], g["v"], g["text_k"], g["text_v"], g["lam"])
+        ok &= np.allclose(xt, g["x_text"], rtol=RTOL, atol=1e-14)
+        ok &= np.allclose(xf, g["x_fwd"], rtol=RTOL, atol=1e-14)
+        ok &= np.allclose(xb, g["x_bwd"], rtol=RTOL, atol=1e-14)
+        ok &= out.shape == g["out"].shape and np.allclose(out, g["out"], rtol=RTOL, atol=1e-14)
+    return bool(ok)
+
+
+def _stacked_lstsq_step(X_prev, K_f, V_f, lam):
+    """The least-squares problem min ||K X - V||^2 + lam ||X - X_prev||^2 solved by QR/SVD
+    on the stacked system [K; sqrt(lam) I] X = [V; sqrt(lam) X_prev] -- no normal equations."""
+    d = K_f.shape[1]
+    A = np.vstack([K_f, np.sqrt(lam) * np.eye(d)])
+    R = np.vstack([V_f, np.sqrt(lam) * X_prev])
+    return np.linalg.lstsq(A, R, rcond=None)[0]
+
+
+def pin_lstsq(seed=1, lam=0.7, n=5, d=3, dv=2, F=4, T=3):
+    h = _tiny_head(seed, F=F, n=n, d=d, dv=dv, T=T)
+    xt, xf, xb = oracle.head_states(h["k"], h["v"], h["text_k"], h["text_v"], lam)
+    ref_t = _stacked_lstsq_step(np.zeros((d, dv)), h["text_k"], h["text_v"], lam)
+    ok = np.allclose(xt, ref_t, rtol=1e-9, atol=1e-12)
+    x = ref_t
+    for f in range(F):
+        x = _stacked_lstsq_step(x, h["k"][f], h["v"][f], lam)
+        ok &= np.allclose(xf[f], x, rtol=1e-9, atol=1e-12)
+    x = ref_t
+    for f in reversed(range(F)):
+        x = _stacked_lstsq_step(x, h["k"][f], h["v"][f], lam)
+        ok &= np.allclose(xb[f], x, rtol=1e-9, atol=1e-12)
+    out = oracle.vda_forward_head(h["q"], h["k"], h["v"], h["text_k"], h["text_v"], lam)
+    ok &= np.allclose(out, np.stack([h["q"][f] @ (0.5 * (xf[f] + xb[f])) for f in range(F)]),
+                      rtol=1e-12, atol=1e-13)
+    return bool(ok)
+
+
+def _delta_rule(tokens_k, tokens_v, lam, d, dv):
+    """Textbook token-wise delta rule (DeltaNet, Schlag et al. 2021) with step size
+    beta = 1/(lam + ||k||^2), from a zero state: X <- X + beta k^T (v - k X)."""
+    X = np.zeros((d, dv))
+    states = []
+    for kt, vt in zip(tokens_k, tokens_v):
+        beta = 1.0 / (lam + kt @ kt)
+        X = X + beta * np.outer(kt, vt - kt @ X)
+        states.append(X.copy())
+    return states
+
+
+def pin_delta_rule(seed=2, lam=0.6, F=5, d=4, dv=3):
+    h = _tiny_head(seed, F=F, n=1, d=d, dv=dv, T=1)
+    xt, xf, xb = oracle.head_states(h["k"], h["v"], h["text_k"], h["text_v"], lam)
+    fwd_k = [h["text_k"][0]] + [h["k"][f, 0] for f in range(F)]
+    fwd_v = [h["text_v"][0]] + [h["v"][f, 0] for f in range(F)]
+    s = _delta_rule(fwd_k, fwd_v, lam, d, dv)
+    ok = np.allclose(xt, s[0], rtol=1e-10, atol=1e-13)
+    ok &= np.allclose(xf, np.stack(s[1:]), rtol=1e-10, atol=1e-13)
+    bwd_k = [h["text_k"][0]] + [h["k"][f, 0] for f in reversed(range(F))]
+    bwd_v = [h["text_v"][0]] + [h["v"][f, 0] for f in reversed(range(F))]
+    s = _delta_rule(bwd_k, bwd_v, lam, d, dv)
+    ok &= np.allclose(xb, np.stack(s[1:][::-1]), rtol=1e-10, atol=1e-13)
+    return bool(ok)
+
+
+def pin_fixed_point(seed=3, lam=0.3, F=4, n=6, d=3, dv=2):
+    rng = np.random.default_rng(seed)
+    M = _rand(rng, dv, d)
+    K = _rownorm(_rand(rng, F, n, d))
+    V = K @ M.T
+    xs = oracle.scan_from(M.T, K, V, lam)
+    return bool(np.allclose(xs, np.broadcast_to(M.T, xs.shape), rtol=1e-11, atol=1e-12))
+
+
+PINS = [pin_golden, pin_lstsq, lambda: pin_lstsq(seed=4, n=6, d=3, dv=3), pin_delta_rule,
+        pin_fixed_point]
+
+
+# ---------------------------------------------------------------------------
+# tests
+# ---------------------------------------------------------------------------
+
+def test_golden_scalar_cases():
+    assert pin_golden()
+
+
+@pytest.mark.parametrize("shape", [dict(n=5, d=3, dv=2), dict(n=2, d=4, dv=3), dict(n=7, d=2, dv=5)])
+def test_every_step_is_the_stacked_least_squares_solution(shape):
+    assert pin_lstsq(**shape)
+
+
+def test_n1_reduces_to_token_delta_rule():
+    assert pin_delta_rule()
+
+
+def test_fixed_point_state_is_kept():
+    assert pin_fixed_point()
+
+
+def test_fixed_point_readout_and_text_start_contracts():
+    rng = np.random.default_rng(4)
+    F, n, d, dv, T, lam = 5, 7, 4, 3, 5, 0.2
+    M = _rand(rng, dv, d)
+    K = _rownorm(_rand(rng, F, n, d))
+    Q = _rand(rng, F, n, d)
+    tk = _rownorm(_rand(rng, T, d))
+    xt, xf, xb = oracle.head_states(K, K @ M.T, tk, tk @ M.T, lam)
+    # start at the text state, which differs from M^T; the gap never grows
+    gaps = [np.linalg.norm(xt - M.T)] + [np.linalg.norm(xf[f] - M.T) for f in range(F)]
+    assert all(b <= a * (1 + 1e-12) for a, b in zip(gaps, gaps[1:]))
+    gaps = [np.linalg.norm(xt - M.T)] + [np.linalg.norm(xb[f] - M.T) for f in reversed(range(F))]
+    assert all(b <= a * (1 + 1e-12) for a, b in zip(gaps, gaps[1:]))
+    # starting exactly at M^T, the readout is Q M^T
+    xs = oracle.scan_from(M.T, K, K @ M.T, lam)
+    out = oracle.readout(Q, xs, xs)
+    assert np.allclose(out, Q @ M.T, rtol=1e-11, atol=1e-12)
+
+
+def test_non_expansive_with_contraction_bound():
+    rng = np.random.default_rng(5)
+    F, n, d, dv, lam = 6, 5, 4, 3, 0.4
+    K = _rownorm(_rand(rng, F, n, d))
+    V = _rand(rng, F, n, dv)
+    X0, X1 = _rand(rng, d, dv), _rand(rng, d, dv)
+    a, b = oracle.scan_from(X0, K, V, lam), oracle.scan_from(X1, K, V, lam)
+    prev = np.linalg.norm(X0 - X1)
+    for f in range(F):
+        sig_min = np.linalg.eigvalsh(K[f].T @ K[f]).min()
+        cur = np.linalg.norm(a[f] - b[f])
+        assert cur <= prev * lam / (lam + sig_min) * (1 + 1e-10) + 1e-14
+        assert cur <= prev
+        prev = cur
+
+
+def test_small_lambda_gives_per_frame_ols():
+    rng = np.random.default_rng(6)
+    F, n, d, dv = 3, 9, 4, 3
+    K = _rand(rng, F, n, d)
+    V = _rand(rng, F, n, dv)
+    xs = oracle.scan_from(_rand(rng, d, dv), K, V, 1e-10)
+    for f in range(F):
+        ols = np.linalg.lstsq(K[f], V[f], rcond=None)[0]
+        assert np.allclose(xs[f], ols, rtol=1e-6, atol=1e-7)
+
+
+def test_single_frame_closed_form():
+    h = _tiny_head(7, F=1, n=6, d=3, dv=4, T=2)
+    lam = 0.9
+    xt = _stacked_lstsq_step(np.zeros((3, 4)), h["text_k"], h["text_v"], lam)
+    x1 = _stacked_lstsq_step(xt, h["k"][0], h["v"][0], lam)
+    out = oracle.vda_forward_head(h["q"], h["k"], h["v"], h["text_k"], h["text_v"], lam)
+    assert np.allclose(out[0], h["q"][0] @ x1, rtol=1e-10, atol=1e-12)
+
+
+def test_no_text_gives_zero_text_state():
+    h = _tiny_head(8, T=0)
+    xt, _, _ = oracle.head_states(h["k"], h["v"], h["text_k"], h["text_v"], 0.5)
+    assert xt.shape == (3, 2) and np.all(xt == 0)
+
+
+def test_frame_reversal_reverses_outputs():
+    h = _tiny_head(9, F=5)
+    lam = 0.8
+    out = oracle.vda_forward_head(h["q"], h["k"], h["v"], h["text_k"], h["text_v"], lam)
+    rev = oracle.vda_forward_head(h["q"][::-1], h["k"][::-1], h["v"][::-1], h["text_k"], h["text_v"], lam)
+    assert np.allclose(rev, out[::-1], rtol=1e-12, atol=1e-13)
+
+
+def test_token_permutation_within_a_frame():
+    h = _tiny_head(10, F=4, n=6)
+    lam = 0.8
+    out = oracle.vda_forward_head(h["q"], h["k"], h["v"], h["text_k"], h["text_v"], lam)
+    perm = np.random.default_rng(0).permutation(6)
+    q, k, v = h["q"].copy(), h["k"].copy(), h["v"].copy()
+    q[2], k[2], v[2] = q[2][perm], k[2][perm], v[2][perm]
+    out2 = oracle.vda_forward_head(q, k, v, h["text_k"], h["text_v"], lam)
+    exp = out.copy()
+    exp[2] = out[2][perm]
+    assert np.allclose(out2, exp, rtol=1e-11, atol=1e-12)
+
+
+def test_linearity_in_values_and_queries():
+    h = _tiny_head(11)
+    lam = 0.5
+    f = lambda **kw: oracle.vda_forward_head(**{**h, **kw}, lam=lam)
+    base = f()
+    assert np.allclose(f(v=2.5 * h["v"], text_v=2.5 * h["text_v"]), 2.5 * base, rtol=1e-11, atol=1e-12)
+    q2 = np.random.default_rng(1).standard_normal(h["q"].shape)
+    assert np.allclose(f(q=h["q"] + q2) - f(q=q2), base, rtol=1e-10, atol=1e-11)
+
+
+def test_heads_and_batch_are_independent():
+    rng = np.random.default_rng(12)
+    B, H, F, n, d, dv, T = 2, 3, 3, 4, 3, 2, 2
+    q, k, v = _rand(rng, B, H, F, n, d), _rownorm(_rand(rng, B, H, F, n, d)), _rand(rng, B, H, F, n, dv)
+    tk, tv = _rownorm(_rand(rng, B, H, T, d)), _rand(rng, B, H, T, dv)
+    out = oracle.vda_forward(q, k, v, tk, tv, 0.6)
+    for b in range(B):
+        for hh in range(H):
+            ref = oracle.vda_forward_head(q[b, hh], k[b, hh], v[b, hh], tk[b, hh], tv[b, hh], 0.6)
+            assert np.array_equal(out[b, hh], ref)
+    k2 = k.copy()
+    k2[1, 2] = _rownorm(_rand(rng, F, n, d))
+    out2 = oracle.vda_forward(q, k2, v, tk, tv, 0.6)
+    assert np.array_equal(out2[0], out[0]) and np.array_equal(out2[1, :2], out[1, :2])
+
+
+def test_rejects_nonpositive_lambda():
+    h = _tiny_head(13)
+    with pytest.raises(ValueError):
+        oracle.vda_forward_head(**h, lam=0.0)
+
+
+# ---------------------------------------------------------------------------
+# planted mistakes: each must make at least one pin fail
+# ---------------------------------------------------------------------------
+
+def _update_no_lam_on_prev(X_prev, K_f, V_f, lam):
+    G, Bm = O.frame_statistics(K_f, V_f)
+    return np.linalg.solve(lam * np.eye(G.shape[0]) + G, X_prev + Bm)
+
+
+def _update_no_lam_on_identity(X_prev, K_f, V_f, lam):
+    G, Bm = O.frame_statistics(K_f, V_f)
+    return np.linalg.solve(np.eye(G.shape[0]) + G, lam * X_prev + Bm)
+
+
+def _update_sign(X_prev, K_f, V_f, lam):
+    G, Bm = O.frame_statistics(K_f, V_f)
+    return np.linalg.solve(lam * np.eye(G.shape[0]) + G, lam * X_prev - Bm)
+
+
+def _update_n_scaled(X_prev, K_f, V_f, lam):
+    G, Bm = O.frame_statistics(K_f, V_f)
+    n = K_f.shape[0]
+    return np.linalg.solve(lam * np.eye(G.shape[0]) + G / n, lam * X_prev + Bm / n)
+
+
+def _stats_transposed_cross(K_f, V_f):
+    return K_f.T @ K_f, V_f.T @ K_f
+
+
+def _readout_sum(q, X_fwd, X_bwd):
+    return np.stack([q[f] @ (X_fwd[f] + X_bwd[f]) for f in range(q.shape[0])])
+
+
+def _readout_forward_only(q, X_fwd, X_bwd):
+    return np.stack([q[f] @ X_fwd[f] for f in range(q.shape[0])])
+
+
+def _states_bwd_from_zero(k, v, text_k, text_v, lam):
+    d, dv = k.shape[-1], v.shape[-1]
+    X_text = O.text_state(text_k, text_v, lam, d, dv)
+    return X_text, O.scan_from(X_text, k, v, lam), O.scan_from(np.zeros((d, dv)), k[::-1], v[::-1], lam)[::-1]
+
+
+def _states_bwd_not_reversed(k, v, text_k, text_v, lam):
+    d, dv = k.shape[-1], v.shape[-1]
+    X_text = O.text_state(text_k, text_v, lam, d, dv)
+    return X_text, O.scan_from(X_text, k, v, lam), O.scan_from(X_text, k[::-1], v[::-1], lam)
+
+
+def _states_exclusive(k, v, text_k, text_v, lam):
+    d, dv = k.shape[-1], v.shape[-1]
+    X_text = O.text_state(text_k, text_v, lam, d, dv)
+    f = O.scan_from(X_text, k, v, lam)
+    b = O.scan_from(X_text, k[::-1], v[::-1], lam)[::-1]
+    fx = np.concatenate([X_text[None], f[:-1]])
+    bx = np.concatenate([b[1:], X_text[None]])
+    return X_text, fx, bx
+
+
+MUTANTS = {
+    "no_lam_on_prev": ("normal_equation_update", _update_no_lam_on_prev),
+    "no_lam_on_identity": ("normal_equation_update", _update_no_lam_on_identity),
+    "sign_of_cross_term": ("normal_equation_update", _update_sign),
+    "frame_size_scaling": ("normal_equation_update", _update_n_scaled),
+    "cross_term_wrong_operand": ("frame_statistics", _stats_transposed_cross),
+    "readout_without_half": ("readout", _readout_sum),
+    "readout_forward_only": ("readout", _readout_forward_only),
+    "backward_from_zero": ("head_states", _states_bwd_from_zero),
+    "backward_not_reordered": ("head_states", _states_bwd_not_reversed),
+    "exclusive_states": ("head_states", _states_exclusive),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutants_are_caught(name, monkeypatch):
+    attr, fn = MUTANTS[name]
+    monkeypatch.setattr(O, attr, fn)
+    monkeypatch.setattr(oracle, attr, fn, raising=False)
+    results = []
+    for pin in PINS:
+        try:
+            results.append(pin())
+        except Exception:
+            results.append(False)
+    assert not all(results), f"mutant {name} passes every pin"

@@ -1,0 +1,207 @@
+"""Seeded synthetic inputs for the Video Delta Attention (VDA) forward pass.
+
+This module is shared by the oracle side (tests, the CPU baseline) and the GPU
+side (tests, bench).  It holds only the input recipe -- shapes, random draws,
+key normalisation and rounding to the storage type -- and none of the VDA
+arithmetic itself.
+
+Workloads.  The pages measure a 768p, 14.4 s clip (VDN-MiniMax-H3 pages, the
+"performance numbers" table of the agentlenshq project page and the results
+section of the model card).  No dataset, prompt or weight is used: every input
+is Gaussian noise of the shape of that workload, drawn from a seed.
+
+Recipe, per (batch b, head h), from ``Generator(PCG64(SeedSequence((seed, b, h))))``
+with ``seed`` the workload's seed; all draws are float32 in this order:
+
+* gaussian workloads:  q ~ N(0,1) [F,n,d];  k ~ N(0,1) [F,n,d];  v ~ N(0,1) [F,n,dv];
+  text_k ~ N(0,1) [T,d];  text_v ~ N(0,1) [T,dv].
+* low-rank ("ill-conditioned") workloads:  m ~ N(0,1) [dv,d] once per (b,h); then per
+  frame f = 0..F-1 in order: u_f ~ N(0,1) [n,r], w_f ~ N(0,1) [r,d], e_f ~ N(0,1) [n,d],
+  z_f ~ N(0,1) [n,dv], with k_f = rownorm(u_f w_f / sqrt(r) + 0.05 e_f) and
+  v_f = k_f m^T + 0.1 z_f (float32, before any rounding); then q ~ N(0,1) [F,n,d],
+  text_k ~ N(0,1) [T,d], text_v ~ N(0,1) [T,dv].
+
+Every row of k and text_k is scaled to unit L2 norm in float32.  For bfloat16
+workloads every tensor is then rounded to bfloat16 with round-to-nearest-even;
+the oracle receives those rounded values upcast exactly.
+"""
+from __future__ import annotations
+
+import dataclasses
+import os
+from concurrent.futures import ThreadPoolExecutor
+from typing import Dict, Optional
+
+import numpy as np
+
+TENSORS = ("q", "k", "v", "text_k", "text_v")
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    """Shape and recipe of one synthetic VDA input set."""
+    name: str
+    B: int
+    H: int
+    F: int
+    n: int
+    d: int
+    dv: int
+    T: int
+    lam: float
+    dtype: str            # "f32" or "bf16": storage type of q,k,v,text_k,text_v and out
+    seed: int
+    kind: str = "gaussian"  # "gaussian" or "lowrank"
+    rank: int = 16
+    grid: Optional[tuple] = None  # spatial token grid (rows, cols), informational
+
+    @property
+    def video_tokens(self) -> int:
+        return self.B * self.F * self.n
+
+    @property
+    def elem_bytes(self) -> int:
+        return 4 if self.dtype == "f32" else 2
+
+    def shapes(self) -> Dict[str, tuple]:
+        B, H, F, n, d, dv, T = self.B, self.H, self.F, self.n, self.d, self.dv, self.T
+        return {"q": (B, H, F, n, d), "k": (B, H, F, n, d), "v": (B, H, F, n, dv),
+                "text_k": (B, H, T, d), "text_v": (B, H, T, dv), "out": (B, H, F, n, dv)}
+
+    def algorithmic_bytes(self) -> int:
+        """Bytes the method must move: q, k, v, text read once and out written once."""
+        B, H, F, n, d, dv, T = self.B, self.H, self.F, self.n, self.d, self.dv, self.T
+        elems = B * H * (F * n * (2 * d + 2 * dv) + T * (d + dv))
+        return elems * self.elem_bytes
+
+    def replace(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+
+# The five named workloads.  Index = seed.
+WORKLOADS: Dict[int, Workload] = {
+    1: Workload("tiny_fp32", B=1, H=2, F=6, n=64, d=32, dv=32, T=16, lam=1.0,
+                dtype="f32", seed=1, grid=(8, 8)),
+    2: Workload("small_bf16", B=1, H=8, F=24, n=1024, d=64, dv=64, T=64, lam=1.0,
+                dtype="bf16", seed=2, grid=(32, 32)),
+    3: Workload("768p_bf16", B=1, H=24, F=90, n=4032, d=128, dv=128, T=256, lam=1.0,
+                dtype="bf16", seed=3, grid=(84, 48)),
+    4: Workload("long_clip_bf16", B=1, H=24, F=360, n=1024, d=128, dv=128, T=256, lam=1.0,
+                dtype="bf16", seed=4, grid=(32, 32)),
+    5: Workload("ill_conditioned_bf16", B=4, H=16, F=45, n=2016, d=128, dv=128, T=128,
+                lam=0.1, dtype="bf16", seed=5, kind="lowrank", rank=16, grid=(56, 36)),
+}
+
+
+def by_name(name: str) -> Workload:
+    for w in WORKLOADS.values():
+        if w.name == name:
+            return w
+    raise KeyError(name)
+
+
+# ----------------------------------------------------------------------------
+# bfloat16 storage helpers (pure data conversion)
+# ----------------------------------------------------------------------------
+
+def float32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 to bfloat16 (round to nearest, ties to even); return the uint16 bits.
+    Inputs here are finite, so no NaN special case is needed."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    bias = ((u >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
+    return ((u + bias) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_float32(b: np.ndarray) -> np.ndarray:
+    """Exact widening of bfloat16 bits to float32."""
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def _rownorm(x: np.ndarray) -> np.ndarray:
+    nrm = np.sqrt(np.sum(x * x, axis=-1, keepdims=True, dtype=np.float32), dtype=np.float32)
+    return (x / nrm).astype(np.float32)
+
+
+def _rng(w: Workload, b: int, h: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence((w.seed, b, h))))
+
+
+def head_float32(w: Workload, b: int, h: int) -> Dict[str, np.ndarray]:
+    """Draw the float32 tensors of one (b,h) slice, before rounding to storage."""
+    g = _rng(w, b, h)
+    F, n, d, dv, T = w.F, w.n, w.d, w.dv, w.T
+    if w.kind == "gaussian":
+        q = g.standard_normal((F, n, d), dtype=np.float32)
+        k = _rownorm(g.standard_normal((F, n, d), dtype=np.float32))
+        v = g.standard_normal((F, n, dv), dtype=np.float32)
+    elif w.kind == "lowrank":
+        m = g.standard_normal((dv, d), dtype=np.float32)
+        k = np.empty((F, n, d), np.float32)
+        v = np.empty((F, n, dv), np.float32)
+        scale = np.float32(1.0 / np.sqrt(w.rank))
+        for f in range(F):
+            u = g.standard_normal((n, w.rank), dtype=np.float32)
+            wf = g.standard_normal((w.rank, d), dtype=np.float32)
+            e = g.standard_normal((n, d), dtype=np.float32)
+            z = g.standard_normal((n, dv), dtype=np.float32)
+            kf = _rownorm((u @ wf) * scale + np.float32(0.05) * e)
+            k[f] = kf
+            v[f] = kf @ m.T + np.float32(0.1) * z
+        q = g.standard_normal((F, n, d), dtype=np.float32)
+    else:
+        raise ValueError(w.kind)
+    tk = _rownorm(g.standard_normal((T, d), dtype=np.float32)) if T > 0 else np.zeros((0, d), np.float32)
+    tv = g.standard_normal((T, dv), dtype=np.float32)
+    return {"q": q, "k": k, "v": v, "text_k": tk, "text_v": tv}
+
+
+def to_storage(w: Workload, x: np.ndarray) -> np.ndarray:
+    """float32 -> storage array (float32 or uint16 bfloat16 bits)."""
+    if w.dtype == "f32":
+        return np.ascontiguousarray(x, dtype=np.float32)
+    return float32_to_bf16_bits(x)
+
+
+def storage_to_float64(w: Workload, s: np.ndarray) -> np.ndarray:
+    """Storage array -> the exact values as float64 (what the oracle receives)."""
+    if w.dtype == "f32":
+        return np.asarray(s, dtype=np.float32).astype(np.float64)
+    return bf16_bits_to_float32(s).astype(np.float64)
+
+
+def head_storage(w: Workload, b: int, h: int) -> Dict[str, np.ndarray]:
+    """One (b,h) slice in storage form."""
+    return {key: to_storage(w, val) for key, val in head_float32(w, b, h).items()}
+
+
+def head_float64(w: Workload, b: int, h: int) -> Dict[str, np.ndarray]:
+    """One (b,h) slice as the exact float64 values of its stored inputs."""
+    return {key: storage_to_float64(w, val) for key, val in head_storage(w, b, h).items()}
+
+
+def storage_dtype(w: Workload):
+    return np.float32 if w.dtype == "f32" else np.uint16
+
+
+def full_storage(w: Workload, threads: Optional[int] = None) -> Dict[str, np.ndarray]:
+    """All (b,h) slices, in storage form, shaped [B,H,...].  Slices are generated on a
+    thread pool; each slice uses its own generator, so the result does not depend on
+    the number of threads."""
+    shapes = w.shapes()
+    out = {key: np.empty(shapes[key], storage_dtype(w)) for key in TENSORS}
+    if threads is None:
+        threads = min(16, len(os.sched_getaffinity(0)))
+
+    def fill(bh):
+        b, h = bh
+        for key, val in head_storage(w, b, h).items():
+            out[key][b, h] = val
+
+    jobs = [(b, h) for b in range(w.B) for h in range(w.H)]
+    if threads <= 1:
+        for j in jobs:
+            fill(j)
+    else:
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(fill, jobs))
+    return out
