@@ -1,0 +1,315 @@
+// Stage 1 of the VDA forward pass: per-frame normal-equation statistics.
+//
+// For every (batch, head) and every frame f (index 0 = the text tokens, written
+// once into the state at initialisation; 1..F = video frames) this computes
+//   G_f = K_f^T K_f  (d x d),   Bm_f = K_f^T V_f  (d x dv),   Ainv_f = (lam I + G_f)^{-1},
+// the statistics through which all spatial tokens of a frame jointly set the new
+// state (VDN-MiniMax-H3 pages: aiezz section 03 and laicaila "technical
+// principles", bullets "Video Delta Attention" and "dual text injection").
+//
+// One workgroup per (b, h, frame).  K and V stream once through LDS in chunks of
+// 64 tokens; G and Bm accumulate in MFMA registers (fp32).  The reduction runs
+// over tokens, so both MFMA operands need 8 consecutive tokens of one feature per
+// lane: each lane loads an 8-token x 8-feature block with 16-byte loads, transposes
+// it in registers (v_perm_b32) and stores it token-contiguous into LDS, from where
+// fragments are read with 16-byte LDS loads.  After the last chunk, G goes to LDS
+// and is inverted in place (Gauss-Jordan); Bm and Ainv go to the workspace.
+#include "vda_device.h"
+#include "vda_internal.h"
+
+namespace vda {
+namespace {
+
+// ---------------------------------------------------------------- bfloat16 inputs
+template <int D, int DV>
+struct StatsBf16 {
+  static constexpr int TC = 64;                  // tokens per chunk
+  static constexpr int ROW = TC + 8;             // bf16 per LDS row (144 B: conflict-free reads)
+  static constexpr int NK = D / 32, NV = DV / 32, NC = NK + NV;
+  static constexpr int RPW = 4 / NK;             // waves sharing one 32-row block of G
+  static constexpr int CPW = (NC + RPW - 1) / RPW;  // 32x32 output tiles per wave
+  static constexpr int NSEG = (D + DV) / 8;      // 8-feature segments per token (K then V)
+  static constexpr int BUF = (D + DV) * ROW;     // bf16 elements per staging buffer
+  static constexpr int STAGE_BYTES = 2 * BUF * 2;
+  static constexpr int GS = D + 4;               // floats per LDS row of G
+  static constexpr int G_BYTES = D * GS * 4;
+  static constexpr int MAIN_BYTES = cmax(STAGE_BYTES, G_BYTES);
+  static constexpr int LDS_BYTES = MAIN_BYTES + 4 * D * 4;  // + pivot row/col buffers
+};
+
+template <int D, int DV>
+__global__ void __launch_bounds__(kThreads, 2)
+stats_bf16_kernel(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                  const uint16_t* __restrict__ tk, const uint16_t* __restrict__ tv,
+                  float* __restrict__ ainv, float* __restrict__ bm,
+                  int64_t F, int64_t n, int64_t T, float lam) {
+  using C = StatsBf16<D, DV>;
+  extern __shared__ __align__(16) unsigned char smem[];
+  uint16_t* stage = reinterpret_cast<uint16_t*>(smem);
+
+  const int64_t F1 = F + 1;
+  const int64_t fi = blockIdx.x % F1;          // 0 = text, 1..F = frames
+  const int64_t bh = blockIdx.x / F1;
+  const uint16_t* kp;
+  const uint16_t* vp;
+  int64_t ntok;
+  if (fi == 0) {
+    kp = tk + bh * T * D;
+    vp = tv + bh * T * DV;
+    ntok = T;
+  } else {
+    kp = k + ((bh * F + (fi - 1)) * n) * D;
+    vp = v + ((bh * F + (fi - 1)) * n) * DV;
+    ntok = n;
+  }
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // loader role: token group tg (8 tokens), 8-feature segment seg of K (seg < D/8) or V
+  const int tg = tid & 7, seg = tid >> 3;
+  const bool loader = seg < C::NSEG;
+  const bool seg_is_k = seg < D / 8;
+  const uint16_t* src = seg_is_k ? kp + seg * 8 : vp + (seg - D / 8) * 8;
+  const int64_t src_stride = seg_is_k ? D : DV;
+  const int lds_row0 = seg * 8;  // transposed rows 8*seg .. 8*seg+7 (K rows, then V rows)
+
+  // compute role: row block rb of G (and Bm), column tiles c = jj*RPW + cofs
+  const int rb = wave % C::NK;
+  const int cofs = wave / C::NK;
+
+  f32x16 acc[C::CPW];
+#pragma unroll
+  for (int j = 0; j < C::CPW; ++j) acc[j] = f32x16{};
+
+  const int64_t nchunks = (ntok + C::TC - 1) / C::TC;
+  uint4 r[8];
+
+  auto load_chunk = [&](int64_t ch) {
+    const int64_t t0 = ch * C::TC + tg * 8;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      r[i] = make_uint4(0, 0, 0, 0);
+      if (loader && t0 + i < ntok)
+        r[i] = *reinterpret_cast<const uint4*>(src + (t0 + i) * src_stride);
+    }
+  };
+  auto store_chunk = [&](int buf) {
+    if (!loader) return;
+    uint4 c[8];
+    transpose8x8_b16(r, c);
+    uint16_t* dst = stage + buf * C::BUF + lds_row0 * C::ROW + tg * 8;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) *reinterpret_cast<uint4*>(dst + j * C::ROW) = c[j];
+  };
+
+  if (nchunks > 0) {
+    load_chunk(0);
+    store_chunk(0);
+  }
+  __syncthreads();
+  for (int64_t ch = 0; ch < nchunks; ++ch) {
+    const int buf = int(ch & 1);
+    if (ch + 1 < nchunks) load_chunk(ch + 1);
+    const uint16_t* kt = stage + buf * C::BUF;
+    const uint16_t* vt = kt + D * C::ROW;
+#pragma unroll
+    for (int ks = 0; ks < C::TC / 16; ++ks) {
+      const int col = ks * 16 + (lane >> 5) * 8;
+      const uint4 a = *reinterpret_cast<const uint4*>(kt + (rb * 32 + (lane & 31)) * C::ROW + col);
+#pragma unroll
+      for (int jj = 0; jj < C::CPW; ++jj) {
+        const int c = jj * C::RPW + cofs;
+        if (c < C::NC) {
+          const uint16_t* bs = c < C::NK ? kt + (c * 32 + (lane & 31)) * C::ROW
+                                         : vt + ((c - C::NK) * 32 + (lane & 31)) * C::ROW;
+          const uint4 b = *reinterpret_cast<const uint4*>(bs + col);
+          acc[jj] = mfma32_bf16(a, b, acc[jj]);
+        }
+      }
+    }
+    if (ch + 1 < nchunks) store_chunk(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: Bm tiles to the workspace, G tiles to LDS, then invert lam I + G
+  float* gsm = reinterpret_cast<float*>(smem);
+  float* bmo = bm + (bh * F1 + fi) * int64_t(D) * DV;
+#pragma unroll
+  for (int jj = 0; jj < C::CPW; ++jj) {
+    const int c = jj * C::RPW + cofs;
+    if (c >= C::NC) continue;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int row = rb * 32 + mfma32_row(e, lane);
+      if (c < C::NK) {
+        gsm[row * C::GS + c * 32 + (lane & 31)] = acc[jj][e];
+      } else {
+        bmo[int64_t(row) * DV + (c - C::NK) * 32 + (lane & 31)] = acc[jj][e];
+      }
+    }
+  }
+  __syncthreads();
+  float* rowv = reinterpret_cast<float*>(smem + C::MAIN_BYTES);
+  float* colv = rowv + 2 * D;
+  float a[D / 16][D / 16];
+  spd_inverse_gj<D>(gsm, C::GS, lam, rowv, colv, a);
+  constexpr int TS = D / 16;
+  float* ao = ainv + (bh * F1 + fi) * int64_t(D) * D;
+  const int tr = tid >> 4, tcol = tid & 15;
+#pragma unroll
+  for (int i = 0; i < TS; ++i)
+#pragma unroll
+    for (int j = 0; j < TS; ++j) ao[(tr * TS + i) * D + tcol * TS + j] = a[i][j];
+}
+
+// ---------------------------------------------------------------- float32 inputs
+// fp32 operands are one value per lane for the 32x32x2 MFMA, so the chunk is kept
+// row-major (as loaded) and no transpose is needed.
+template <int D, int DV>
+struct StatsF32 {
+  static constexpr int TC = 32;
+  static constexpr int NK = D / 32, NV = DV / 32, NC = NK + NV;
+  static constexpr int RPW = 4 / NK;
+  static constexpr int CPW = (NC + RPW - 1) / RPW;
+  static constexpr int ROWF = D + DV + 4;        // floats per token row in LDS (K then V)
+  static constexpr int STAGE_BYTES = TC * ROWF * 4;
+  static constexpr int GS = D + 4;
+  static constexpr int G_BYTES = D * GS * 4;
+  static constexpr int MAIN_BYTES = cmax(STAGE_BYTES, G_BYTES);
+  static constexpr int LDS_BYTES = MAIN_BYTES + 4 * D * 4;
+};
+
+template <int D, int DV>
+__global__ void __launch_bounds__(kThreads)
+stats_f32_kernel(const float* __restrict__ k, const float* __restrict__ v,
+                 const float* __restrict__ tk, const float* __restrict__ tv,
+                 float* __restrict__ ainv, float* __restrict__ bm,
+                 int64_t F, int64_t n, int64_t T, float lam) {
+  using C = StatsF32<D, DV>;
+  extern __shared__ __align__(16) unsigned char smem[];
+  float* st = reinterpret_cast<float*>(smem);
+
+  const int64_t F1 = F + 1;
+  const int64_t fi = blockIdx.x % F1;
+  const int64_t bh = blockIdx.x / F1;
+  const float* kp;
+  const float* vp;
+  int64_t ntok;
+  if (fi == 0) {
+    kp = tk + bh * T * D;
+    vp = tv + bh * T * DV;
+    ntok = T;
+  } else {
+    kp = k + ((bh * F + (fi - 1)) * n) * D;
+    vp = v + ((bh * F + (fi - 1)) * n) * DV;
+    ntok = n;
+  }
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int rb = wave % C::NK, cofs = wave / C::NK;
+  f32x16 acc[C::CPW];
+#pragma unroll
+  for (int j = 0; j < C::CPW; ++j) acc[j] = f32x16{};
+
+  constexpr int Q = (D + DV) / 4;  // float4 pieces per token
+  for (int64_t t0 = 0; t0 < ntok; t0 += C::TC) {
+    for (int idx = tid; idx < C::TC * Q; idx += kThreads) {
+      const int t = idx / Q, p = idx % Q;
+      float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (t0 + t < ntok) {
+        x = p < D / 4 ? *reinterpret_cast<const float4*>(kp + (t0 + t) * D + 4 * p)
+                      : *reinterpret_cast<const float4*>(vp + (t0 + t) * DV + 4 * (p - D / 4));
+      }
+      *reinterpret_cast<float4*>(st + t * C::ROWF + 4 * p) = x;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < C::TC / 2; ++ks) {
+      const int t = ks * 2 + (lane >> 5);
+      const float a = st[t * C::ROWF + rb * 32 + (lane & 31)];
+#pragma unroll
+      for (int jj = 0; jj < C::CPW; ++jj) {
+        const int c = jj * C::RPW + cofs;
+        if (c < C::NC) {
+          const float b = st[t * C::ROWF + c * 32 + (lane & 31)];
+          acc[jj] = mfma32_f32(a, b, acc[jj]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  float* gsm = st;
+  float* bmo = bm + (bh * F1 + fi) * int64_t(D) * DV;
+#pragma unroll
+  for (int jj = 0; jj < C::CPW; ++jj) {
+    const int c = jj * C::RPW + cofs;
+    if (c >= C::NC) continue;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int row = rb * 32 + mfma32_row(e, lane);
+      if (c < C::NK) {
+        gsm[row * C::GS + c * 32 + (lane & 31)] = acc[jj][e];
+      } else {
+        bmo[int64_t(row) * DV + (c - C::NK) * 32 + (lane & 31)] = acc[jj][e];
+      }
+    }
+  }
+  __syncthreads();
+  float* rowv = reinterpret_cast<float*>(smem + C::MAIN_BYTES);
+  float* colv = rowv + 2 * D;
+  float a[D / 16][D / 16];
+  spd_inverse_gj<D>(gsm, C::GS, lam, rowv, colv, a);
+  constexpr int TS = D / 16;
+  float* ao = ainv + (bh * F1 + fi) * int64_t(D) * D;
+  const int tr = tid >> 4, tcol = tid & 15;
+#pragma unroll
+  for (int i = 0; i < TS; ++i)
+#pragma unroll
+    for (int j = 0; j < TS; ++j) ao[(tr * TS + i) * D + tcol * TS + j] = a[i][j];
+}
+
+template <int D, int DV>
+hipError_t launch_stats_t(const Problem& p, const void* k, const void* v, const void* tk,
+                          const void* tv, hipStream_t s) {
+  const int64_t blocks = p.B * p.H * (p.F + 1);
+  if (p.bf16) {
+    constexpr int lds = StatsBf16<D, DV>::LDS_BYTES;
+    auto kern = stats_bf16_kernel<D, DV>;
+    if (lds > 65536) {
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(kThreads), lds, s,
+                       static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+                       static_cast<const uint16_t*>(tk), static_cast<const uint16_t*>(tv), p.ainv,
+                       p.bm, p.F, p.n, p.T, p.lam);
+  } else {
+    constexpr int lds = StatsF32<D, DV>::LDS_BYTES;
+    auto kern = stats_f32_kernel<D, DV>;
+    if (lds > 65536) {
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(kThreads), lds, s,
+                       static_cast<const float*>(k), static_cast<const float*>(v),
+                       static_cast<const float*>(tk), static_cast<const float*>(tv), p.ainv, p.bm,
+                       p.F, p.n, p.T, p.lam);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_stats(const Problem& p, const void* k, const void* v, const void* tk,
+                        const void* tv, hipStream_t s) {
+#define VDA_CASE(DD, VV) \
+  if (p.d == DD && p.dv == VV) return launch_stats_t<DD, VV>(p, k, v, tk, tv, s);
+  VDA_CASE(32, 32) VDA_CASE(32, 64) VDA_CASE(32, 128)
+  VDA_CASE(64, 32) VDA_CASE(64, 64) VDA_CASE(64, 128)
+  VDA_CASE(128, 32) VDA_CASE(128, 64) VDA_CASE(128, 128)
+#undef VDA_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace vda

@@ -1,0 +1,202 @@
+// C ABI of the VDA forward library: plans, argument checks, stage dispatch.
+// The operation and the layouts are documented in include/vda.h.
+#include "vda.h"
+#include "vda_internal.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <new>
+
+struct vda_plan_s {
+  vda::Problem p;
+  int device;
+  void* workspace;
+  size_t workspace_bytes;
+};
+
+namespace {
+
+bool supported_width(int64_t x) { return x == 32 || x == 64 || x == 128; }
+
+// a*b into *out; false on overflow of the positive int64 range.
+bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+  return !__builtin_mul_overflow(a, b, out) && *out >= 0;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+}  // namespace
+
+extern "C" {
+
+const char* vda_status_string(vda_status s) {
+  switch (s) {
+    case VDA_SUCCESS: return "VDA_SUCCESS";
+    case VDA_ERROR_INVALID_VALUE: return "VDA_ERROR_INVALID_VALUE";
+    case VDA_ERROR_NOT_SUPPORTED: return "VDA_ERROR_NOT_SUPPORTED";
+    case VDA_ERROR_MISALIGNED: return "VDA_ERROR_MISALIGNED";
+    case VDA_ERROR_OUT_OF_MEMORY: return "VDA_ERROR_OUT_OF_MEMORY";
+    case VDA_ERROR_DEVICE: return "VDA_ERROR_DEVICE";
+  }
+  return "VDA_ERROR_UNKNOWN";
+}
+
+vda_status vda_plan_create(int64_t B, int64_t H, int64_t F, int64_t n, int64_t d, int64_t dv,
+                           int64_t T, float lambda, vda_dtype dtype, vda_plan_t* plan_out) {
+  if (plan_out == nullptr) return VDA_ERROR_INVALID_VALUE;
+  *plan_out = nullptr;
+  if (B < 0 || H < 0 || F < 0 || n < 0 || T < 0) return VDA_ERROR_INVALID_VALUE;
+  if (!(std::isfinite(lambda) && lambda > 0.0f)) return VDA_ERROR_INVALID_VALUE;
+  if (dtype != VDA_DTYPE_F32 && dtype != VDA_DTYPE_BF16) return VDA_ERROR_NOT_SUPPORTED;
+  if (!supported_width(d) || !supported_width(dv)) return VDA_ERROR_NOT_SUPPORTED;
+
+  // Every element count the kernels index must fit in int64; grids are 1-D.
+  int64_t bh, frames, tok, elems, ws_frames, ws_elems, tmp;
+  if (!mul_ok(B, H, &bh) || !mul_ok(bh, F + 1, &ws_frames) || !mul_ok(bh, F, &frames) ||
+      !mul_ok(frames, n, &tok) || !mul_ok(tok, 128, &elems) || !mul_ok(bh, T, &tmp) ||
+      !mul_ok(tmp, 128, &tmp))
+    return VDA_ERROR_INVALID_VALUE;
+  if (ws_frames > (int64_t(1) << 30)) return VDA_ERROR_INVALID_VALUE;
+  // ainv + bm over F+1 frames, xf + xb over F frames; each block <= 128*128 floats
+  if (!mul_ok(ws_frames, d * d + d * dv, &ws_elems) || !mul_ok(frames, 2 * d * dv, &tmp) ||
+      __builtin_add_overflow(ws_elems, tmp, &ws_elems) || !mul_ok(ws_elems, 4, &tmp))
+    return VDA_ERROR_INVALID_VALUE;
+  (void)elems;
+
+  vda_plan_s* plan = new (std::nothrow) vda_plan_s();
+  if (plan == nullptr) return VDA_ERROR_OUT_OF_MEMORY;
+  if (hipGetDevice(&plan->device) != hipSuccess) {
+    (void)hipGetLastError();
+    delete plan;
+    return VDA_ERROR_DEVICE;
+  }
+  vda::Problem& p = plan->p;
+  p.B = B; p.H = H; p.F = F; p.n = n; p.d = d; p.dv = dv; p.T = T;
+  p.lam = lambda;
+  p.bf16 = (dtype == VDA_DTYPE_BF16);
+  p.ainv = p.bm = p.xf = p.xb = nullptr;
+  plan->workspace = nullptr;
+  plan->workspace_bytes = 0;
+
+  const size_t ainv_n = size_t(ws_frames) * d * d;
+  const size_t bm_n = size_t(ws_frames) * d * dv;
+  const size_t x_n = size_t(frames) * d * dv;
+  const size_t total = (ainv_n + bm_n + 2 * x_n) * sizeof(float);
+  if (total > 0) {
+    void* ws = nullptr;
+    if (hipMalloc(&ws, total) != hipSuccess || ws == nullptr) {
+      (void)hipGetLastError();
+      delete plan;
+      return VDA_ERROR_OUT_OF_MEMORY;
+    }
+    plan->workspace = ws;
+    plan->workspace_bytes = total;
+    float* base = static_cast<float*>(ws);
+    p.ainv = base;
+    p.bm = p.ainv + ainv_n;
+    p.xf = p.bm + bm_n;
+    p.xb = p.xf + x_n;
+  }
+  *plan_out = plan;
+  return VDA_SUCCESS;
+}
+
+vda_status vda_plan_destroy(vda_plan_t plan) {
+  if (plan == nullptr) return VDA_SUCCESS;
+  vda_status st = VDA_SUCCESS;
+  if (plan->workspace != nullptr && hipFree(plan->workspace) != hipSuccess) {
+    (void)hipGetLastError();
+    st = VDA_ERROR_DEVICE;
+  }
+  delete plan;
+  return st;
+}
+
+size_t vda_plan_workspace_bytes(vda_plan_t plan) {
+  return plan == nullptr ? 0 : plan->workspace_bytes;
+}
+
+vda_status vda_debug_workspace(vda_plan_t plan, const float** ainv, const float** bm,
+                               const float** x_fwd, const float** x_bwd) {
+  if (plan == nullptr) return VDA_ERROR_INVALID_VALUE;
+  if (ainv) *ainv = plan->p.ainv;
+  if (bm) *bm = plan->p.bm;
+  if (x_fwd) *x_fwd = plan->p.xf;
+  if (x_bwd) *x_bwd = plan->p.xb;
+  return VDA_SUCCESS;
+}
+
+vda_status vda_forward_stages(vda_plan_t plan, unsigned stages, const void* q, const void* k,
+                              const void* v, const void* text_k, const void* text_v, void* out,
+                              void* stream) {
+  if (plan == nullptr) return VDA_ERROR_INVALID_VALUE;
+  if (stages == 0 || (stages & ~unsigned(VDA_STAGE_ALL)) != 0) return VDA_ERROR_INVALID_VALUE;
+  const vda::Problem& p = plan->p;
+  // No output element: nothing to compute and no pointer is read.
+  if (p.B == 0 || p.H == 0 || p.F == 0 || p.n == 0) return VDA_SUCCESS;
+  const size_t es = p.bf16 ? 2 : 4;
+  const size_t bh = size_t(p.B) * size_t(p.H);
+  const size_t qk_bytes = bh * size_t(p.F) * size_t(p.n) * size_t(p.d) * es;
+  const size_t vo_bytes = bh * size_t(p.F) * size_t(p.n) * size_t(p.dv) * es;
+  const size_t tk_bytes = bh * size_t(p.T) * size_t(p.d) * es;
+  const size_t tv_bytes = bh * size_t(p.T) * size_t(p.dv) * es;
+  const bool do_stats = stages & VDA_STAGE_STATS;
+  const bool do_scan = stages & VDA_STAGE_SCAN;
+  const bool do_read = stages & VDA_STAGE_READOUT;
+
+  // Pointer checks: a tensor the selected stages read or write must be non-NULL
+  // and 16-byte aligned when it has any element.
+  struct Arg {
+    const void* ptr;
+    size_t bytes;
+    bool used;
+  } args[6] = {{q, qk_bytes, do_read},         {k, qk_bytes, do_stats},
+               {v, vo_bytes, do_stats},        {text_k, tk_bytes, do_stats},
+               {text_v, tv_bytes, do_stats},   {out, vo_bytes, do_read}};
+  for (const Arg& a : args) {
+    if (!a.used || a.bytes == 0) continue;
+    if (a.ptr == nullptr) return VDA_ERROR_INVALID_VALUE;
+    if (!aligned16(a.ptr)) return VDA_ERROR_MISALIGNED;
+  }
+  if (do_read && vo_bytes > 0) {
+    Range o{reinterpret_cast<uintptr_t>(out), reinterpret_cast<uintptr_t>(out) + vo_bytes};
+    for (int i = 0; i < 5; ++i) {
+      if (args[i].ptr == nullptr || args[i].bytes == 0) continue;
+      Range r{reinterpret_cast<uintptr_t>(args[i].ptr),
+              reinterpret_cast<uintptr_t>(args[i].ptr) + args[i].bytes};
+      if (overlaps(o, r)) return VDA_ERROR_INVALID_VALUE;
+    }
+  }
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return VDA_ERROR_DEVICE;
+  }
+  if (dev != plan->device) return VDA_ERROR_INVALID_VALUE;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  if (do_stats) e = vda::launch_stats(p, k, v, text_k, text_v, s);
+  if (e == hipSuccess && do_scan) e = vda::launch_scan(p, s);
+  if (e == hipSuccess && do_read) e = vda::launch_readout(p, q, out, s);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return VDA_ERROR_DEVICE;
+  }
+  return VDA_SUCCESS;
+}
+
+vda_status vda_forward(vda_plan_t plan, const void* q, const void* k, const void* v,
+                       const void* text_k, const void* text_v, void* out, void* stream) {
+  return vda_forward_stages(plan, VDA_STAGE_ALL, q, k, v, text_k, text_v, out, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,170 @@
+// Device helpers for the gfx950 (CDNA4) VDA kernels: vector types, MFMA wrappers,
+// bfloat16 packing, the XCD-aware block remap and the in-LDS SPD inversion.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace vda {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kThreads = 256;  // 4 waves per workgroup in every kernel
+constexpr int kXcds = 8;       // MI355X: 8 XCDs, workgroups dealt round-robin
+
+template <typename T>
+__host__ __device__ constexpr T cmax(T a, T b) { return a > b ? a : b; }
+
+// 32x32x16 bf16 MFMA, fp32 accumulate.  Operand lane layout: lane l holds row
+// (A) / column (B) l%32 and 8 consecutive k values starting at 8*(l/32).
+// Result lane layout: column l%32, rows 8*(r/4) + 4*(l/32) + r%4 for r = 0..15.
+__device__ __forceinline__ f32x16 mfma32_bf16(uint4 a, uint4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// 32x32x2 fp32 MFMA.  Lane l holds A[l%32][l/32] and B[l/32][l%32]; result
+// layout as for mfma32_bf16.
+__device__ __forceinline__ f32x16 mfma32_f32(float a, float b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+// 16x16x4 fp32 MFMA.  Lane l holds A[l%16][l/16] and B[l/16][l%16]; result lane
+// layout: column l%16, rows 4*(l/16) + r for r = 0..3.
+__device__ __forceinline__ f32x4 mfma16_f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ int mfma32_row(int r, int lane) {
+  return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+}
+
+// float -> bfloat16 bits, round to nearest even; NaN stays NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
+  uint32_t u = __builtin_bit_cast(uint32_t, x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// Dword made of the low (sel=0) or high (sel=1) 16-bit halves of a (low) and b (high).
+__device__ __forceinline__ uint32_t interleave16(uint32_t a, uint32_t b, int hi) {
+  return __builtin_amdgcn_perm(b, a, hi ? 0x07060302u : 0x05040100u);
+}
+
+// Transpose an 8x8 block of 16-bit elements held as 8 rows of 4 dwords:
+// out[j] dword p = (in[2p] element j, in[2p+1] element j).
+__device__ __forceinline__ void transpose8x8_b16(const uint4 (&in)[8], uint4 (&out)[8]) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int w = j >> 1, hi = j & 1;
+    uint32_t d[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const uint4 a = in[2 * p], b = in[2 * p + 1];
+      const uint32_t aw = w == 0 ? a.x : w == 1 ? a.y : w == 2 ? a.z : a.w;
+      const uint32_t bw = w == 0 ? b.x : w == 1 ? b.y : w == 2 ? b.z : b.w;
+      d[p] = interleave16(aw, bw, hi);
+    }
+    out[j] = make_uint4(d[0], d[1], d[2], d[3]);
+  }
+}
+
+// Workgroup index remap so that consecutive logical indices land on one XCD.
+// Hardware deals workgroup id w to XCD w % 8; logical index i = xcd * per + slot.
+// `count` must be the padded grid size (a multiple of 8).
+__device__ __forceinline__ int64_t xcd_remap(int64_t w, int64_t count) {
+  const int64_t per = count / kXcds;
+  return (w % kXcds) * per + (w / kXcds);
+}
+
+// In-place inversion of the SPD matrix A = G + lam*I by Gauss-Jordan elimination
+// without pivoting (pivots of an SPD matrix are positive Schur complements).
+// G is read from LDS (row stride gs floats); each of the 256 threads owns a
+// TS x TS tile, TS = D/16, of the result, returned in `a`.
+// rowv/colv: LDS scratch of 2*D floats each (pivot row / column, double buffered).
+template <int D>
+__device__ __forceinline__ void spd_inverse_gj(const float* gsm, int gs, float lam,
+                                               float* rowv, float* colv,
+                                               float (&a)[D / 16][D / 16]) {
+  constexpr int TS = D / 16;
+  const int tid = threadIdx.x;
+  const int tr = tid >> 4, tc = tid & 15;
+#pragma unroll
+  for (int i = 0; i < TS; ++i)
+#pragma unroll
+    for (int j = 0; j < TS; ++j) {
+      const int gi = tr * TS + i, gj = tc * TS + j;
+      a[i][j] = gsm[gi * gs + gj] + (gi == gj ? lam : 0.0f);
+    }
+  // pivot row / column 0 into slot 0
+  if (tr == 0) {
+#pragma unroll
+    for (int j = 0; j < TS; ++j) rowv[tc * TS + j] = a[0][j];
+  }
+  if (tc == 0) {
+#pragma unroll
+    for (int i = 0; i < TS; ++i) colv[tr * TS + i] = a[i][0];
+  }
+  for (int kb = 0; kb < 16; ++kb) {
+#pragma unroll
+    for (int kk = 0; kk < TS; ++kk) {
+      const int k = kb * TS + kk;
+      const int slot = kk & 1;  // TS is even, so k & 1 == kk & 1
+      const float* rv = rowv + slot * D;
+      const float* cv = colv + slot * D;
+      __syncthreads();
+      const float p = rv[k];
+      const float ip = 1.0f / p;
+      float c[TS], r[TS];
+#pragma unroll
+      for (int i = 0; i < TS; ++i) c[i] = cv[tr * TS + i];
+#pragma unroll
+      for (int j = 0; j < TS; ++j) r[j] = rv[tc * TS + j] * ip;
+      const bool own_row = (tr == kb), own_col = (tc == kb);
+      float rk[TS], ck[TS];
+#pragma unroll
+      for (int j = 0; j < TS; ++j) rk[j] = r[j];
+#pragma unroll
+      for (int i = 0; i < TS; ++i) ck[i] = -c[i] * ip;
+      if (own_row) c[kk] = 0.0f;
+      if (own_col) r[kk] = 0.0f;
+#pragma unroll
+      for (int i = 0; i < TS; ++i)
+#pragma unroll
+        for (int j = 0; j < TS; ++j) a[i][j] = __builtin_fmaf(-c[i], r[j], a[i][j]);
+      if (own_row) {
+#pragma unroll
+        for (int j = 0; j < TS; ++j) a[kk][j] = rk[j];
+      }
+      if (own_col) {
+#pragma unroll
+        for (int i = 0; i < TS; ++i) a[i][kk] = ck[i];
+      }
+      if (own_row && own_col) a[kk][kk] = ip;
+      // publish pivot row / column k+1 into the other slot
+      if (k + 1 < D) {
+        const int kk1 = (kk + 1) % TS;
+        const int kb1 = (kk + 1 == TS) ? kb + 1 : kb;
+        float* rv1 = rowv + (slot ^ 1) * D;
+        float* cv1 = colv + (slot ^ 1) * D;
+        if (tr == kb1) {
+#pragma unroll
+          for (int j = 0; j < TS; ++j) rv1[tc * TS + j] = a[kk1][j];
+        }
+        if (tc == kb1) {
+#pragma unroll
+          for (int i = 0; i < TS; ++i) cv1[tr * TS + i] = a[i][kk1];
+        }
+      }
+    }
+  }
+}
+
+}  // namespace vda

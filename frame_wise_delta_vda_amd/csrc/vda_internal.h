@@ -1,0 +1,28 @@
+// Internal interface between the C ABI layer (vda_api.cpp) and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstddef>
+#include <cstdint>
+
+namespace vda {
+
+// Problem shape and float32 workspace of one plan.
+struct Problem {
+  int64_t B, H, F, n, d, dv, T;
+  float lam;
+  bool bf16;        // element type of q, k, v, text and out
+  // workspace (float32), frame index 0 = text, 1..F = frames
+  float* ainv;      // [BH][F+1][d][d]
+  float* bm;        // [BH][F+1][d][dv]
+  float* xf;        // [BH][F][d][dv]
+  float* xb;        // [BH][F][d][dv]
+};
+
+// Each launcher enqueues one stage on `stream` and returns the launch status.
+hipError_t launch_stats(const Problem& p, const void* k, const void* v, const void* tk,
+                        const void* tv, hipStream_t stream);
+hipError_t launch_scan(const Problem& p, hipStream_t stream);
+hipError_t launch_readout(const Problem& p, const void* q, void* out, hipStream_t stream);
+
+}  // namespace vda

@@ -1,0 +1,133 @@
+/*
+ * vda.h -- C ABI of the MI355X (gfx950) Video Delta Attention forward library.
+ *
+ * Video Delta Attention (VDA) is the linear-attention branch of VDN-MiniMax-H3.
+ * What it computes, per (batch b, head h), is described on the VDN-MiniMax-H3
+ * pages: the aiezz page, section 03 "technical principles", bullets "Video Delta
+ * Attention" (each frame's spatial tokens jointly set the new state through the
+ * normal equations; the frame-wise extension of the token-wise delta rule) and
+ * "dual text injection" (the text is written once, at initialisation, into the
+ * bidirectional state); the laicaila page, section "technical principles", the
+ * same two bullets; and the comfyui-wiki page, section "how Video DeltaNet speeds
+ * up H3" (a bidirectional linear-attention branch with a constant-cost recurrent
+ * state).  The pages give no formula; this library computes the regularised
+ * frame-level least-squares reading of them.  With the state X = S^T (d x dv):
+ *
+ *   X_text   = (lam I + Kt^T Kt)^{-1} (Kt^T Vt)                 text tokens, zero start
+ *   X_fwd_0  = X_text,  X_fwd_f = (lam I + K_f^T K_f)^{-1} (lam X_fwd_{f-1} + K_f^T V_f),  f = 1..F
+ *   X_bwd_F+1= X_text,  X_bwd_f = (lam I + K_f^T K_f)^{-1} (lam X_bwd_{f+1} + K_f^T V_f),  f = F..1
+ *   O_f      = Q_f (X_fwd_f + X_bwd_f) / 2                      n x dv per frame
+ *
+ * There is no feature map, 1/sqrt(d) scaling, decay or gate inside the op, and
+ * no output rows for the text tokens.
+ *
+ * Conventions for every call:
+ *  - Every call returns a vda_status.  Nothing aborts, and no C++ exception
+ *    crosses this boundary.
+ *  - All tensors are device pointers into the memory of the GPU that was current
+ *    when the plan was created, contiguous and row-major, in the plan's dtype
+ *    (float32, or bfloat16 as raw 16-bit words), 16-byte aligned.  The caller owns
+ *    them; the library never frees or keeps them past the call.
+ *  - Layouts (head-major, one contiguous n x d slab per (b,h,frame)):
+ *      q, k   [B][H][F][n][d]      v, out [B][H][F][n][dv]
+ *      text_k [B][H][T][d]         text_v [B][H][T][dv]
+ *  - out must not overlap any input.
+ */
+#ifndef VDA_H
+#define VDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct vda_plan_s* vda_plan_t;
+
+/* Element type of q, k, v, text_k, text_v and out.  Accumulation, the state and
+ * the solves are float32 in both cases. */
+typedef enum {
+  VDA_DTYPE_F32 = 0,
+  VDA_DTYPE_BF16 = 1
+} vda_dtype;
+
+typedef enum {
+  VDA_SUCCESS = 0,
+  VDA_ERROR_INVALID_VALUE = 1,  /* bad size, lambda, NULL pointer, aliasing, wrong device */
+  VDA_ERROR_NOT_SUPPORTED = 2,  /* d or dv outside {32, 64, 128}, unknown dtype */
+  VDA_ERROR_MISALIGNED = 3,     /* a tensor pointer is not 16-byte aligned */
+  VDA_ERROR_OUT_OF_MEMORY = 4,  /* workspace allocation failed */
+  VDA_ERROR_DEVICE = 5          /* a HIP runtime call or kernel launch failed */
+} vda_status;
+
+/* Pipeline stages of one forward pass, in the order they must run. */
+typedef enum {
+  VDA_STAGE_STATS = 1,    /* per frame (and the text): G = K^T K, Bm = K^T V, (lam I + G)^{-1} */
+  VDA_STAGE_SCAN = 2,     /* forward and backward state scans over the frames */
+  VDA_STAGE_READOUT = 4,  /* O_f = Q_f (X_fwd_f + X_bwd_f) / 2 */
+  VDA_STAGE_ALL = 7
+} vda_stage;
+
+/* Create a plan for one problem shape.
+ *   B, H, F, n, T >= 0: batch, heads, frames, spatial tokens per frame, text tokens.
+ *     B*H*F*n == 0 gives a plan whose forward pass has no output element: it does
+ *     nothing, reads no pointer and returns VDA_SUCCESS.  T == 0 means no text: the
+ *     text state is zero and text_k / text_v may be NULL.
+ *   d, dv in {32, 64, 128}: key/query width and value width.
+ *   lambda: the regulariser, finite and > 0, shared by the text and every frame.
+ *   dtype: element type of all tensors.
+ * The plan allocates its float32 workspace (hipMalloc) on the current device and
+ * keeps it until vda_plan_destroy.  On error *plan_out is set to NULL.
+ * Errors: INVALID_VALUE, NOT_SUPPORTED, OUT_OF_MEMORY, DEVICE. */
+vda_status vda_plan_create(int64_t B, int64_t H, int64_t F, int64_t n, int64_t d, int64_t dv,
+                           int64_t T, float lambda, vda_dtype dtype, vda_plan_t* plan_out);
+
+/* Enqueue the whole forward pass on `stream` (a hipStream_t; NULL is the null
+ * stream) and return without waiting.  Arguments are checked on the host before
+ * anything is enqueued; an error leaves out untouched.  Faults during execution
+ * surface at the caller's next synchronisation, as for any HIP work.
+ * The plan's workspace is reused by every call, so at most one forward pass per
+ * plan may be in flight; separate plans are independent.
+ * Results are bitwise reproducible for the same inputs and plan.
+ * Errors: INVALID_VALUE, MISALIGNED, DEVICE. */
+vda_status vda_forward(vda_plan_t plan, const void* q, const void* k, const void* v,
+                       const void* text_k, const void* text_v, void* out, void* stream);
+
+/* Enqueue only the stages in `stages` (a bitwise OR of vda_stage), in pipeline
+ * order.  A stage reads what the previous stage last wrote into the plan's
+ * workspace, so running SCAN or READOUT alone is valid only after the earlier
+ * stages have run on this plan.  Pointers a selected stage does not read may be
+ * NULL (STATS reads k, v, text_k, text_v; SCAN none; READOUT q and writes out).
+ * Used for per-stage timing and for checking intermediate results.
+ * Errors: as vda_forward, and INVALID_VALUE for stages outside VDA_STAGE_ALL. */
+vda_status vda_forward_stages(vda_plan_t plan, unsigned stages, const void* q, const void* k,
+                              const void* v, const void* text_k, const void* text_v, void* out,
+                              void* stream);
+
+/* Free the plan and its workspace.  The caller must make sure no forward pass on
+ * the plan is still running (synchronise its stream first).  NULL is accepted. */
+vda_status vda_plan_destroy(vda_plan_t plan);
+
+/* Bytes of device workspace the plan holds (0 for NULL). */
+size_t vda_plan_workspace_bytes(vda_plan_t plan);
+
+/* Static, human-readable name of a status code. */
+const char* vda_status_string(vda_status s);
+
+/* Device pointers into the plan's float32 workspace, for checking intermediate
+ * results after a synchronised forward pass.  Layouts, with BH = B*H and frame
+ * index 0 for the text and 1..F for the frames:
+ *   ainv  [BH][F+1][d][d]   (lam I + K^T K)^{-1}
+ *   bm    [BH][F+1][d][dv]  K^T V
+ *   x_fwd [BH][F][d][dv]    forward state after frame f (f = 1..F at index f-1)
+ *   x_bwd [BH][F][d][dv]    backward state after frame f
+ * The memory stays owned by the plan.  Any output pointer may be NULL. */
+vda_status vda_debug_workspace(vda_plan_t plan, const float** ainv, const float** bm,
+                               const float** x_fwd, const float** x_bwd);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VDA_H */

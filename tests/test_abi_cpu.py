@@ -1,0 +1,71 @@
+"""The C-ABI library on the host (no GPU needed): it loads, exports every function
+include/vda.h declares, and rejects bad plan arguments before touching a device."""
+import ctypes
+import math
+
+import pytest
+
+import frame_wise_delta_vda_amd as vda
+from frame_wise_delta_vda_amd import vda as binding
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return vda.load_library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = vda.declared_functions()
+    assert set(names) == {"vda_plan_create", "vda_forward", "vda_forward_stages", "vda_plan_destroy",
+                          "vda_plan_workspace_bytes", "vda_status_string", "vda_debug_workspace"}
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for code, name in vda.STATUS.items():
+        assert vda.vda_status_string(code) == name
+    assert vda.vda_status_string(99) == "VDA_ERROR_UNKNOWN"
+
+
+def _create(lib, *args):
+    h = ctypes.c_void_p(12345)
+    st = lib.vda_plan_create(*args[:7], ctypes.c_float(args[7]), args[8], ctypes.byref(h))
+    return st, h.value
+
+
+@pytest.mark.parametrize("args,expected", [
+    ((1, 1, 1, 1, 48, 32, 0, 1.0, 1), binding.VDA_ERROR_NOT_SUPPORTED),     # d not supported
+    ((1, 1, 1, 1, 32, 256, 0, 1.0, 1), binding.VDA_ERROR_NOT_SUPPORTED),    # dv not supported
+    ((1, 1, 1, 1, 32, 32, 0, 1.0, 7), binding.VDA_ERROR_NOT_SUPPORTED),     # dtype
+    ((-1, 1, 1, 1, 32, 32, 0, 1.0, 1), binding.VDA_ERROR_INVALID_VALUE),
+    ((1, 1, -2, 1, 32, 32, 0, 1.0, 1), binding.VDA_ERROR_INVALID_VALUE),
+    ((1, 1, 1, 1, 32, 32, -1, 1.0, 1), binding.VDA_ERROR_INVALID_VALUE),
+    ((1, 1, 1, 1, 32, 32, 0, 0.0, 1), binding.VDA_ERROR_INVALID_VALUE),     # lambda == 0
+    ((1, 1, 1, 1, 32, 32, 0, -1.0, 1), binding.VDA_ERROR_INVALID_VALUE),
+    ((1, 1, 1, 1, 32, 32, 0, math.nan, 1), binding.VDA_ERROR_INVALID_VALUE),
+    ((1, 1, 1, 1, 32, 32, 0, math.inf, 1), binding.VDA_ERROR_INVALID_VALUE),
+    ((2**40, 2**40, 1, 1, 32, 32, 0, 1.0, 1), binding.VDA_ERROR_INVALID_VALUE),  # overflow
+])
+def test_plan_create_rejects_bad_arguments(lib, args, expected):
+    st, h = _create(lib, *args)
+    assert st == expected
+    assert h is None  # *plan_out cleared on error
+
+
+def test_null_handles(lib):
+    assert lib.vda_plan_create(1, 1, 1, 1, 32, 32, 0, ctypes.c_float(1.0), 1, None) == \
+        binding.VDA_ERROR_INVALID_VALUE
+    assert lib.vda_plan_destroy(None) == binding.VDA_SUCCESS
+    assert lib.vda_plan_workspace_bytes(None) == 0
+    assert lib.vda_forward(None, *([None] * 7)) == binding.VDA_ERROR_INVALID_VALUE
+    assert lib.vda_forward_stages(None, 7, *([None] * 7)) == binding.VDA_ERROR_INVALID_VALUE
+    p = ctypes.c_void_p()
+    assert lib.vda_debug_workspace(None, ctypes.byref(p), None, None, None) == \
+        binding.VDA_ERROR_INVALID_VALUE
+
+
+def test_binding_raises_vda_error(lib):
+    with pytest.raises(vda.VdaError) as e:
+        vda.vda_plan_create(1, 1, 1, 1, 40, 32, 0, 1.0, "bf16")
+    assert e.value.status == binding.VDA_ERROR_NOT_SUPPORTED

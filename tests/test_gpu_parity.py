@@ -1,0 +1,161 @@
+"""GPU parity: the HIP library (through its C ABI) against the float64 oracle, on the
+same seeded, identically rounded inputs.  Bar: max per-(b,h,frame) relative Frobenius
+error <= 1e-4 for float32 workloads and <= 1e-2 for bfloat16 workloads."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from frame_wise_delta_vda_amd import vda as binding
+from vda_gpu_util import TOL, frame_errors, out_to_float64, run_gpu, say, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _oracle_heads(w, heads):
+    """Oracle output for the listed (b,h) slices: dict (b,h) -> [F,n,dv] float64."""
+    res = {}
+    for b, h in heads:
+        x = W.head_float64(w, b, h)
+        res[(b, h)] = oracle.vda_forward_head(x["q"], x["k"], x["v"], x["text_k"], x["text_v"], w.lam)
+    return res
+
+
+def _check_heads(w, out, heads):
+    got = out_to_float64(out)
+    ref = _oracle_heads(w, heads)
+    worst = 0.0
+    for (b, h), r in ref.items():
+        e = frame_errors(got[b, h], r)
+        worst = max(worst, float(e.max()))
+    say(f"  {w.name} B={w.B} H={w.H} F={w.F} n={w.n} d={w.d} dv={w.dv} T={w.T}: "
+        f"max rel err {worst:.3e} over {len(heads)} heads")
+    assert np.all(np.isfinite(got))
+    assert worst <= TOL[w.dtype], worst
+    return worst
+
+
+@pytest.mark.parametrize("idx", [1, 2])
+def test_named_workload_full_parity(idx):
+    w = W.WORKLOADS[idx]
+    say(f"[gpu] full parity {w.name}")
+    dev = to_device(w, W.full_storage(w))
+    out, plan = run_gpu(w, dev)
+    _check_heads(w, out, [(b, h) for b in range(w.B) for h in range(w.H)])
+    plan.close()
+
+
+@pytest.mark.parametrize("idx", [3, 4, 5])
+def test_named_workload_sampled_parity(idx):
+    """Full-size problem in the launch configuration the benchmark times; the oracle
+    recomputes three whole (b,h) slices, every other slice is checked for finiteness."""
+    w = W.WORKLOADS[idx]
+    say(f"[gpu] full-size {w.name}: generating inputs")
+    dev = to_device(w, W.full_storage(w))
+    say(f"[gpu] full-size {w.name}: running")
+    out, plan = run_gpu(w, dev)
+    del dev
+    heads = [(0, 0), (w.B - 1, w.H - 1), (w.B // 2, w.H // 2)]
+    _check_heads(w, out, sorted(set(heads)))
+    plan.close()
+
+
+SMALL = [
+    # name, overrides: span several 64-token chunks and 32-token units with ragged tails
+    ("bf16_128x128_ragged", dict(dtype="bf16", d=128, dv=128, n=200, T=37, F=5, B=2, H=2)),
+    ("bf16_64x128", dict(dtype="bf16", d=64, dv=128, n=130, T=5, F=4, B=1, H=3)),
+    ("bf16_128x64", dict(dtype="bf16", d=128, dv=64, n=97, T=64, F=3, B=1, H=2)),
+    ("bf16_32x32", dict(dtype="bf16", d=32, dv=32, n=300, T=1, F=6, B=1, H=2)),
+    ("bf16_32x128", dict(dtype="bf16", d=32, dv=128, n=65, T=0, F=2, B=1, H=1)),
+    ("bf16_128x32", dict(dtype="bf16", d=128, dv=32, n=64, T=3, F=2, B=1, H=1)),
+    ("bf16_n1", dict(dtype="bf16", d=64, dv=64, n=1, T=1, F=7, B=1, H=2)),
+    ("bf16_F1", dict(dtype="bf16", d=128, dv=128, n=333, T=20, F=1, B=1, H=1)),
+    ("f32_128x128", dict(dtype="f32", d=128, dv=128, n=150, T=9, F=3, B=1, H=2)),
+    ("f32_64x32", dict(dtype="f32", d=64, dv=32, n=77, T=0, F=4, B=2, H=1)),
+    ("f32_32x64", dict(dtype="f32", d=32, dv=64, n=33, T=40, F=3, B=1, H=1)),
+    ("bf16_lowrank_lam_small", dict(dtype="bf16", d=128, dv=128, n=300, T=16, F=6, B=1, H=1,
+                                    kind="lowrank", lam=0.05)),
+]
+
+
+@pytest.mark.parametrize("name,over", SMALL, ids=[s[0] for s in SMALL])
+def test_small_shapes_parity(name, over):
+    w = W.WORKLOADS[2].replace(name=name, seed=100 + [s[0] for s in SMALL].index(name), **over)
+    say(f"[gpu] small parity {name}")
+    dev = to_device(w, W.full_storage(w, threads=1))
+    if w.T == 0:
+        dev["text_k"] = dev["text_v"] = None  # NULL text pointers are allowed when T == 0
+    out, plan = run_gpu(w, dev)
+    _check_heads(w, out, [(b, h) for b in range(w.B) for h in range(w.H)])
+    plan.close()
+
+
+def test_intermediates_match_oracle():
+    """Workspace after a forward pass: Ainv_f (lam I + K_f^T K_f) = I, Bm_f = K_f^T V_f, and
+    the forward/backward states against the oracle's."""
+    for w in (W.WORKLOADS[1], W.WORKLOADS[2].replace(H=2, F=5, n=200, T=30)):
+        say(f"[gpu] intermediates {w.name}")
+        dev = to_device(w, W.full_storage(w, threads=1))
+        out, plan = run_gpu(w, dev)
+        ainv_p, bm_p, xf_p, xb_p = plan.debug_workspace()
+        BH, F1, d, dv = w.B * w.H, w.F + 1, w.d, w.dv
+
+        def fetch(ptr, shape):
+            t = torch.empty(shape, dtype=torch.float32, device="cuda")
+            nbytes = t.numel() * 4
+            torch.cuda.synchronize()
+            import ctypes
+            hip = ctypes.CDLL("libamdhip64.so.7")  # the runtime torch already loaded
+            hip.hipMemcpy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
+            assert hip.hipMemcpy(t.data_ptr(), ptr, nbytes, 3) == 0  # device to device
+            return t.cpu().numpy().astype(np.float64)
+
+        ainv = fetch(ainv_p, (BH, F1, d, d))
+        bm = fetch(bm_p, (BH, F1, d, dv))
+        xf = fetch(xf_p, (BH, w.F, d, dv))
+        xb = fetch(xb_p, (BH, w.F, d, dv))
+        tol = 1e-5 if w.dtype == "f32" else 1e-4
+        for b in range(w.B):
+            for h in range(w.H):
+                x = W.head_float64(w, b, h)
+                i = b * w.H + h
+                frames = [(x["text_k"], x["text_v"])] + [(x["k"][f], x["v"][f]) for f in range(w.F)]
+                for fi, (K, V) in enumerate(frames):
+                    G, Bm = oracle.frame_statistics(K, V)
+                    A = w.lam * np.eye(d) + G
+                    assert np.abs(ainv[i, fi] @ A - np.eye(d)).max() < tol * 10
+                    assert np.abs(bm[i, fi] - Bm).max() <= tol * (1 + np.abs(Bm).max())
+                xt, Xf, Xb = oracle.head_states(x["k"], x["v"], x["text_k"], x["text_v"], w.lam)
+                for f in range(w.F):
+                    assert np.linalg.norm(xf[i, f] - Xf[f]) <= tol * np.linalg.norm(Xf[f])
+                    assert np.linalg.norm(xb[i, f] - Xb[f]) <= tol * np.linalg.norm(Xb[f])
+        plan.close()
+
+
+def test_bitwise_repeatable_and_no_unwritten_outputs():
+    w = W.WORKLOADS[2].replace(H=3, F=4, n=777, T=50)
+    say("[gpu] repeatability")
+    dev = to_device(w, W.full_storage(w, threads=1))
+    out1 = torch.full(w.shapes()["out"], float("nan"), dtype=torch.bfloat16, device="cuda")
+    out1, plan = run_gpu(w, dev, out=out1)
+    assert not torch.isnan(out1).any()
+    out2 = torch.full_like(out1, float("nan"))
+    run_gpu(w, dev, plan=plan, out=out2)
+    assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
+    plan.close()
+
+
+def test_stages_compose_to_forward():
+    w = W.WORKLOADS[2].replace(H=2, F=3, n=300, T=10)
+    say("[gpu] stages")
+    dev = to_device(w, W.full_storage(w, threads=1))
+    full, plan = run_gpu(w, dev)
+    staged = torch.empty_like(full)
+    plan.stages(binding.VDA_STAGE_STATS, k=dev["k"], v=dev["v"], text_k=dev["text_k"],
+                text_v=dev["text_v"])
+    plan.stages(binding.VDA_STAGE_SCAN)
+    plan.stages(binding.VDA_STAGE_READOUT, q=dev["q"], out=staged)
+    torch.cuda.synchronize()
+    assert torch.equal(full.view(torch.int16), staged.view(torch.int16))
+    plan.close()
