@@ -1,0 +1,314 @@
+#!/usr/bin/env python3
+"""Benchmark of the VDA forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 768p_bf16]
+
+One step = one whole forward pass (statistics, scans, readout) over one batch of
+seeded synthetic input already resident in HBM.  Prints ONE JSON line with the
+headline metric (video tokens/s at the 768p shape), the HBM roofline of the
+dominant kernel (timed live with HIP events on the launch stream) and the float64
+oracle's throughput on a bounded sample of the same workload on the host cores.
+
+Profiling helpers (used to produce the committed summaries under profiles/):
+    python bench.py --copy-probe            plain copy kernel of known size, for
+                                            calibrating rocprofv3 byte counters
+    python bench.py --summarize-stats CSV   kernel_stats.csv -> text summary
+    python bench.py --summarize-pmc FETCH_CSV WRITE_CSV COPY_FETCH_CSV COPY_WRITE_CSV
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
+KERNEL_SOURCES = {"stats": "stats.hip", "scan": "scan.hip", "readout": "readout.hip"}
+KERNEL_SYMBOLS = {"stats": "stats_bf16_kernel", "scan": "scan_kernel", "readout": "readout_bf16_kernel"}
+COPY_PROBE_BYTES = 1 << 30
+
+
+def source_hash(kernel: str) -> str:
+    path = os.path.join(ROOT, "frame_wise_delta_vda_amd", "csrc", KERNEL_SOURCES[kernel])
+    h = hashlib.sha256()
+    for p in (path, os.path.join(ROOT, "frame_wise_delta_vda_amd", "csrc", "vda_device.h")):
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic(w):
+    """Bytes and flops the method itself requires, per launch of each stage."""
+    es = w.elem_bytes
+    BH = w.B * w.H
+    tok = BH * (w.F * w.n + w.T)
+    vid = BH * w.F * w.n
+    return {
+        "stats": {"bytes": tok * (w.d + w.dv) * es,
+                  "flops": tok * (2 * w.d * w.d + 2 * w.d * w.dv) + BH * (w.F + 1) * 2 * w.d ** 3},
+        "scan": {"bytes": 0, "flops": 2 * BH * (w.F + 1) * 2 * w.d * w.d * w.dv},
+        "readout": {"bytes": vid * (w.d + w.dv) * es, "flops": vid * 2 * w.d * w.dv},
+    }
+
+
+def read_traffic(workload_name):
+    """Per-launch HBM bytes from the committed counter summary, or None per kernel when
+    the summary is missing or the kernel source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload_name}.txt")
+    out = {}
+    if not os.path.exists(path):
+        return out
+    with open(path) as f:
+        for line in f:
+            if line.startswith("traffic "):
+                parts = dict(kv.split("=", 1) for kv in line.split()[1:])
+                k = parts["kernel"]
+                if parts.get("source") == source_hash(k):
+                    out[k] = float(parts["bytes_per_launch"])
+    return out
+
+
+def cpu_baseline(w, arrays, budget_s=20.0, max_heads=None):
+    """Time the float64 oracle on whole (b,h) slices of the same inputs until ~budget_s."""
+    import numpy as np
+    import threadpoolctl
+    import oracle
+    import workloads as W
+
+    info = threadpoolctl.threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)][: max_heads or None]
+    spent, done = 0.0, 0
+    for b, h in heads:
+        x = {k: W.storage_to_float64(w, arrays[k][b, h]) for k in W.TENSORS}
+        t0 = time.perf_counter()
+        oracle.vda_forward_head(x["q"], x["k"], x["v"], x["text_k"], x["text_v"], w.lam)
+        spent += time.perf_counter() - t0
+        done += 1
+        if spent >= budget_s:
+            break
+    toks = done * w.F * w.n
+    return {"value": toks / spent, "unit": "video tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} of {w.B * w.H} (b,h) slices of {w.name} ({toks} video tokens), "
+                      f"numpy float64, {spent:.1f} s"}
+
+
+def to_device(w, arrays):
+    import numpy as np
+    import torch
+    dev = {}
+    for k, a in arrays.items():
+        t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if w.dtype == "bf16" \
+            else torch.from_numpy(a)
+        dev[k] = t.to("cuda")
+    return dev
+
+
+def run(args):
+    import torch
+    import workloads as W
+    from frame_wise_delta_vda_amd import vda as binding
+
+    w = W.by_name(args.workload)
+    print(f"[bench] {w.name}: generating inputs", file=sys.stderr, flush=True)
+    arrays = W.full_storage(w)
+    dev = to_device(w, arrays)
+    if args.no_cpu_baseline:
+        del arrays
+    out = torch.empty(w.shapes()["out"], dtype=dev["q"].dtype, device="cuda")
+    plan = binding.Plan(w.B, w.H, w.F, w.n, w.d, w.dv, w.T, w.lam, w.dtype)
+    q, k, v, tk, tv = (dev[x] for x in W.TENSORS)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        plan.stages(binding.VDA_STAGE_STATS, k=k, v=v, text_k=tk, text_v=tv)
+        if ev is not None:
+            ev[1].record()
+        plan.stages(binding.VDA_STAGE_SCAN)
+        if ev is not None:
+            ev[2].record()
+        plan.stages(binding.VDA_STAGE_READOUT, q=q, out=out)
+        if ev is not None:
+            ev[3].record()
+
+    print(f"[bench] {w.name}: warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    names = ["stats", "scan", "readout"]
+    kern_ms = {n: sum(events[i][j].elapsed_time(events[i][j + 1]) for i in range(args.steps)) / args.steps
+               for j, n in enumerate(names)}
+    print(f"[bench] {w.name}: {ms_step:.3f} ms/step; " +
+          ", ".join(f"{n} {kern_ms[n]:.3f} ms" for n in names), file=sys.stderr, flush=True)
+
+    alg = algorithmic(w)
+    traffic = read_traffic(w.name)
+    kernels = {}
+    for n in names:
+        ms = kern_ms[n]
+        entry = {"ms": round(ms, 4)}
+        if alg[n]["bytes"]:
+            gbs = alg[n]["bytes"] / (ms * 1e-3) / 1e9
+            entry.update({"alg_bytes": alg[n]["bytes"], "GB/s": round(gbs, 1),
+                          "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)})
+        entry["TFLOP/s"] = round(alg[n]["flops"] / (ms * 1e-3) / 1e12, 2)
+        entry["traffic"] = traffic.get(n)
+        kernels[n] = entry
+    dom = max(("stats", "readout"), key=lambda n: kern_ms[n])
+    ach = kernels[dom]["GB/s"]
+    roofline = {"kernel": dom, "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic.get(dom)}
+    value = w.video_tokens / (ms_step * 1e-3)
+    result = {
+        "metric": "VDA forward video tokens/s at 768p shape; % of HBM/MFMA roofline",
+        "value": round(value, 1),
+        "unit": "video tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "F": w.F, "n": w.n, "d": w.d, "dv": w.dv,
+                   "T": w.T, "lambda": w.lam, "video_tokens_per_step": w.video_tokens,
+                   "alg_bytes_per_step": w.algorithmic_bytes(),
+                   "whole_step_GB/s": round(w.algorithmic_bytes() / (ms_step * 1e-3) / 1e9, 1)},
+        "roofline": roofline,
+        "kernels": kernels,
+    }
+    plan.close()
+    del dev, out
+    if not args.no_cpu_baseline:
+        print(f"[bench] {w.name}: timing the oracle on host cores", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(w, arrays, budget_s=args.cpu_budget)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+def copy_probe(args):
+    """A plain read-once/write-once elementwise kernel over COPY_PROBE_BYTES."""
+    import torch
+    n = COPY_PROBE_BYTES // 2
+    src = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(max(args.steps, 1)):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": COPY_PROBE_BYTES, "copy_probe_bytes_written": COPY_PROBE_BYTES}))
+
+
+def short_name(name: str) -> str:
+    name = name.replace("(anonymous namespace)::", "").replace("void ", "", 1)
+    return name.split("(")[0]
+
+
+def _rows(path):
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def summarize_stats(args):
+    rows = _rows(args.summarize_stats)
+    print(f"# rocprofv3 --kernel-trace --stats summary")
+    print(f"# command: {args.command}")
+    print(f"{'kernel':<60} {'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'pct':>6}")
+    for r in rows:
+        name = r.get("Name") or r.get("KernelName") or r.get("Kernel_Name")
+        short = short_name(name)[:60]
+        print(f"{short:<60} {int(r['Calls']):>6} {float(r['AverageNs'])/1e3:>10.2f} "
+              f"{float(r['MinNs'])/1e3:>10.2f} {float(r['MaxNs'])/1e3:>10.2f} {float(r['Percentage']):>6.2f}")
+
+
+def _pmc_per_kernel(path, counter):
+    """Average counter value per dispatch for each kernel in a counter_collection CSV."""
+    acc = {}
+    for r in _rows(path):
+        if r.get("Counter_Name") != counter:
+            continue
+        name = r["Kernel_Name"]
+        acc.setdefault(name, []).append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+def summarize_pmc(args):
+    """Per-launch HBM traffic of the VDA kernels from FETCH_SIZE / WRITE_SIZE (KiB per
+    dispatch), each scaled by what the same counter reads for the copy probe."""
+    import workloads as W
+    fetch_csv, write_csv, cfetch_csv, cwrite_csv = args.summarize_pmc
+    w = W.by_name(args.workload)
+    fetch = _pmc_per_kernel(fetch_csv, "FETCH_SIZE")
+    write = _pmc_per_kernel(write_csv, "WRITE_SIZE")
+    cf = _pmc_per_kernel(cfetch_csv, "FETCH_SIZE")
+    cw = _pmc_per_kernel(cwrite_csv, "WRITE_SIZE")
+    copy_name = max(cf, key=cf.get)
+    f_scale = COPY_PROBE_BYTES / (cf[copy_name] * 1024.0)
+    w_scale = COPY_PROBE_BYTES / (cw[copy_name] * 1024.0)
+    alg = algorithmic(w)
+    print(f"# HBM traffic per launch, {w.name}, from rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE")
+    print(f"# command: {args.command}")
+    print(f"# calibration: copy probe '{short_name(copy_name)[:50]}' over {COPY_PROBE_BYTES} B read + "
+          f"{COPY_PROBE_BYTES} B written reads FETCH_SIZE {cf[copy_name]:.0f} KiB, WRITE_SIZE "
+          f"{cw[copy_name]:.0f} KiB -> scale fetch x{f_scale:.4f}, write x{w_scale:.4f}")
+    for kern, sym in KERNEL_SYMBOLS.items():
+        names = [n for n in fetch if sym in n]
+        if not names:
+            continue
+        n = names[0]
+        fb = fetch[n] * 1024.0 * f_scale
+        wb = write.get(n, 0.0) * 1024.0 * w_scale
+        print(f"# {kern}: fetch {fb/1e9:.4f} GB, write {wb/1e9:.4f} GB per launch; algorithmic "
+              f"{alg[kern]['bytes']/1e9:.4f} GB")
+        print(f"traffic kernel={kern} bytes_per_launch={fb + wb:.0f} fetch_bytes={fb:.0f} "
+              f"write_bytes={wb:.0f} alg_bytes={alg[kern]['bytes']} source={source_hash(kern)}")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="768p_bf16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--summarize-stats", metavar="CSV")
+    ap.add_argument("--summarize-pmc", nargs=4, metavar="CSV")
+    ap.add_argument("--command", default="", help="command line recorded in summaries")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the VDA path is benchmarked on a single MI355X.", file=sys.stderr)
+        sys.exit(2)
+    if args.summarize_stats:
+        return summarize_stats(args)
+    if args.summarize_pmc:
+        return summarize_pmc(args)
+    if args.copy_probe:
+        return copy_probe(args)
+    run(args)
+
+
+if __name__ == "__main__":
+    main()
