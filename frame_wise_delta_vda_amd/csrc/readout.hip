@@ -6,103 +6,145 @@
 // that frame's own update:
 //   W_f = (X_fwd_f + X_bwd_f) / 2,   O_f = Q_f W_f   (n x dv)
 //
-// bfloat16 path: a workgroup owns one frame (or a contiguous token range of it).
-// It forms W_f in fp32, rounds it to bf16 and stores W_f^T in LDS; each wave then
-// streams 32-token units of Q straight from HBM into MFMA operands (16-byte loads)
-// and computes O^T = W^T Q^T on 32x32x16 bf16 MFMA, so each lane ends up with four
-// consecutive output columns of one token, written as one 8-byte store.
-// float32 path: the same scheme with W kept in fp32 and 32x32x2 fp32 MFMA.
+// float32 path: one workgroup per frame (or token range), W kept in fp32 in LDS,
+// 32x32x2 fp32 MFMA, operands loaded straight from HBM.
 #include "vda_device.h"
 #include "vda_internal.h"
 
 namespace vda {
 namespace {
 
+// bfloat16 path.  Each workgroup owns a contiguous range of 64-token tiles (a tile
+// never straddles two frames) and keeps the W^T fragments of the current frame in
+// registers.  Q tiles are loaded with 16-byte loads where one workgroup instruction
+// covers whole rows (4 KB contiguous), staged through padded LDS, and read back as
+// MFMA operands; each wave computes O^T = W^T Q^T for one 32-wide output-column block
+// (32x32x16 bf16 MFMA); the bf16 O tile goes back through LDS so the stores are whole
+// rows as well.  The next two tiles are always in flight in registers.
 template <int D, int DV>
 struct ReadBf16 {
-  static constexpr int WROW = D + 8;  // bf16 per LDS row of W^T (conflict-free fragment reads)
-  static constexpr int LDS_BYTES = DV * WROW * 2;
-  static constexpr int NDB = DV / 32;  // 32-wide output column blocks
-  static constexpr int KS = D / 16;    // MFMA k-steps
+  static constexpr int TT = 64;                 // tokens per tile
+  static constexpr int QROW = D * 2 + 16;       // bytes per LDS row of Q (padded)
+  static constexpr int OROW = DV * 2 + 16;      // bytes per LDS row of O
+  static constexpr int WROW = D + 8;            // bf16 per LDS row of W^T
+  static constexpr int QCH = D / 8, OCH = DV / 8;        // 16-byte chunks per row
+  static constexpr int QLD = TT * QCH / kThreads;        // 16-byte loads per thread per tile
+  static constexpr int OST = TT * OCH / kThreads;        // 16-byte stores per thread per tile
+  static constexpr int NB = DV / 32;            // 32-wide output column blocks
+  static constexpr int NT = TT / 32;            // 32-token sub-tiles
+  static constexpr int WPB = 4 / NB < 1 ? 1 : 4 / NB;     // waves per column block
+  static constexpr int SPW = NT / WPB < 1 ? 1 : NT / WPB;  // sub-tiles per wave
+  static constexpr int KS = D / 16;             // MFMA k-steps
+  static constexpr int QS_BYTES = TT * QROW, OS_BYTES = TT * OROW, WT_BYTES = DV * WROW * 2;
+  static constexpr int LDS_BYTES = QS_BYTES + OS_BYTES + WT_BYTES;
+  static_assert(QLD >= 1 && OST >= 1, "tile too small for the workgroup");
 };
-
-// W^T (bf16) into LDS from the two fp32 states of frame index f (0-based).
-template <int D, int DV>
-__device__ __forceinline__ void build_wt_bf16(const float* xf, const float* xb, uint16_t* wt) {
-  using C = ReadBf16<D, DV>;
-  // thread handles rows (2kp, 2kp+1) of W for column j -> one dword of W^T row j
-  for (int idx = threadIdx.x; idx < (D / 2) * DV; idx += kThreads) {
-    const int j = idx % DV, kp = idx / DV;
-    const int r0 = 2 * kp;
-    const float w0 = 0.5f * (xf[r0 * DV + j] + xb[r0 * DV + j]);
-    const float w1 = 0.5f * (xf[(r0 + 1) * DV + j] + xb[(r0 + 1) * DV + j]);
-    *reinterpret_cast<uint32_t*>(wt + j * C::WROW + r0) = pack_bf16x2(w0, w1);
-  }
-}
 
 template <int D, int DV>
 __global__ void __launch_bounds__(kThreads, 2)
 readout_bf16_kernel(const uint16_t* __restrict__ q, const float* __restrict__ xf,
-                    const float* __restrict__ xb, uint16_t* __restrict__ out, int64_t F,
-                    int64_t n, int64_t splits, int64_t tokens_per_split) {
+                    const float* __restrict__ xb, uint16_t* __restrict__ out, int64_t n,
+                    int64_t total_tiles, int64_t tiles_per_frame, int64_t per_wg) {
   using C = ReadBf16<D, DV>;
   extern __shared__ __align__(16) unsigned char smem[];
-  uint16_t* wt = reinterpret_cast<uint16_t*>(smem);
-
-  const int64_t split = blockIdx.x % splits;
-  const int64_t frame = blockIdx.x / splits;  // bh * F + f
-  const int64_t t_begin = split * tokens_per_split;
-  const int64_t t_end = t_begin + tokens_per_split < n ? t_begin + tokens_per_split : n;
-
-  build_wt_bf16<D, DV>(xf + frame * int64_t(D) * DV, xb + frame * int64_t(D) * DV, wt);
-  __syncthreads();
+  unsigned char* qs = smem;
+  unsigned char* os = smem + C::QS_BYTES;
+  uint16_t* wt = reinterpret_cast<uint16_t*>(smem + C::QS_BYTES + C::OS_BYTES);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, half = lane >> 5;
-  const uint16_t* qf = q + frame * n * D;
-  uint16_t* of = out + frame * n * DV;
+  const int64_t t_first = blockIdx.x * per_wg;
+  const int64_t t_last = (t_first + per_wg < total_tiles) ? t_first + per_wg : total_tiles;
+  if (t_first >= t_last) return;
 
-  const int64_t units = (t_end - t_begin + 31) / 32;
-  uint4 qa[C::KS], qn[C::KS];
-  auto load_q = [&](int64_t u, uint4 (&dst)[C::KS]) {
-    const int64_t t = t_begin + u * 32 + col;
-    const bool ok = t < t_end;
-    const uint16_t* src = qf + t * D + half * 8;
+  const int b = wave % C::NB;                    // output column block of this wave
+  const int sub0 = (wave / C::NB) * C::SPW;      // first 32-token sub-tile of this wave
+  const bool mfma_wave = (wave / C::NB) < C::WPB && sub0 < C::NT;
+  constexpr int RPI = kThreads / C::QCH;         // rows per load instruction
+  const int lrow = tid / C::QCH, lch = tid % C::QCH;
+  constexpr int SRPI = kThreads / C::OCH;
+  const int srow = tid / C::OCH, sch = tid % C::OCH;
+
+  uint4 pfa[C::QLD], pfb[C::QLD];
+  auto load_tile = [&](int64_t tile, uint4 (&dst)[C::QLD]) {
+    const int64_t frame = tile / tiles_per_frame;
+    const int64_t tok0 = (tile % tiles_per_frame) * C::TT;
+    const uint16_t* base = q + (frame * n + tok0) * D + lch * 8;
 #pragma unroll
-    for (int s = 0; s < C::KS; ++s) {
-      dst[s] = make_uint4(0, 0, 0, 0);
-      if (ok) dst[s] = *reinterpret_cast<const uint4*>(src + s * 16);
+    for (int i = 0; i < C::QLD; ++i) {
+      const int r = i * RPI + lrow;
+      dst[i] = make_uint4(0, 0, 0, 0);
+      if (tok0 + r < n) dst[i] = *reinterpret_cast<const uint4*>(base + int64_t(r) * D);
     }
   };
 
-  int64_t u = wave;
-  if (u < units) load_q(u, qa);
-  for (; u < units; u += 4) {
-    if (u + 4 < units) load_q(u + 4, qn);
-    const int64_t t = t_begin + u * 32 + col;
-    uint16_t* dst = of + t * DV + half * 4;
-    // one 32-column output block at a time keeps 16 accumulators live
-#pragma unroll
-    for (int b = 0; b < C::NDB; ++b) {
-      f32x16 acc = f32x16{};
-#pragma unroll
-      for (int s = 0; s < C::KS; ++s) {
-        const uint4 w = *reinterpret_cast<const uint4*>(wt + (b * 32 + col) * C::WROW + s * 16 +
-                                                        half * 8);
-        acc = mfma32_bf16(w, qa[s], acc);
+  int64_t cur_frame = -1;
+  uint4 wf[C::KS];  // W^T fragments of this wave's column block
+
+  auto step = [&](int64_t tile, uint4 (&pf)[C::QLD]) {
+    const int64_t frame = tile / tiles_per_frame;
+    const int64_t tok0 = (tile % tiles_per_frame) * C::TT;
+    if (frame != cur_frame) {
+      // W = (X_fwd + X_bwd) / 2 of the new frame, rounded to bf16, into LDS as W^T
+      __syncthreads();
+      const float* xff = xf + frame * int64_t(D) * DV;
+      const float* xbf = xb + frame * int64_t(D) * DV;
+      for (int idx = tid; idx < (D / 2) * DV; idx += kThreads) {
+        const int j = idx % DV, r0 = 2 * (idx / DV);
+        const float w0 = 0.5f * (xff[r0 * DV + j] + xbf[r0 * DV + j]);
+        const float w1 = 0.5f * (xff[(r0 + 1) * DV + j] + xbf[(r0 + 1) * DV + j]);
+        *reinterpret_cast<uint32_t*>(wt + j * C::WROW + r0) = pack_bf16x2(w0, w1);
       }
-      if (t < t_end) {
+      __syncthreads();
+#pragma unroll
+      for (int s = 0; s < C::KS; ++s)
+        wf[s] = *reinterpret_cast<const uint4*>(wt + (b * 32 + col) * C::WROW + s * 16 + half * 8);
+      cur_frame = frame;
+    }
+    // this tile: registers -> LDS; refill the registers with the tile two ahead
+#pragma unroll
+    for (int i = 0; i < C::QLD; ++i)
+      *reinterpret_cast<uint4*>(qs + (i * RPI + lrow) * C::QROW + lch * 16) = pf[i];
+    if (tile + 2 < t_last) load_tile(tile + 2, pf);
+    __syncthreads();
+    if (mfma_wave) {
+#pragma unroll
+      for (int si = 0; si < C::SPW; ++si) {
+        const int sub = sub0 + si;
+        f32x16 acc = f32x16{};
+#pragma unroll
+        for (int s = 0; s < C::KS; ++s) {
+          const uint4 qv = *reinterpret_cast<const uint4*>(qs + (sub * 32 + col) * C::QROW +
+                                                           s * 32 + half * 16);
+          acc = mfma32_bf16(wf[s], qv, acc);
+        }
+        // lane holds O[token sub*32+col][b*32 + 8i + 4*half + 0..3]
+        unsigned char* orow = os + (sub * 32 + col) * C::OROW + (b * 32 + half * 4) * 2;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           uint2 pk;
           pk.x = pack_bf16x2(acc[4 * i + 0], acc[4 * i + 1]);
           pk.y = pack_bf16x2(acc[4 * i + 2], acc[4 * i + 3]);
-          *reinterpret_cast<uint2*>(dst + b * 32 + 8 * i) = pk;
+          *reinterpret_cast<uint2*>(orow + 16 * i) = pk;
         }
       }
     }
+    __syncthreads();
+    uint16_t* obase = out + (frame * n + tok0) * DV + sch * 8;
 #pragma unroll
-    for (int s = 0; s < C::KS; ++s) qa[s] = qn[s];
+    for (int i = 0; i < C::OST; ++i) {
+      const int r = i * SRPI + srow;
+      if (tok0 + r < n)
+        *reinterpret_cast<uint4*>(obase + int64_t(r) * DV) =
+            *reinterpret_cast<const uint4*>(os + r * C::OROW + sch * 16);
+    }
+  };
+
+  load_tile(t_first, pfa);
+  if (t_first + 1 < t_last) load_tile(t_first + 1, pfb);
+  for (int64_t tile = t_first; tile < t_last; tile += 2) {
+    step(tile, pfa);
+    if (tile + 1 < t_last) step(tile + 1, pfb);
   }
 }
 
@@ -167,25 +209,30 @@ readout_f32_kernel(const float* __restrict__ q, const float* __restrict__ xf,
 template <int D, int DV>
 hipError_t launch_readout_t(const Problem& p, const void* q, void* out, hipStream_t s) {
   const int64_t frames = p.B * p.H * p.F;
-  // one workgroup per frame; split frames only when there are too few of them to
-  // fill the chip
-  int64_t splits = 1;
-  while (frames * splits < 1024 && p.n > 256 * splits) splits *= 2;
-  const int64_t tps = ((p.n + splits - 1) / splits + 31) / 32 * 32;
-  splits = (p.n + tps - 1) / tps;
-  const int64_t grid = frames * splits;
   if (p.bf16) {
-    constexpr int lds = ReadBf16<D, DV>::LDS_BYTES;
+    using C = ReadBf16<D, DV>;
+    const int64_t tpf = (p.n + C::TT - 1) / C::TT;
+    const int64_t total = frames * tpf;
+    int64_t grid = 2 * int64_t(p.num_cus);        // two persistent workgroups per CU
+    if (grid > total) grid = total;
+    const int64_t per = (total + grid - 1) / grid;
+    grid = (total + per - 1) / per;
     auto kern = readout_bf16_kernel<D, DV>;
-    if (lds > 65536) {
+    if (C::LDS_BYTES > 65536) {
       hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
       if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(kern, dim3(unsigned(grid)), dim3(kThreads), lds, s,
+    hipLaunchKernelGGL(kern, dim3(unsigned(grid)), dim3(kThreads), C::LDS_BYTES, s,
                        static_cast<const uint16_t*>(q), p.xf, p.xb, static_cast<uint16_t*>(out),
-                       p.F, p.n, splits, tps);
+                       p.n, total, tpf, per);
   } else {
+    // one workgroup per frame, split only when there are too few frames to fill the chip
+    int64_t splits = 1;
+    while (frames * splits < 1024 && p.n > 256 * splits) splits *= 2;
+    const int64_t tps = ((p.n + splits - 1) / splits + 31) / 32 * 32;
+    splits = (p.n + tps - 1) / tps;
+    const int64_t grid = frames * splits;
     constexpr int lds = ReadF32<D, DV>::LDS_BYTES;
     auto kern = readout_f32_kernel<D, DV>;
     if (lds > 65536) {

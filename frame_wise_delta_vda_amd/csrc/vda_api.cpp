@@ -79,6 +79,14 @@ vda_status vda_plan_create(int64_t B, int64_t H, int64_t F, int64_t n, int64_t d
     return VDA_ERROR_DEVICE;
   }
   vda::Problem& p = plan->p;
+  p.num_cus = 0;
+  if (hipDeviceGetAttribute(&p.num_cus, hipDeviceAttributeMultiprocessorCount, plan->device) !=
+          hipSuccess ||
+      p.num_cus <= 0) {
+    (void)hipGetLastError();
+    delete plan;
+    return VDA_ERROR_DEVICE;
+  }
   p.B = B; p.H = H; p.F = F; p.n = n; p.d = d; p.dv = dv; p.T = T;
   p.lam = lambda;
   p.bf16 = (dtype == VDA_DTYPE_BF16);

@@ -76,6 +76,23 @@ __device__ __forceinline__ void transpose8x8_b16(const uint4 (&in)[8], uint4 (&o
   }
 }
 
+// Raw buffer access: the descriptor (base, byte size) lives in SGPRs and must be
+// wave-uniform; the hardware range-checks every access against the size, so
+// out-of-range loads return zero and out-of-range stores are dropped, with no
+// branches around the memory instructions.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kBufferFlags = 0x00020000;  // raw buffer, 32-bit data format
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferFlags);
+}
+__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0));
+}
+__device__ __forceinline__ void buffer_store16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, uint4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)byte_off, 0, 0);
+}
+
 // Workgroup index remap so that consecutive logical indices land on one XCD.
 // Hardware deals workgroup id w to XCD w % 8; logical index i = xcd * per + slot.
 // `count` must be the padded grid size (a multiple of 8).

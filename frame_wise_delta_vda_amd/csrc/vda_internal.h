@@ -12,6 +12,7 @@ struct Problem {
   int64_t B, H, F, n, d, dv, T;
   float lam;
   bool bf16;        // element type of q, k, v, text and out
+  int num_cus;      // compute units of the plan's device (sizes persistent grids)
   // workspace (float32), frame index 0 = text, 1..F = frames
   float* ainv;      // [BH][F+1][d][d]
   float* bm;        // [BH][F+1][d][dv]
