@@ -89,11 +89,15 @@ readout_bf16_kernel(const uint16_t* __restrict__ q, const float* __restrict__ xf
       __syncthreads();
       const float* xff = xf + frame * int64_t(D) * DV;
       const float* xbf = xb + frame * int64_t(D) * DV;
-      for (int idx = tid; idx < (D / 2) * DV; idx += kThreads) {
-        const int j = idx % DV, r0 = 2 * (idx / DV);
-        const float w0 = 0.5f * (xff[r0 * DV + j] + xbf[r0 * DV + j]);
-        const float w1 = 0.5f * (xff[(r0 + 1) * DV + j] + xbf[(r0 + 1) * DV + j]);
-        *reinterpret_cast<uint32_t*>(wt + j * C::WROW + r0) = pack_bf16x2(w0, w1);
+      // the states are stored blocked: each float4 holds rows row..row+3 of one column
+      for (int i4 = tid; i4 < D * DV / 4; i4 += kThreads) {
+        const int blk = i4 >> 6, g = (i4 >> 4) & 3, col = (blk / (D / 16)) * 16 + (i4 & 15);
+        const int row = (blk % (D / 16)) * 16 + 4 * g;
+        const float4 a = reinterpret_cast<const float4*>(xff)[i4];
+        const float4 c = reinterpret_cast<const float4*>(xbf)[i4];
+        *reinterpret_cast<uint2*>(wt + col * C::WROW + row) =
+            make_uint2(pack_bf16x2(0.5f * (a.x + c.x), 0.5f * (a.y + c.y)),
+                       pack_bf16x2(0.5f * (a.z + c.z), 0.5f * (a.w + c.w)));
       }
       __syncthreads();
 #pragma unroll
@@ -171,7 +175,8 @@ readout_f32_kernel(const float* __restrict__ q, const float* __restrict__ xf,
   const float* xff = xf + frame * int64_t(D) * DV;
   const float* xbf = xb + frame * int64_t(D) * DV;
   for (int idx = threadIdx.x; idx < D * DV; idx += kThreads) {
-    const int kr = idx / DV, j = idx % DV;
+    const int blk = idx >> 8, g = (idx >> 6) & 3, j = (blk / (D / 16)) * 16 + ((idx >> 2) & 15);
+    const int kr = (blk % (D / 16)) * 16 + 4 * g + (idx & 3);
     w[kr * C::WROW + j] = 0.5f * (xff[idx] + xbf[idx]);
   }
   __syncthreads();

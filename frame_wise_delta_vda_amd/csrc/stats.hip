@@ -2,7 +2,8 @@
 //
 // For every (batch, head) and every frame f (index 0 = the text tokens, written
 // once into the state at initialisation; 1..F = video frames) this computes
-//   G_f = K_f^T K_f  (d x d),   Bm_f = K_f^T V_f  (d x dv),   Ainv_f = (lam I + G_f)^{-1},
+//   G_f = K_f^T K_f  (d x d),   Bm_f = K_f^T V_f  (d x dv, blocked layout),
+//   Ainv_f = (lam I + G_f)^{-1},
 // the statistics through which all spatial tokens of a frame jointly set the new
 // state (VDN-MiniMax-H3 pages: aiezz section 03 and laicaila "technical
 // principles", bullets "Video Delta Attention" and "dual text injection").
@@ -143,7 +144,7 @@ stats_bf16_kernel(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v
       if (c < C::NK) {
         gsm[row * C::GS + c * 32 + (lane & 31)] = acc[jj][e];
       } else {
-        bmo[int64_t(row) * DV + (c - C::NK) * 32 + (lane & 31)] = acc[jj][e];
+        bmo[blk_index(row, (c - C::NK) * 32 + (lane & 31), D)] = acc[jj][e];
       }
     }
   }
@@ -152,13 +153,23 @@ stats_bf16_kernel(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v
   float* colv = rowv + 2 * D;
   float a[D / 16][D / 16];
   spd_inverse_gj<D>(gsm, C::GS, lam, rowv, colv, a);
+  // A^{-1} as two bfloat16 planes, hi then lo (hi + lo = A^{-1} to ~2^-17 relative), for
+  // the split-bf16 MFMA products of the scan; same bytes as one float32 matrix.
   constexpr int TS = D / 16;
-  float* ao = ainv + (bh * F1 + fi) * int64_t(D) * D;
+  uint16_t* hi_plane = reinterpret_cast<uint16_t*>(ainv + (bh * F1 + fi) * int64_t(D) * D);
+  uint16_t* lo_plane = hi_plane + D * D;
   const int tr = tid >> 4, tcol = tid & 15;
 #pragma unroll
   for (int i = 0; i < TS; ++i)
 #pragma unroll
-    for (int j = 0; j < TS; ++j) ao[(tr * TS + i) * D + tcol * TS + j] = a[i][j];
+    for (int j = 0; j < TS; j += 2) {
+      uint32_t h0, l0, h1, l1;
+      split_bf16(a[i][j], h0, l0);
+      split_bf16(a[i][j + 1], h1, l1);
+      const int off = (tr * TS + i) * D + tcol * TS + j;
+      *reinterpret_cast<uint32_t*>(hi_plane + off) = h0 | (h1 << 16);
+      *reinterpret_cast<uint32_t*>(lo_plane + off) = l0 | (l1 << 16);
+    }
 }
 
 // ---------------------------------------------------------------- float32 inputs
@@ -249,7 +260,7 @@ stats_f32_kernel(const float* __restrict__ k, const float* __restrict__ v,
       if (c < C::NK) {
         gsm[row * C::GS + c * 32 + (lane & 31)] = acc[jj][e];
       } else {
-        bmo[int64_t(row) * DV + (c - C::NK) * 32 + (lane & 31)] = acc[jj][e];
+        bmo[blk_index(row, (c - C::NK) * 32 + (lane & 31), D)] = acc[jj][e];
       }
     }
   }

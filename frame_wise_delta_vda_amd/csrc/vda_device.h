@@ -53,6 +53,25 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
 }
 
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
+  return __builtin_bit_cast(float, b << 16);
+}
+
+// Split x into bfloat16 hi + lo with x - hi - lo = O(2^-17 |x|): hi = rne(x), lo = rne(x - hi).
+__device__ __forceinline__ void split_bf16(float x, uint32_t& hi, uint32_t& lo) {
+  hi = f32_to_bf16_bits(x);
+  lo = f32_to_bf16_bits(x - bf16_bits_to_f32(hi));
+}
+
+typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
+
+// 16x16x32 bf16 MFMA, fp32 accumulate.  Lane l holds row (A) / column (B) l%16 and
+// 8 consecutive k values starting at 8*(l/16); result: column l%16, rows 4*(l/16)+r.
+__device__ __forceinline__ f32x4 mfma16_bf16(uint4 a, uint4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8v, a),
+                                                 __builtin_bit_cast(bf16x8v, b), c, 0, 0, 0);
+}
+
 // Dword made of the low (sel=0) or high (sel=1) 16-bit halves of a (low) and b (high).
 __device__ __forceinline__ uint32_t interleave16(uint32_t a, uint32_t b, int hi) {
   return __builtin_amdgcn_perm(b, a, hi ? 0x07060302u : 0x05040100u);
@@ -74,6 +93,14 @@ __device__ __forceinline__ void transpose8x8_b16(const uint4 (&in)[8], uint4 (&o
     }
     out[j] = make_uint4(d[0], d[1], d[2], d[3]);
   }
+}
+
+// Blocked layout of a d x dv float32 matrix in the workspace (Bm and the states X):
+// 16-column blocks, then 16-row blocks, then the lane pattern of a 16x16 MFMA tile,
+// [row/4 within the tile][column][row%4], so each lane of a tile owns 4 contiguous floats.
+__host__ __device__ constexpr int blk_index(int row, int col, int d) {
+  return ((((col >> 4) * (d >> 4) + (row >> 4)) * 4 + ((row & 15) >> 2)) * 16 + (col & 15)) * 4 +
+         (row & 3);
 }
 
 // Raw buffer access: the descriptor (base, byte size) lives in SGPRs and must be

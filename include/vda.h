@@ -115,13 +115,17 @@ size_t vda_plan_workspace_bytes(vda_plan_t plan);
 /* Static, human-readable name of a status code. */
 const char* vda_status_string(vda_status s);
 
-/* Device pointers into the plan's float32 workspace, for checking intermediate
- * results after a synchronised forward pass.  Layouts, with BH = B*H and frame
- * index 0 for the text and 1..F for the frames:
- *   ainv  [BH][F+1][d][d]   (lam I + K^T K)^{-1}
- *   bm    [BH][F+1][d][dv]  K^T V
- *   x_fwd [BH][F][d][dv]    forward state after frame f (f = 1..F at index f-1)
- *   x_bwd [BH][F][d][dv]    backward state after frame f
+/* Device pointers into the plan's workspace, for checking intermediate results
+ * after a synchronised forward pass.  Layouts, with BH = B*H and frame index 0 for
+ * the text and 1..F for the frames:
+ *   ainv  [BH][F+1][d][d]   (lam I + K^T K)^{-1}: float32 for float32 plans; for
+ *                           bfloat16 plans each frame's d*d*4 bytes hold two bfloat16
+ *                           planes, [d][d] hi then [d][d] lo, with hi + lo = the inverse
+ *   bm    [BH][F+1][d*dv]   K^T V, float32, blocked (below)
+ *   x_fwd [BH][F][d*dv]     forward state after frame f (f = 1..F at index f-1), blocked
+ *   x_bwd [BH][F][d*dv]     backward state after frame f, blocked
+ * Blocked layout of a d x dv matrix M: element (r, c) is at
+ *   (((c/16 * d/16 + r/16) * 4 + (r%16)/4) * 16 + c%16) * 4 + r%4.
  * The memory stays owned by the plan.  Any output pointer may be NULL. */
 vda_status vda_debug_workspace(vda_plan_t plan, const float** ainv, const float** bm,
                                const float** x_fwd, const float** x_bwd);

@@ -112,9 +112,20 @@ def test_intermediates_match_oracle():
             return t.cpu().numpy().astype(np.float64)
 
         ainv = fetch(ainv_p, (BH, F1, d, d))
-        bm = fetch(bm_p, (BH, F1, d, dv))
-        xf = fetch(xf_p, (BH, w.F, d, dv))
-        xb = fetch(xb_p, (BH, w.F, d, dv))
+        if w.dtype == "bf16":  # per frame two bfloat16 planes, hi then lo
+            u16 = ainv.astype(np.float32).view(np.uint16).reshape(BH, F1, 2, d, d)
+            ainv = (W.bf16_bits_to_float32(u16[:, :, 0]).astype(np.float64) +
+                    W.bf16_bits_to_float32(u16[:, :, 1]).astype(np.float64))
+        def unblock(a):  # [..., d*dv] blocked -> [..., d, dv] row-major (layout in include/vda.h)
+            lead = a.shape[:-1]
+            a = a.reshape(lead + (dv // 16, d // 16, 4, 16, 4))
+            nl = len(lead)
+            perm = tuple(range(nl)) + (nl + 1, nl + 2, nl + 4, nl, nl + 3)
+            return np.transpose(a, perm).reshape(lead + (d, dv))
+
+        bm = unblock(fetch(bm_p, (BH, F1, d * dv)))
+        xf = unblock(fetch(xf_p, (BH, w.F, d * dv)))
+        xb = unblock(fetch(xb_p, (BH, w.F, d * dv)))
         tol = 1e-5 if w.dtype == "f32" else 1e-4
         for b in range(w.B):
             for h in range(w.H):
