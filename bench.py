@@ -31,7 +31,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
 KERNEL_SOURCES = {"stats": "stats.hip", "scan": "scan.hip", "readout": "readout.hip"}
-KERNEL_SYMBOLS = {"stats": "stats_bf16_kernel", "scan": "scan_kernel", "readout": "readout_bf16_kernel"}
+KERNEL_SYMBOLS = {"stats": "stats_bf16_kernel", "scan": "scan_bf16_kernel", "readout": "readout_bf16_kernel"}
 COPY_PROBE_BYTES = 1 << 30
 
 
