@@ -12,17 +12,17 @@
 // d x dv product -- the serial chain does no triangular solves.
 //
 // Columns of X are independent (the left factor Ainv_f is shared), so a chain is
-// split over DV/16 workgroups of 16 columns each; all workgroups of one chain are
-// placed on one XCD so that Ainv_f is fetched from HBM once and hit in L2 after.
-// Within a workgroup each wave owns 16-row blocks of X; the right operand
-// R = lam X + Bm of a step is exchanged through LDS.
+// split over several workgroups, each owning a slice of the columns; all workgroups
+// of one chain are placed on one XCD so that Ainv_f is fetched from HBM once and hit
+// in L2 after.  Within a workgroup each wave owns 16-row blocks of X; the right
+// operand R = lam X + Bm of a step is exchanged through LDS.
 //
-// float32 plans: 16x16x4 fp32 MFMA.
-// bfloat16 plans: split-bf16 products on 16x16x32 bf16 MFMA.  Ainv_f arrives as two
-// bf16 planes (hi + lo) and R is split the same way each step; Ainv R is taken as
-// hi*hi + hi*lo + lo*hi, which leaves a relative error of order 2^-16 per product
-// (far below the bf16 rounding of the inputs and output).  Operand fragments of the
-// next two steps are kept in flight in a register ring.
+// float32 plans: 16x16x4 fp32 MFMA, 16 columns per workgroup.
+// bfloat16 plans: split-bf16 products on 16x16x32 bf16 MFMA, 32 columns per workgroup
+// and one wave per 16 rows.  Ainv_f arrives as two bf16 planes (hi + lo) and R is split
+// the same way each step; Ainv R is taken as hi*hi + hi*lo + lo*hi, which leaves a
+// relative error of order 2^-16 per product (far below the bf16 rounding of the inputs
+// and output).  The operands of the next step are in flight while a step computes.
 #include "vda_device.h"
 #include "vda_internal.h"
 
@@ -157,25 +157,28 @@ scan_kernel(const float* __restrict__ ainv, const float* __restrict__ bm,
   }
 }
 
+// bfloat16 plans.  One wave per 16-row block of X (D/16 waves), 32 columns of X per
+// workgroup (DV/32 workgroups per chain).  Each wave loads only its own 16 rows of
+// Ainv_f, as 1 KB fragment-ordered runs (frag_index), and the 32-column slice of Bm.
 template <int D, int DV>
 struct ScanBf16Cfg {
-  static constexpr int RB = D / 16;               // 16-row blocks of X
-  static constexpr int NW = RB < 4 ? RB : 4;      // waves holding rows
-  static constexpr int RBW = RB / NW;             // row blocks per wave
+  static constexpr int NW = D / 16;               // waves; wave w owns rows 16w..16w+15
+  static constexpr int THREADS = 64 * NW;
   static constexpr int KS = D / 32;               // k-steps of the 16x16x32 MFMA
-  static constexpr int NCB = DV / 16;             // 16-column workgroups per chain
-  static constexpr int NPF = 2;                   // steps of operand prefetch
-  static constexpr int NSLOT = NPF + 1;           // register ring slots
-  static constexpr int RS_ELEMS = 2 * KS * 4 * 16 * 8;  // one R buffer: [hi/lo][ks][kg][n][8]
+  static constexpr int CW = 2;                    // 16-column blocks per workgroup
+  static constexpr int NCB = DV / (16 * CW);      // workgroups per chain
+  static constexpr int NSLOT = 2;                 // operand ring: this step and the next
+  static constexpr int CBE = 2 * KS * 4 * 16 * 8;  // R of one 16-column block: [hi/lo][ks][kg][n][8]
+  static_assert(DV % (16 * CW) == 0, "value width must be a multiple of 32");
 };
 
 template <int D, int DV>
-__global__ void __launch_bounds__(kThreads, 2)
+__global__ void __launch_bounds__(4 * D)
 scan_bf16_kernel(const uint16_t* __restrict__ ainv_planes, const float* __restrict__ bm,
                  float* __restrict__ xf, float* __restrict__ xb, int64_t nchains, int64_t F,
                  float lam, int64_t grid) {
   using C = ScanBf16Cfg<D, DV>;
-  __shared__ __align__(16) uint16_t rs[2][C::RS_ELEMS];
+  __shared__ __align__(16) uint16_t rs[2][C::CW * C::CBE];
 
   const int64_t L = xcd_remap(blockIdx.x, grid);
   const int64_t chain = L / C::NCB;
@@ -186,10 +189,10 @@ scan_bf16_kernel(const uint16_t* __restrict__ ainv_planes, const float* __restri
   const int64_t F1 = F + 1;
 
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6) & 3;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g = lane >> 4;
-  const bool active = wave < C::NW;
-  const int c0 = cb * 16;
+  const int c0 = cb * 16 * C::CW;
+  const int row0 = wave * 16 + 4 * g;  // first of the 4 output rows of this lane
 
   const uint16_t* ainv_h = ainv_planes + bh * F1 * int64_t(2 * D * D);
   const float* bm_h = bm + bh * F1 * int64_t(D) * DV;
@@ -200,105 +203,91 @@ scan_bf16_kernel(const uint16_t* __restrict__ ainv_planes, const float* __restri
     if (s > F) s = F;
     return (s == 0 || !backward) ? s : F + 1 - s;
   };
-  // slot t of the ring holds Ainv of step t and the Bm that step t adds for step t+1
-  uint4 A[C::NSLOT][C::RBW][C::KS][2];
-  float Bv[C::NSLOT][C::RBW][4];
-  auto load_slot = [&](int64_t t, uint4 (&a)[C::RBW][C::KS][2], float (&bv)[C::RBW][4]) {
+  // slot t of the ring holds the Ainv rows of step t and the Bm that step t adds for t+1
+  uint4 A[C::NSLOT][C::KS][2];
+  float4 Bv[C::NSLOT][C::CW];
+  auto load_slot = [&](int64_t t, uint4 (&a)[C::KS][2], float4 (&bv)[C::CW]) {
     const uint16_t* hi = ainv_h + frame_at(t) * int64_t(2 * D * D);
     const uint16_t* lo = hi + D * D;
     const float* bsrc = bm_h + frame_at(t + 1) * int64_t(D) * DV;
 #pragma unroll
-    for (int i = 0; i < C::RBW; ++i) {
-      const int row = (wave * C::RBW + i) * 16 + n;
-#pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) {
-        a[i][ks][0] = *reinterpret_cast<const uint4*>(hi + row * D + ks * 32 + g * 8);
-        a[i][ks][1] = *reinterpret_cast<const uint4*>(lo + row * D + ks * 32 + g * 8);
-      }
-      const float4 b4 = *reinterpret_cast<const float4*>(
-          bsrc + blk_index((wave * C::RBW + i) * 16 + 4 * g, c0 + n, D));
-      bv[i][0] = b4.x; bv[i][1] = b4.y; bv[i][2] = b4.z; bv[i][3] = b4.w;
+    for (int ks = 0; ks < C::KS; ++ks) {
+      const int off = ((wave * C::KS + ks) * 64 + lane) * 8;  // frag_index(16 wave + n, 32 ks + 8 g, D)
+      a[ks][0] = *reinterpret_cast<const uint4*>(hi + off);
+      a[ks][1] = *reinterpret_cast<const uint4*>(lo + off);
     }
+#pragma unroll
+    for (int cw = 0; cw < C::CW; ++cw)
+      bv[cw] = *reinterpret_cast<const float4*>(bsrc + blk_index(row0, c0 + 16 * cw + n, D));
   };
   // R fragment (8 consecutive k of column n) and the 4-row output slot of a lane
-  auto rs_frag = [&](int buf, int hl, int ks) -> const uint4* {
-    return reinterpret_cast<const uint4*>(&rs[buf][((hl * C::KS + ks) * 4 + g) * 128 + n * 8]);
+  auto rs_frag = [&](int buf, int cw, int hl, int ks) -> const uint4* {
+    return reinterpret_cast<const uint4*>(&rs[buf][cw * C::CBE + ((hl * C::KS + ks) * 4 + g) * 128 + n * 8]);
   };
-  auto rs_out = [&](int buf, int hl, int rbx) -> uint2* {
-    return reinterpret_cast<uint2*>(
-        &rs[buf][((hl * C::KS + rbx / 2) * 4 + 2 * (rbx % 2) + g / 2) * 128 + n * 8 + 4 * (g % 2)]);
+  auto rs_out = [&](int buf, int cw, int hl) -> uint2* {
+    return reinterpret_cast<uint2*>(&rs[buf][cw * C::CBE + ((hl * C::KS + wave / 2) * 4 + 2 * (wave % 2) + g / 2) * 128 +
+                                             n * 8 + 4 * (g % 2)]);
   };
-  auto write_r = [&](int buf, int i, float r0, float r1, float r2, float r3) {
+  auto write_r = [&](int buf, int cw, float r0, float r1, float r2, float r3) {
     uint32_t h0, l0, h1, l1, h2, l2, h3, l3;
     split_bf16(r0, h0, l0);
     split_bf16(r1, h1, l1);
     split_bf16(r2, h2, l2);
     split_bf16(r3, h3, l3);
-    const int rbx = wave * C::RBW + i;
-    *rs_out(buf, 0, rbx) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
-    *rs_out(buf, 1, rbx) = make_uint2(l0 | (l1 << 16), l2 | (l3 << 16));
+    *rs_out(buf, cw, 0) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+    *rs_out(buf, cw, 1) = make_uint2(l0 | (l1 << 16), l2 | (l3 << 16));
   };
 
-  if (active) {
-    // R_0 = lam * 0 + Bm_0
+  // R_0 = lam * 0 + Bm_0
 #pragma unroll
-    for (int i = 0; i < C::RBW; ++i) {
-      const float4 b4 = *reinterpret_cast<const float4*>(
-          bm_h + blk_index((wave * C::RBW + i) * 16 + 4 * g, c0 + n, D));
-      write_r(0, i, b4.x, b4.y, b4.z, b4.w);
-    }
-#pragma unroll
-    for (int t = 0; t < C::NPF; ++t) load_slot(t, A[t], Bv[t]);
+  for (int cw = 0; cw < C::CW; ++cw) {
+    const float4 b4 = *reinterpret_cast<const float4*>(bm_h + blk_index(row0, c0 + 16 * cw + n, D));
+    write_r(0, cw, b4.x, b4.y, b4.z, b4.w);
   }
+#pragma unroll
+  for (int t = 0; t < C::NSLOT - 1; ++t) load_slot(t, A[t], Bv[t]);
   __syncthreads();
 
-  auto step = [&](int64_t s, uint4 (&a)[C::RBW][C::KS][2], float (&bv)[C::RBW][4],
-                  uint4 (&a_fill)[C::RBW][C::KS][2], float (&bv_fill)[C::RBW][4]) {
+  auto step = [&](int64_t s, uint4 (&a)[C::KS][2], float4 (&bv)[C::CW], uint4 (&a_fill)[C::KS][2],
+                  float4 (&bv_fill)[C::CW]) {
     const int buf = int(s & 1);
-    if (active) {
-      load_slot(s + C::NPF, a_fill, bv_fill);
-      f32x4 hh[C::RBW], hl[C::RBW], lh[C::RBW];
+    load_slot(s + C::NSLOT - 1, a_fill, bv_fill);
+    f32x4 x[C::CW];
 #pragma unroll
-      for (int i = 0; i < C::RBW; ++i) hh[i] = hl[i] = lh[i] = f32x4{};
+    for (int cw = 0; cw < C::CW; ++cw) {
+      f32x4 hh = f32x4{}, hl = f32x4{}, lh = f32x4{};
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
-        const uint4 rh = *rs_frag(buf, 0, ks);
-        const uint4 rl = *rs_frag(buf, 1, ks);
-#pragma unroll
-        for (int i = 0; i < C::RBW; ++i) {
-          hh[i] = mfma16_bf16(a[i][ks][0], rh, hh[i]);
-          hl[i] = mfma16_bf16(a[i][ks][0], rl, hl[i]);
-          lh[i] = mfma16_bf16(a[i][ks][1], rh, lh[i]);
-        }
+        const uint4 rh = *rs_frag(buf, cw, 0, ks);
+        const uint4 rl = *rs_frag(buf, cw, 1, ks);
+        hh = mfma16_bf16(a[ks][0], rh, hh);
+        hl = mfma16_bf16(a[ks][0], rl, hl);
+        lh = mfma16_bf16(a[ks][1], rh, lh);
       }
-      f32x4 x[C::RBW];
+      x[cw] = hh + (hl + lh);
+    }
+    if (s >= 1) {
+      // the states are read back only by the readout, so keep them out of the caches
+      float* dst = xo_h + (frame_at(s) - 1) * int64_t(D) * DV;
 #pragma unroll
-      for (int i = 0; i < C::RBW; ++i) x[i] = hh[i] + (hl[i] + lh[i]);
-      if (s >= 1) {
-        float* dst = xo_h + (frame_at(s) - 1) * int64_t(D) * DV;
+      for (int cw = 0; cw < C::CW; ++cw)
+        __builtin_nontemporal_store(x[cw], reinterpret_cast<f32x4*>(dst + blk_index(row0, c0 + 16 * cw + n, D)));
+    }
+    if (s < F) {
 #pragma unroll
-        for (int i = 0; i < C::RBW; ++i)
-          *reinterpret_cast<float4*>(dst + blk_index((wave * C::RBW + i) * 16 + 4 * g, c0 + n, D)) =
-              make_float4(x[i][0], x[i][1], x[i][2], x[i][3]);
-      }
-      if (s < F) {
-#pragma unroll
-        for (int i = 0; i < C::RBW; ++i)
-          write_r(buf ^ 1, i, __builtin_fmaf(lam, x[i][0], bv[i][0]),
-                  __builtin_fmaf(lam, x[i][1], bv[i][1]), __builtin_fmaf(lam, x[i][2], bv[i][2]),
-                  __builtin_fmaf(lam, x[i][3], bv[i][3]));
-      }
+      for (int cw = 0; cw < C::CW; ++cw)
+        write_r(buf ^ 1, cw, __builtin_fmaf(lam, x[cw][0], bv[cw].x), __builtin_fmaf(lam, x[cw][1], bv[cw].y),
+                __builtin_fmaf(lam, x[cw][2], bv[cw].z), __builtin_fmaf(lam, x[cw][3], bv[cw].w));
     }
     __syncthreads();
   };
 
-  static_assert(C::NSLOT == 3, "ring unrolled for three slots");
-  for (int64_t s0 = 0; s0 <= F; s0 += 3) {
-    step(s0, A[0], Bv[0], A[2], Bv[2]);
-    if (s0 + 1 > F) break;
-    step(s0 + 1, A[1], Bv[1], A[0], Bv[0]);
-    if (s0 + 2 > F) break;
-    step(s0 + 2, A[2], Bv[2], A[1], Bv[1]);
+  for (int64_t s0 = 0; s0 <= F; s0 += C::NSLOT) {
+#pragma unroll
+    for (int u = 0; u < C::NSLOT; ++u) {
+      if (s0 + u > F) break;
+      step(s0 + u, A[u], Bv[u], A[(u + C::NSLOT - 1) % C::NSLOT], Bv[(u + C::NSLOT - 1) % C::NSLOT]);
+    }
   }
 }
 
@@ -308,7 +297,7 @@ hipError_t launch_scan_t(const Problem& p, hipStream_t s) {
   if (p.bf16) {
     using C = ScanBf16Cfg<D, DV>;
     const int64_t grid = ((nchains + kXcds - 1) / kXcds) * kXcds * C::NCB;
-    hipLaunchKernelGGL((scan_bf16_kernel<D, DV>), dim3(unsigned(grid)), dim3(kThreads), 0, s,
+    hipLaunchKernelGGL((scan_bf16_kernel<D, DV>), dim3(unsigned(grid)), dim3(C::THREADS), 0, s,
                        reinterpret_cast<const uint16_t*>(p.ainv), p.bm, p.xf, p.xb, nchains, p.F,
                        p.lam, grid);
   } else {

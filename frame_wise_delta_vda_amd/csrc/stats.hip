@@ -154,22 +154,36 @@ stats_bf16_kernel(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v
   float a[D / 16][D / 16];
   spd_inverse_gj<D>(gsm, C::GS, lam, rowv, colv, a);
   // A^{-1} as two bfloat16 planes, hi then lo (hi + lo = A^{-1} to ~2^-17 relative), for
-  // the split-bf16 MFMA products of the scan; same bytes as one float32 matrix.
+  // the split-bf16 MFMA products of the scan; same bytes as one float32 matrix.  The
+  // planes are fragment-ordered (frag_index): a thread's TS consecutive columns of a row
+  // stay contiguous, so each row goes out as one TS*2-byte store per plane.
   constexpr int TS = D / 16;
   uint16_t* hi_plane = reinterpret_cast<uint16_t*>(ainv + (bh * F1 + fi) * int64_t(D) * D);
   uint16_t* lo_plane = hi_plane + D * D;
   const int tr = tid >> 4, tcol = tid & 15;
 #pragma unroll
-  for (int i = 0; i < TS; ++i)
+  for (int i = 0; i < TS; ++i) {
+    uint32_t hw[TS / 2], lw[TS / 2];
 #pragma unroll
     for (int j = 0; j < TS; j += 2) {
       uint32_t h0, l0, h1, l1;
       split_bf16(a[i][j], h0, l0);
       split_bf16(a[i][j + 1], h1, l1);
-      const int off = (tr * TS + i) * D + tcol * TS + j;
-      *reinterpret_cast<uint32_t*>(hi_plane + off) = h0 | (h1 << 16);
-      *reinterpret_cast<uint32_t*>(lo_plane + off) = l0 | (l1 << 16);
+      hw[j / 2] = h0 | (h1 << 16);
+      lw[j / 2] = l0 | (l1 << 16);
     }
+    const int off = frag_index(tr * TS + i, tcol * TS, D);
+    if constexpr (TS == 8) {
+      *reinterpret_cast<uint4*>(hi_plane + off) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+      *reinterpret_cast<uint4*>(lo_plane + off) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+    } else if constexpr (TS == 4) {
+      *reinterpret_cast<uint2*>(hi_plane + off) = make_uint2(hw[0], hw[1]);
+      *reinterpret_cast<uint2*>(lo_plane + off) = make_uint2(lw[0], lw[1]);
+    } else {
+      *reinterpret_cast<uint32_t*>(hi_plane + off) = hw[0];
+      *reinterpret_cast<uint32_t*>(lo_plane + off) = lw[0];
+    }
+  }
 }
 
 // ---------------------------------------------------------------- float32 inputs

@@ -103,6 +103,16 @@ __host__ __device__ constexpr int blk_index(int row, int col, int d) {
          (row & 3);
 }
 
+// Fragment-ordered layout of a d x d bfloat16 plane (the hi and lo planes of Ainv for
+// the scan): the 16-row x 32-column operand block (row block r/16, column block c/32)
+// of a 16x16x32 MFMA is 1 KB contiguous, in lane order, lane 16*((c%32)/8) + r%16
+// holding the 8 consecutive columns it feeds to the MFMA.  One 16-byte load per lane
+// then reads a whole operand with a single contiguous wave access.
+__host__ __device__ constexpr int frag_index(int row, int col, int d) {
+  return ((((row >> 4) * (d >> 5) + (col >> 5)) * 4 + ((col & 31) >> 3)) * 16 + (row & 15)) * 8 +
+         (col & 7);
+}
+
 // Raw buffer access: the descriptor (base, byte size) lives in SGPRs and must be
 // wave-uniform; the hardware range-checks every access against the size, so
 // out-of-range loads return zero and out-of-range stores are dropped, with no

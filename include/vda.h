@@ -118,9 +118,11 @@ const char* vda_status_string(vda_status s);
 /* Device pointers into the plan's workspace, for checking intermediate results
  * after a synchronised forward pass.  Layouts, with BH = B*H and frame index 0 for
  * the text and 1..F for the frames:
- *   ainv  [BH][F+1][d][d]   (lam I + K^T K)^{-1}: float32 for float32 plans; for
+ *   ainv  [BH][F+1][d][d]   (lam I + K^T K)^{-1}: float32 row-major for float32 plans; for
  *                           bfloat16 plans each frame's d*d*4 bytes hold two bfloat16
- *                           planes, [d][d] hi then [d][d] lo, with hi + lo = the inverse
+ *                           planes of d*d, hi then lo, with hi + lo = the inverse, each
+ *                           fragment-ordered: element (r, c) at
+ *                           (((r/16 * d/32 + c/32) * 4 + (c%32)/8) * 16 + r%16) * 8 + c%8
  *   bm    [BH][F+1][d*dv]   K^T V, float32, blocked (below)
  *   x_fwd [BH][F][d*dv]     forward state after frame f (f = 1..F at index f-1), blocked
  *   x_bwd [BH][F][d*dv]     backward state after frame f, blocked

@@ -94,7 +94,9 @@ def test_small_shapes_parity(name, over):
 def test_intermediates_match_oracle():
     """Workspace after a forward pass: Ainv_f (lam I + K_f^T K_f) = I, Bm_f = K_f^T V_f, and
     the forward/backward states against the oracle's."""
-    for w in (W.WORKLOADS[1], W.WORKLOADS[2].replace(H=2, F=5, n=200, T=30)):
+    for w in (W.WORKLOADS[1], W.WORKLOADS[2].replace(H=2, F=5, n=200, T=30),
+              W.WORKLOADS[3].replace(H=1, F=4, n=300, T=20),
+              W.WORKLOADS[2].replace(H=1, F=3, n=100, T=8, d=32, dv=128)):
         say(f"[gpu] intermediates {w.name}")
         dev = to_device(w, W.full_storage(w, threads=1))
         out, plan = run_gpu(w, dev)
@@ -112,8 +114,10 @@ def test_intermediates_match_oracle():
             return t.cpu().numpy().astype(np.float64)
 
         ainv = fetch(ainv_p, (BH, F1, d, d))
-        if w.dtype == "bf16":  # per frame two bfloat16 planes, hi then lo
-            u16 = ainv.astype(np.float32).view(np.uint16).reshape(BH, F1, 2, d, d)
+        if w.dtype == "bf16":  # per frame two fragment-ordered bfloat16 planes, hi then lo
+            u16 = ainv.astype(np.float32).view(np.uint16).reshape(BH, F1, 2, d // 16, d // 32, 4, 16, 8)
+            # [rb][cb][c%32/8][r%16][c%8] -> [rb][r%16][cb][c%32/8][c%8] (layout in include/vda.h)
+            u16 = np.transpose(u16, (0, 1, 2, 3, 6, 4, 5, 7)).reshape(BH, F1, 2, d, d)
             ainv = (W.bf16_bits_to_float32(u16[:, :, 0]).astype(np.float64) +
                     W.bf16_bits_to_float32(u16[:, :, 1]).astype(np.float64))
         def unblock(a):  # [..., d*dv] blocked -> [..., d, dv] row-major (layout in include/vda.h)
