@@ -21,6 +21,114 @@
 namespace vda {
 namespace {
 
+// -(lam I + G)^{-1} in place, for d = 128, with G held in the MFMA accumulators of the
+// four waves of a workgroup: wave w holds rows 32w..32w+31 as four 32x32 tiles t[c]
+// (columns 32c..32c+31, lane l: column l%32, register e: row mfma32_row(e, l)).
+//
+// Blocked symmetric sweep.  Sweeping an SPD matrix on every index in turn gives minus
+// its inverse; sweeping a block K of 16 indices at once is, with the old panel
+// P = M[K,:] (= M[:,K]^T), its rows swept on the pivot columns W (which holds
+// S = -M[K,K]^{-1} on those columns):
+//   M <- M - P^T W,  then  M[K,:] = W,  M[:,K] = W^T,  M[K,K] = S.
+// Rounding makes M drift from symmetric, and the update takes panel rows for panel
+// columns, so P is taken as the mean of the panel rows and the transposed panel columns
+// (without it the inverse of an ill-conditioned frame loses two orders of magnitude of
+// accuracy).  W is swept inside each wave (every wave its own 32 columns plus a copy of
+// the pivot columns); forming W as -S P instead loses about one more.  The rank-16
+// update runs on fp32 MFMA straight on the accumulator tiles -- 8 panels, two barriers
+// each.  lds needs 3 * 2 * 16 * kPbs floats.
+constexpr int kPbs = 132;  // floats per LDS row of a panel (128 + pad)
+
+__device__ __forceinline__ void sweep_neg_inverse_128(f32x16 (&t)[4], float* lds, int wave,
+                                                      int lane) {
+  float* pb = lds;                  // [2][16][kPbs] old panel rows M[K,:]
+  float* cb = lds + 2 * 16 * kPbs;  // [2][16][kPbs] old panel columns, transposed: M[:,K]^T
+  float* wb = lds + 4 * 16 * kPbs;  // [2][16][kPbs] W (S in the pivot columns)
+  const int l32 = lane & 31, h = lane >> 5;
+  const int c16 = lane & 15;
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    const int wo = p >> 1, hp = p & 1, b = p & 1;
+    float* P = pb + b * 16 * kPbs;
+    float* Pc = cb + b * 16 * kPbs;
+    float* Wb = wb + b * 16 * kPbs;
+    // 1. the owner wave publishes the 16 panel rows, every wave its rows of the 16 panel
+    // columns.  The old panel used below is their mean: rounding makes the swept matrix
+    // drift from symmetric, and the update takes panel rows for panel columns.
+    if (wave == wo) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int e = 8 * hp; e < 8 * hp + 8; ++e)
+          P[(mfma32_row(e, lane) - 16 * hp) * kPbs + 32 * c + l32] = t[c][e];
+    }
+    if ((l32 >> 4) == hp) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) Pc[(l32 - 16 * hp) * kPbs + 32 * wave + mfma32_row(e, lane)] = t[wo][e];
+    }
+    __syncthreads();
+    // 2. sweep the 16 panel rows on the 16 pivot columns.  Lane l < 32 takes column
+    // 32 wave + l, lanes 32..63 a copy of pivot column 16p + l%16; a lane holds its
+    // column's 16 rows, so the pivot row is a register and the pivot column comes from
+    // lane 32 + kk by readlane.  Afterwards the panel holds W off the pivot columns and
+    // S = -M[K,K]^{-1} on them.
+    const int col = lane < 32 ? 32 * wave + lane : 16 * p + c16;
+    float m[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) m[r] = 0.5f * (P[r * kPbs + col] + Pc[r * kPbs + col]);
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      float ck[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        ck[r] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m[r]), 32 + kk));
+      const float ip = 1.0f / ck[kk];
+      const bool isk = col == 16 * p + kk;
+      const float rki = m[kk] * ip;
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (r != kk) m[r] = isk ? ck[r] * ip : __builtin_fmaf(-ck[r], rki, m[r]);
+      m[kk] = isk ? -ip : rki;
+    }
+    // 3. this wave's 32 columns of the swept panel
+    if (lane < 32) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) Wb[r * kPbs + col] = m[r];
+    }
+    __syncthreads();
+    // 4. M -= P^T W on the accumulator tiles (k = 2s + l/32 per 32x32x2 MFMA)
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const int k = 2 * s + h;
+      const float a = -0.5f * (P[k * kPbs + 32 * wave + l32] + Pc[k * kPbs + 32 * wave + l32]);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) t[c] = mfma32_f32(a, Wb[k * kPbs + 32 * c + l32], t[c]);
+    }
+    // 5. panel rows become W (S in the pivot block), panel columns W^T
+    if (wave == wo) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int e = 8 * hp; e < 8 * hp + 8; ++e)
+          t[c][e] = Wb[(mfma32_row(e, lane) - 16 * hp) * kPbs + 32 * c + l32];
+    }
+    {
+      const bool kcol = (l32 >> 4) == hp;
+      const float* src = Wb + (kcol ? l32 - 16 * hp : 0) * kPbs + 32 * wave + 4 * h;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 v4 = *reinterpret_cast<const float4*>(src + 8 * q);
+        if (kcol) {
+          t[wo][4 * q + 0] = v4.x;
+          t[wo][4 * q + 1] = v4.y;
+          t[wo][4 * q + 2] = v4.z;
+          t[wo][4 * q + 3] = v4.w;
+        }
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------- bfloat16 inputs
 template <int D, int DV>
 struct StatsBf16 {
@@ -131,9 +239,47 @@ stats_bf16_kernel(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v
     __syncthreads();
   }
 
+  float* bmo = bm + (bh * F1 + fi) * int64_t(D) * DV;
+  uint16_t* hi_plane = reinterpret_cast<uint16_t*>(ainv + (bh * F1 + fi) * int64_t(D) * D);
+  uint16_t* lo_plane = hi_plane + D * D;
+  if constexpr (D == 128) {
+    // ---- epilogue (d = 128): Bm tiles to the workspace; lam I + G inverted in the
+    // accumulators by the blocked sweep; A^{-1} = -(swept matrix) written out.
+    const int l32 = lane & 31;
+#pragma unroll
+    for (int jj = C::NK; jj < C::CPW; ++jj)
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        bmo[blk_index(rb * 32 + mfma32_row(e, lane), (jj - C::NK) * 32 + l32, D)] = acc[jj][e];
+    f32x16 t[4] = {acc[0], acc[1], acc[2], acc[3]};
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      if (c == wave) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (mfma32_row(e, lane) == l32) t[c][e] += lam;
+      }
+    static_assert(6 * 16 * kPbs * 4 <= C::MAIN_BYTES, "sweep buffers exceed the staging area");
+    sweep_neg_inverse_128(t, reinterpret_cast<float*>(smem), wave, lane);
+    // A^{-1} is symmetric: lane l's column j of tile c is row j of A^{-1}, and its
+    // registers 4q..4q+3 are 4 consecutive columns of that row (8 bytes per plane).
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint32_t h0, l0, h1, l1, h2, l2, h3, l3;
+        split_bf16(-t[c][4 * q + 0], h0, l0);
+        split_bf16(-t[c][4 * q + 1], h1, l1);
+        split_bf16(-t[c][4 * q + 2], h2, l2);
+        split_bf16(-t[c][4 * q + 3], h3, l3);
+        const int off = frag_index(32 * c + l32, 32 * wave + 8 * q + 4 * (lane >> 5), D);
+        *reinterpret_cast<uint2*>(hi_plane + off) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+        *reinterpret_cast<uint2*>(lo_plane + off) = make_uint2(l0 | (l1 << 16), l2 | (l3 << 16));
+      }
+    return;
+  }
   // ---- epilogue: Bm tiles to the workspace, G tiles to LDS, then invert lam I + G
   float* gsm = reinterpret_cast<float*>(smem);
-  float* bmo = bm + (bh * F1 + fi) * int64_t(D) * DV;
 #pragma unroll
   for (int jj = 0; jj < C::CPW; ++jj) {
     const int c = jj * C::RPW + cofs;
@@ -158,8 +304,6 @@ stats_bf16_kernel(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v
   // planes are fragment-ordered (frag_index): a thread's TS consecutive columns of a row
   // stay contiguous, so each row goes out as one TS*2-byte store per plane.
   constexpr int TS = D / 16;
-  uint16_t* hi_plane = reinterpret_cast<uint16_t*>(ainv + (bh * F1 + fi) * int64_t(D) * D);
-  uint16_t* lo_plane = hi_plane + D * D;
   const int tr = tid >> 4, tcol = tid & 15;
 #pragma unroll
   for (int i = 0; i < TS; ++i) {
