@@ -82,13 +82,15 @@ __device__ __forceinline__ void sweep_neg_inverse_128(f32x16 (&t)[4], float* lds
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         ck[r] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m[r]), 32 + kk));
-      const float ip = 1.0f / ck[kk];
+      const float ip = __builtin_amdgcn_rcpf(ck[kk]);
       const bool isk = col == 16 * p + kk;
-      const float rki = m[kk] * ip;
+      // off the pivot column: m - ck * (row k / pivot); on it (where m = ck): m / pivot
+      const float rki = isk ? 0.0f : m[kk] * ip;
+      const float sc = isk ? ip : 1.0f;
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        if (r != kk) m[r] = isk ? ck[r] * ip : __builtin_fmaf(-ck[r], rki, m[r]);
-      m[kk] = isk ? -ip : rki;
+        if (r != kk) m[r] = __builtin_fmaf(-ck[r], rki, m[r]) * sc;
+      m[kk] = isk ? -ip : m[kk] * ip;
     }
     // 3. this wave's 32 columns of the swept panel
     if (lane < 32) {
@@ -97,12 +99,20 @@ __device__ __forceinline__ void sweep_neg_inverse_128(f32x16 (&t)[4], float* lds
     }
     __syncthreads();
     // 4. M -= P^T W on the accumulator tiles (k = 2s + l/32 per 32x32x2 MFMA)
+    {
+      float a[8], bw[8][4];  // all operands first, so the LDS reads overlap
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const int k = 2 * s + h;
-      const float a = -0.5f * (P[k * kPbs + 32 * wave + l32] + Pc[k * kPbs + 32 * wave + l32]);
+      for (int s = 0; s < 8; ++s) {
+        const int k = 2 * s + h;
+        a[s] = -0.5f * (P[k * kPbs + 32 * wave + l32] + Pc[k * kPbs + 32 * wave + l32]);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) t[c] = mfma32_f32(a, Wb[k * kPbs + 32 * c + l32], t[c]);
+        for (int c = 0; c < 4; ++c) bw[s][c] = Wb[k * kPbs + 32 * c + l32];
+      }
+      __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the MFMA chain
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) t[c] = mfma32_f32(a[s], bw[s][c], t[c]);
     }
     // 5. panel rows become W (S in the pivot block), panel columns W^T
     if (wave == wo) {
