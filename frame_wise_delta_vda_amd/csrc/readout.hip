@@ -66,15 +66,18 @@ readout_bf16_kernel(const uint16_t* __restrict__ q, const float* __restrict__ xf
   const int srow = tid / C::OCH, sch = tid % C::OCH;
 
   uint4 pfa[C::QLD], pfb[C::QLD];
+  // Q tiles load through a buffer descriptor bounded by the frame's last row: rows past
+  // it read as zero (their outputs are not stored), so the loads carry no branch and the
+  // tile two ahead stays in flight.
   auto load_tile = [&](int64_t tile, uint4 (&dst)[C::QLD]) {
     const int64_t frame = tile / tiles_per_frame;
     const int64_t tok0 = (tile % tiles_per_frame) * C::TT;
-    const uint16_t* base = q + (frame * n + tok0) * D + lch * 8;
+    const int64_t rows = n - tok0 < C::TT ? n - tok0 : C::TT;
+    const auto qrsrc = make_rsrc(q + (frame * n + tok0) * D, uint32_t(rows * D * 2));
 #pragma unroll
     for (int i = 0; i < C::QLD; ++i) {
       const int r = i * RPI + lrow;
-      dst[i] = make_uint4(0, 0, 0, 0);
-      if (tok0 + r < n) dst[i] = *reinterpret_cast<const uint4*>(base + int64_t(r) * D);
+      dst[i] = buffer_load16(qrsrc, uint32_t(r * D * 2 + lch * 16));
     }
   };
 
@@ -109,7 +112,7 @@ readout_bf16_kernel(const uint16_t* __restrict__ q, const float* __restrict__ xf
 #pragma unroll
     for (int i = 0; i < C::QLD; ++i)
       *reinterpret_cast<uint4*>(qs + (i * RPI + lrow) * C::QROW + lch * 16) = pf[i];
-    if (tile + 2 < t_last) load_tile(tile + 2, pf);
+    load_tile(tile + 2 < t_last ? tile + 2 : t_last - 1, pf);  // unconditional: no phi, no copy
     __syncthreads();
     if (mfma_wave) {
 #pragma unroll
@@ -134,18 +137,20 @@ readout_bf16_kernel(const uint16_t* __restrict__ q, const float* __restrict__ xf
       }
     }
     __syncthreads();
-    uint16_t* obase = out + (frame * n + tok0) * DV + sch * 8;
+    // stores through a buffer descriptor bounded by the frame's last row: rows past it
+    // are dropped by the hardware range check, without a branch
+    const int64_t rows = n - tok0 < C::TT ? n - tok0 : C::TT;
+    const auto orsrc = make_rsrc(out + (frame * n + tok0) * DV, uint32_t(rows * DV * 2));
 #pragma unroll
     for (int i = 0; i < C::OST; ++i) {
       const int r = i * SRPI + srow;
-      if (tok0 + r < n)
-        *reinterpret_cast<uint4*>(obase + int64_t(r) * DV) =
-            *reinterpret_cast<const uint4*>(os + r * C::OROW + sch * 16);
+      buffer_store16(orsrc, uint32_t(r * DV * 2 + sch * 16),
+                     *reinterpret_cast<const uint4*>(os + r * C::OROW + sch * 16));
     }
   };
 
   load_tile(t_first, pfa);
-  if (t_first + 1 < t_last) load_tile(t_first + 1, pfb);
+  load_tile(t_first + 1 < t_last ? t_first + 1 : t_first, pfb);
   for (int64_t tile = t_first; tile < t_last; tile += 2) {
     step(tile, pfa);
     if (tile + 1 < t_last) step(tile + 1, pfb);
