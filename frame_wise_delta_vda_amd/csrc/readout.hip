@@ -14,31 +14,35 @@
 namespace vda {
 namespace {
 
-// bfloat16 path.  Each workgroup owns a contiguous range of 64-token tiles (a tile
-// never straddles two frames) and keeps the W^T fragments of the current frame in
-// registers.  Q tiles are loaded with 16-byte loads where one workgroup instruction
-// covers whole rows (4 KB contiguous), staged through padded LDS, and read back as
-// MFMA operands; each wave computes O^T = W^T Q^T for one 32-wide output-column block
-// (32x32x16 bf16 MFMA); the bf16 O tile goes back through LDS so the stores are whole
-// rows as well.  The next two tiles are always in flight in registers.
+// bfloat16 path.  Persistent workgroups, each owning a contiguous range of 64-token
+// tiles (a tile never straddles two frames).  Wave w of a workgroup takes tokens
+// 16w..16w+15 of every tile and works alone -- there is no workgroup barrier per tile,
+// only when the frame changes:
+//  - W^T of the frame (bf16) is built once per workgroup in LDS and each wave keeps all
+//    of its 16x16x32 MFMA fragments in registers;
+//  - the wave's Q rows are loaded straight into MFMA operands (lane: token l%16, eight
+//    consecutive features), two tiles ahead;
+//  - O^T = W^T Q^T goes through a wave-private LDS patch so the stores are whole rows
+//    (1 KB contiguous per wave instruction).
+// Q and O are streamed with the non-temporal cache policy, through buffer descriptors
+// bounded by the frame's last row, so ragged frame ends need no branch.
 template <int D, int DV>
 struct ReadBf16 {
-  static constexpr int TT = 64;                 // tokens per tile
-  static constexpr int QROW = D * 2 + 16;       // bytes per LDS row of Q (padded)
-  static constexpr int OROW = DV * 2 + 16;      // bytes per LDS row of O
+  static constexpr int TT = 64;                 // tokens per tile (16 per wave)
+  static constexpr int KS = D / 32;             // k-steps of the 16x16x32 MFMA
+  static constexpr int NBF = DV / 16;           // 16-feature output blocks
   static constexpr int WROW = D + 8;            // bf16 per LDS row of W^T
-  static constexpr int QCH = D / 8, OCH = DV / 8;        // 16-byte chunks per row
-  static constexpr int QLD = TT * QCH / kThreads;        // 16-byte loads per thread per tile
-  static constexpr int OST = TT * OCH / kThreads;        // 16-byte stores per thread per tile
-  static constexpr int NB = DV / 32;            // 32-wide output column blocks
-  static constexpr int NT = TT / 32;            // 32-token sub-tiles
-  static constexpr int WPB = 4 / NB < 1 ? 1 : 4 / NB;     // waves per column block
-  static constexpr int SPW = NT / WPB < 1 ? 1 : NT / WPB;  // sub-tiles per wave
-  static constexpr int KS = D / 16;             // MFMA k-steps
-  static constexpr int QS_BYTES = TT * QROW, OS_BYTES = TT * OROW, WT_BYTES = DV * WROW * 2;
-  static constexpr int LDS_BYTES = QS_BYTES + OS_BYTES + WT_BYTES;
-  static_assert(QLD >= 1 && OST >= 1, "tile too small for the workgroup");
+  static constexpr int OWROW = DV + 8;          // bf16 per LDS row of a wave's O patch
+  static constexpr int OCH = DV / 8;            // 16-byte chunks per output row
+  static constexpr int ORPI = 64 / OCH;         // output rows per wave store instruction
+  static constexpr int OST = 16 / ORPI;         // store instructions per wave per tile
+  static constexpr int WT_BYTES = DV * WROW * 2;
+  static constexpr int OW_BYTES = 16 * OWROW * 2;  // per wave
+  static constexpr int LDS_BYTES = WT_BYTES + 4 * OW_BYTES;
+  static_assert(OST >= 1, "value width too large for one wave store pass");
 };
+
+constexpr int kReadoutWgPerCu = 2;
 
 template <int D, int DV>
 __global__ void __launch_bounds__(kThreads, 2)
@@ -47,46 +51,35 @@ readout_bf16_kernel(const uint16_t* __restrict__ q, const float* __restrict__ xf
                     int64_t total_tiles, int64_t tiles_per_frame, int64_t per_wg) {
   using C = ReadBf16<D, DV>;
   extern __shared__ __align__(16) unsigned char smem[];
-  unsigned char* qs = smem;
-  unsigned char* os = smem + C::QS_BYTES;
-  uint16_t* wt = reinterpret_cast<uint16_t*>(smem + C::QS_BYTES + C::OS_BYTES);
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int col = lane & 31, half = lane >> 5;
+  uint16_t* wt = reinterpret_cast<uint16_t*>(smem);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  uint16_t* ow = reinterpret_cast<uint16_t*>(smem + C::WT_BYTES + wave * C::OW_BYTES);
+  const int c16 = lane & 15, g4 = lane >> 4;
   const int64_t t_first = blockIdx.x * per_wg;
   const int64_t t_last = (t_first + per_wg < total_tiles) ? t_first + per_wg : total_tiles;
   if (t_first >= t_last) return;
 
-  const int b = wave % C::NB;                    // output column block of this wave
-  const int sub0 = (wave / C::NB) * C::SPW;      // first 32-token sub-tile of this wave
-  const bool mfma_wave = (wave / C::NB) < C::WPB && sub0 < C::NT;
-  constexpr int RPI = kThreads / C::QCH;         // rows per load instruction
-  const int lrow = tid / C::QCH, lch = tid % C::QCH;
-  constexpr int SRPI = kThreads / C::OCH;
-  const int srow = tid / C::OCH, sch = tid % C::OCH;
-
-  uint4 pfa[C::QLD], pfb[C::QLD];
-  // Q tiles load through a buffer descriptor bounded by the frame's last row: rows past
-  // it read as zero (their outputs are not stored), so the loads carry no branch and the
-  // tile two ahead stays in flight.
-  auto load_tile = [&](int64_t tile, uint4 (&dst)[C::QLD]) {
+  // rows of this wave's 16 tokens that lie inside the frame (0 past its end)
+  auto wave_rows = [&](int64_t tok0) -> uint32_t {
+    const int64_t r = n - tok0;
+    return uint32_t(r < 0 ? 0 : (r < 16 ? r : 16));
+  };
+  auto load_q = [&](int64_t tile, uint4 (&dst)[C::KS]) {
     const int64_t frame = tile / tiles_per_frame;
-    const int64_t tok0 = (tile % tiles_per_frame) * C::TT;
-    const int64_t rows = n - tok0 < C::TT ? n - tok0 : C::TT;
-    const auto qrsrc = make_rsrc(q + (frame * n + tok0) * D, uint32_t(rows * D * 2));
+    const int64_t tok0 = (tile % tiles_per_frame) * C::TT + 16 * wave;
+    const auto rs = make_rsrc(q + (frame * n + tok0) * D, wave_rows(tok0) * D * 2);
 #pragma unroll
-    for (int i = 0; i < C::QLD; ++i) {
-      const int r = i * RPI + lrow;
-      dst[i] = buffer_load16(qrsrc, uint32_t(r * D * 2 + lch * 16));
-    }
+    for (int ks = 0; ks < C::KS; ++ks)
+      dst[ks] = buffer_load16<kCacheNt>(rs, uint32_t(c16 * D * 2 + (32 * ks + 8 * g4) * 2));
   };
 
   int64_t cur_frame = -1;
-  uint4 wf[C::KS];  // W^T fragments of this wave's column block
+  uint4 wfr[C::NBF][C::KS];  // W^T fragments: rows = output features, k = input features
+  uint4 pfa[C::KS], pfb[C::KS];
 
-  auto step = [&](int64_t tile, uint4 (&pf)[C::QLD]) {
+  auto step = [&](int64_t tile, uint4 (&pf)[C::KS]) {
     const int64_t frame = tile / tiles_per_frame;
-    const int64_t tok0 = (tile % tiles_per_frame) * C::TT;
     if (frame != cur_frame) {
       // W = (X_fwd + X_bwd) / 2 of the new frame, rounded to bf16, into LDS as W^T
       __syncthreads();
@@ -104,53 +97,39 @@ readout_bf16_kernel(const uint16_t* __restrict__ q, const float* __restrict__ xf
       }
       __syncthreads();
 #pragma unroll
-      for (int s = 0; s < C::KS; ++s)
-        wf[s] = *reinterpret_cast<const uint4*>(wt + (b * 32 + col) * C::WROW + s * 16 + half * 8);
+      for (int nb = 0; nb < C::NBF; ++nb)
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks)
+          wfr[nb][ks] = *reinterpret_cast<const uint4*>(wt + (16 * nb + c16) * C::WROW + 32 * ks + 8 * g4);
       cur_frame = frame;
     }
-    // this tile: registers -> LDS; refill the registers with the tile two ahead
+    const int64_t tok0 = (tile % tiles_per_frame) * C::TT + 16 * wave;
+    uint4 qf[C::KS];
 #pragma unroll
-    for (int i = 0; i < C::QLD; ++i)
-      *reinterpret_cast<uint4*>(qs + (i * RPI + lrow) * C::QROW + lch * 16) = pf[i];
-    load_tile(tile + 2 < t_last ? tile + 2 : t_last - 1, pf);  // unconditional: no phi, no copy
-    __syncthreads();
-    if (mfma_wave) {
+    for (int ks = 0; ks < C::KS; ++ks) qf[ks] = pf[ks];
+    load_q(tile + 2 < t_last ? tile + 2 : t_last - 1, pf);  // unconditional: no phi, no copy
+    // O^T block nb: the lane holds token c16, output features 16 nb + 4 g4 + 0..3
 #pragma unroll
-      for (int si = 0; si < C::SPW; ++si) {
-        const int sub = sub0 + si;
-        f32x16 acc = f32x16{};
+    for (int nb = 0; nb < C::NBF; ++nb) {
+      f32x4 acc = f32x4{};
 #pragma unroll
-        for (int s = 0; s < C::KS; ++s) {
-          const uint4 qv = *reinterpret_cast<const uint4*>(qs + (sub * 32 + col) * C::QROW +
-                                                           s * 32 + half * 16);
-          acc = mfma32_bf16(wf[s], qv, acc);
-        }
-        // lane holds O[token sub*32+col][b*32 + 8i + 4*half + 0..3]
-        unsigned char* orow = os + (sub * 32 + col) * C::OROW + (b * 32 + half * 4) * 2;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          uint2 pk;
-          pk.x = pack_bf16x2(acc[4 * i + 0], acc[4 * i + 1]);
-          pk.y = pack_bf16x2(acc[4 * i + 2], acc[4 * i + 3]);
-          *reinterpret_cast<uint2*>(orow + 16 * i) = pk;
-        }
-      }
+      for (int ks = 0; ks < C::KS; ++ks) acc = mfma16_bf16(wfr[nb][ks], qf[ks], acc);
+      *reinterpret_cast<uint2*>(ow + c16 * C::OWROW + 16 * nb + 4 * g4) =
+          make_uint2(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]));
     }
-    __syncthreads();
-    // stores through a buffer descriptor bounded by the frame's last row: rows past it
-    // are dropped by the hardware range check, without a branch
-    const int64_t rows = n - tok0 < C::TT ? n - tok0 : C::TT;
-    const auto orsrc = make_rsrc(out + (frame * n + tok0) * DV, uint32_t(rows * DV * 2));
+    // the patch is private to this wave, whose LDS accesses complete in order
+    const auto rs = make_rsrc(out + (frame * n + tok0) * DV, wave_rows(tok0) * DV * 2);
+    const int orow = lane / C::OCH, och = lane % C::OCH;
 #pragma unroll
-    for (int i = 0; i < C::OST; ++i) {
-      const int r = i * SRPI + srow;
-      buffer_store16(orsrc, uint32_t(r * DV * 2 + sch * 16),
-                     *reinterpret_cast<const uint4*>(os + r * C::OROW + sch * 16));
+    for (int j = 0; j < C::OST; ++j) {
+      const int r = orow + j * C::ORPI;
+      buffer_store16<kCacheNt>(rs, uint32_t(r * DV * 2 + och * 16),
+                               *reinterpret_cast<const uint4*>(ow + r * C::OWROW + och * 8));
     }
   };
 
-  load_tile(t_first, pfa);
-  load_tile(t_first + 1 < t_last ? t_first + 1 : t_first, pfb);
+  load_q(t_first, pfa);
+  load_q(t_first + 1 < t_last ? t_first + 1 : t_first, pfb);
   for (int64_t tile = t_first; tile < t_last; tile += 2) {
     step(tile, pfa);
     if (tile + 1 < t_last) step(tile + 1, pfb);
@@ -223,7 +202,7 @@ hipError_t launch_readout_t(const Problem& p, const void* q, void* out, hipStrea
     using C = ReadBf16<D, DV>;
     const int64_t tpf = (p.n + C::TT - 1) / C::TT;
     const int64_t total = frames * tpf;
-    int64_t grid = 2 * int64_t(p.num_cus);        // two persistent workgroups per CU
+    int64_t grid = kReadoutWgPerCu * int64_t(p.num_cus);  // persistent workgroups
     if (grid > total) grid = total;
     const int64_t per = (total + grid - 1) / grid;
     grid = (total + per - 1) / per;

@@ -123,11 +123,15 @@ constexpr int kBufferFlags = 0x00020000;  // raw buffer, 32-bit data format
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferFlags);
 }
+// Cache policy of a buffer access: kCacheNt marks data that is touched once (streamed).
+constexpr int kCacheDefault = 0, kCacheNt = 2;
+template <int CPOL = kCacheDefault>
 __device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0));
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, CPOL));
 }
+template <int CPOL = kCacheDefault>
 __device__ __forceinline__ void buffer_store16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, uint4 v) {
-  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)byte_off, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)byte_off, 0, CPOL);
 }
 
 // Workgroup index remap so that consecutive logical indices land on one XCD.
