@@ -126,34 +126,30 @@ def run(args):
     plan = binding.Plan(w.B, w.H, w.F, w.n, w.d, w.dv, w.T, w.lam, w.dtype)
     q, k, v, tk, tv = (dev[x] for x in W.TENSORS)
 
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record()
-        plan.stages(binding.VDA_STAGE_STATS, k=k, v=v, text_k=tk, text_v=tv)
-        if ev is not None:
-            ev[1].record()
-        plan.stages(binding.VDA_STAGE_SCAN)
-        if ev is not None:
-            ev[2].record()
-        plan.stages(binding.VDA_STAGE_READOUT, q=q, out=out)
-        if ev is not None:
-            ev[3].record()
+    def step():
+        # one whole forward pass through the C ABI: the product call, with its own
+        # schedule (the scans may overlap the last statistics launch on a second stream)
+        plan.forward(q, k, v, tk, tv, out)
 
     print(f"[bench] {w.name}: warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # per-stage durations of the timed passes themselves: the library brackets every
+    # launch with HIP events on the stream it runs on
+    plan.enable_timing(args.steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(events[i])
+        step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
     names = ["stats", "scan", "readout"]
-    kern_ms = {n: sum(events[i][j].elapsed_time(events[i][j + 1]) for i in range(args.steps)) / args.steps
-               for j, n in enumerate(names)}
+    calls, st_ms, sc_ms, rd_ms = plan.timings()
+    if calls != args.steps:
+        raise RuntimeError(f"timed {calls} of {args.steps} passes")
+    kern_ms = {"stats": st_ms, "scan": sc_ms, "readout": rd_ms}
     print(f"[bench] {w.name}: {ms_step:.3f} ms/step; " +
           ", ".join(f"{n} {kern_ms[n]:.3f} ms" for n in names), file=sys.stderr, flush=True)
 

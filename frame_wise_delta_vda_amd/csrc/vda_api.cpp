@@ -14,7 +14,27 @@ struct vda_plan_s {
   int device;
   void* workspace;
   size_t workspace_bytes;
+  // Per-stage timing of whole passes: kTimingEvents events per call in a ring of
+  // timing_capacity calls; timed_calls counts the calls recorded since the last read.
+  int timing_capacity;
+  int timed_calls;
+  hipEvent_t* timing_events;
 };
+
+namespace {
+// Event slots of one timed call: begin and end of each stage.
+enum { kEvStatsBegin, kEvStatsEnd, kEvScanBegin, kEvScanEnd, kEvReadBegin, kEvReadEnd,
+       kTimingEvents };
+
+void free_timing(vda_plan_s* plan) {
+  for (int i = 0; i < plan->timing_capacity * kTimingEvents; ++i)
+    if (plan->timing_events[i] != nullptr) (void)hipEventDestroy(plan->timing_events[i]);
+  delete[] plan->timing_events;
+  plan->timing_events = nullptr;
+  plan->timing_capacity = 0;
+  plan->timed_calls = 0;
+}
+}  // namespace
 
 namespace {
 
@@ -113,6 +133,9 @@ vda_status vda_plan_create(int64_t B, int64_t H, int64_t F, int64_t n, int64_t d
     p.xf = p.bm + bm_n;
     p.xb = p.xf + x_n;
   }
+  plan->timing_capacity = 0;
+  plan->timed_calls = 0;
+  plan->timing_events = nullptr;
   *plan_out = plan;
   return VDA_SUCCESS;
 }
@@ -120,10 +143,14 @@ vda_status vda_plan_create(int64_t B, int64_t H, int64_t F, int64_t n, int64_t d
 vda_status vda_plan_destroy(vda_plan_t plan) {
   if (plan == nullptr) return VDA_SUCCESS;
   vda_status st = VDA_SUCCESS;
-  if (plan->workspace != nullptr && hipFree(plan->workspace) != hipSuccess) {
-    (void)hipGetLastError();
-    st = VDA_ERROR_DEVICE;
-  }
+  auto check = [&](hipError_t e) {
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      st = VDA_ERROR_DEVICE;
+    }
+  };
+  free_timing(plan);
+  if (plan->workspace != nullptr) check(hipFree(plan->workspace));
   delete plan;
   return st;
 }
@@ -192,13 +219,74 @@ vda_status vda_forward_stages(vda_plan_t plan, unsigned stages, const void* q, c
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
+  // timing events of this call (whole passes only), or none
+  hipEvent_t* tev = nullptr;
+  if (stages == VDA_STAGE_ALL && plan->timing_capacity > 0 && plan->timed_calls < plan->timing_capacity)
+    tev = plan->timing_events + size_t(plan->timed_calls) * kTimingEvents;
+  auto mark = [&](int slot) {
+    if (tev != nullptr && e == hipSuccess) e = hipEventRecord(tev[slot], s);
+  };
+  mark(kEvStatsBegin);
   if (do_stats) e = vda::launch_stats(p, k, v, text_k, text_v, s);
+  mark(kEvStatsEnd);
+  mark(kEvScanBegin);
   if (e == hipSuccess && do_scan) e = vda::launch_scan(p, s);
+  mark(kEvScanEnd);
+  mark(kEvReadBegin);
   if (e == hipSuccess && do_read) e = vda::launch_readout(p, q, out, s);
+  mark(kEvReadEnd);
+  if (tev != nullptr && e == hipSuccess) ++plan->timed_calls;
   if (e != hipSuccess) {
     (void)hipGetLastError();
     return VDA_ERROR_DEVICE;
   }
+  return VDA_SUCCESS;
+}
+
+vda_status vda_plan_enable_timing(vda_plan_t plan, int capacity) {
+  if (plan == nullptr || capacity < 0 || capacity > 100000) return VDA_ERROR_INVALID_VALUE;
+  free_timing(plan);
+  if (capacity == 0) return VDA_SUCCESS;
+  const int nev = capacity * kTimingEvents;
+  plan->timing_events = new (std::nothrow) hipEvent_t[nev]();
+  if (plan->timing_events == nullptr) return VDA_ERROR_OUT_OF_MEMORY;
+  plan->timing_capacity = capacity;
+  for (int i = 0; i < nev; ++i) {
+    if (hipEventCreate(&plan->timing_events[i]) != hipSuccess) {
+      (void)hipGetLastError();
+      free_timing(plan);
+      return VDA_ERROR_DEVICE;
+    }
+  }
+  return VDA_SUCCESS;
+}
+
+vda_status vda_plan_timings(vda_plan_t plan, int* calls, float* stats_ms, float* scan_ms,
+                            float* readout_ms) {
+  if (plan == nullptr || calls == nullptr) return VDA_ERROR_INVALID_VALUE;
+  const int n = plan->timed_calls;
+  double acc[3] = {0.0, 0.0, 0.0};
+  for (int c = 0; c < n; ++c) {
+    hipEvent_t* ev = plan->timing_events + size_t(c) * kTimingEvents;
+    const int spans[3][3] = {{kEvStatsBegin, kEvStatsEnd, 0},
+                             {kEvScanBegin, kEvScanEnd, 1},
+                             {kEvReadBegin, kEvReadEnd, 2}};
+    for (const auto& sp : spans) {
+      float ms = 0.0f;
+      if (hipEventSynchronize(ev[sp[1]]) != hipSuccess ||
+          hipEventElapsedTime(&ms, ev[sp[0]], ev[sp[1]]) != hipSuccess) {
+        (void)hipGetLastError();
+        return VDA_ERROR_DEVICE;
+      }
+      acc[sp[2]] += ms;
+    }
+  }
+  *calls = n;
+  const double div = n > 0 ? double(n) : 1.0;
+  if (stats_ms) *stats_ms = float(acc[0] / div);
+  if (scan_ms) *scan_ms = float(acc[1] / div);
+  if (readout_ms) *readout_ms = float(acc[2] / div);
+  plan->timed_calls = 0;
   return VDA_SUCCESS;
 }
 

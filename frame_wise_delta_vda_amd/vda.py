@@ -62,6 +62,11 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     fp = ctypes.POINTER(ctypes.c_void_p)
     lib.vda_debug_workspace.argtypes = [c_vp, fp, fp, fp, fp]
     lib.vda_debug_workspace.restype = c_int
+    lib.vda_plan_enable_timing.argtypes = [c_vp, c_int]
+    lib.vda_plan_enable_timing.restype = c_int
+    flp = ctypes.POINTER(ctypes.c_float)
+    lib.vda_plan_timings.argtypes = [c_vp, ctypes.POINTER(c_int), flp, flp, flp]
+    lib.vda_plan_timings.restype = c_int
     if path is None:
         _lib = lib
     return lib
@@ -137,6 +142,19 @@ def vda_debug_workspace(plan):
     return tuple(p.value for p in ptrs)
 
 
+def vda_plan_enable_timing(plan, capacity: int):
+    _check(load_library().vda_plan_enable_timing(plan, capacity), "vda_plan_enable_timing")
+
+
+def vda_plan_timings(plan):
+    """(calls, stats_ms, scan_ms, readout_ms) of the timed whole passes since the last read."""
+    calls = ctypes.c_int()
+    ms = [ctypes.c_float() for _ in range(3)]
+    _check(load_library().vda_plan_timings(plan, ctypes.byref(calls), *[ctypes.byref(m) for m in ms]),
+           "vda_plan_timings")
+    return (calls.value,) + tuple(m.value for m in ms)
+
+
 class Plan:
     """Owns one vda plan; `forward` takes torch tensors in the documented layouts."""
 
@@ -184,3 +202,9 @@ class Plan:
 
     def debug_workspace(self):
         return vda_debug_workspace(self.handle)
+
+    def enable_timing(self, capacity: int):
+        vda_plan_enable_timing(self.handle, capacity)
+
+    def timings(self):
+        return vda_plan_timings(self.handle)

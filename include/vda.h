@@ -105,6 +105,21 @@ vda_status vda_forward_stages(vda_plan_t plan, unsigned stages, const void* q, c
                               const void* v, const void* text_k, const void* text_v, void* out,
                               void* stream);
 
+/* Per-stage timing of whole forward passes, for benchmarks.  After
+ * vda_plan_enable_timing(plan, capacity) with capacity > 0, each of the next `capacity`
+ * vda_forward calls brackets each stage's launch with HIP events on the stream it runs
+ * on.  capacity == 0 turns timing off; enabling again discards what was recorded.  The
+ * events are created on the current device, which must be the plan's.
+ * Errors: INVALID_VALUE (capacity < 0 or > 100000), OUT_OF_MEMORY, DEVICE. */
+vda_status vda_plan_enable_timing(vda_plan_t plan, int capacity);
+
+/* Waits for the timed calls recorded since timing was enabled or last read, and returns
+ * their number in *calls and the mean duration in milliseconds of each stage launch
+ * (statistics, scan, readout).  Any of the float pointers may be NULL.  Resets the count.
+ * Errors: INVALID_VALUE (NULL plan or calls), DEVICE. */
+vda_status vda_plan_timings(vda_plan_t plan, int* calls, float* stats_ms, float* scan_ms,
+                            float* readout_ms);
+
 /* Free the plan and its workspace.  The caller must make sure no forward pass on
  * the plan is still running (synchronise its stream first).  NULL is accepted. */
 vda_status vda_plan_destroy(vda_plan_t plan);

@@ -102,3 +102,25 @@ def test_nan_inputs_propagate_to_their_frame_only():
     o[0, 0, 1, 5] = 0
     assert np.isfinite(o).all()
     plan.close()
+
+
+def test_timing_of_whole_passes():
+    """Timing records only whole passes, at most `capacity` of them, and each stage of a
+    pass takes positive time; enabling with a bad capacity is an argument error."""
+    w = W.WORKLOADS[2].replace(H=2, F=3, n=300, T=10)
+    say("[gpu] timing")
+    dev = to_device(w, W.full_storage(w, threads=1))
+    out, plan = run_gpu(w, dev)
+    with pytest.raises(binding.VdaError):
+        plan.enable_timing(-1)
+    plan.enable_timing(2)
+    for _ in range(3):
+        run_gpu(w, dev, plan=plan, out=out)
+    plan.stages(binding.VDA_STAGE_SCAN)
+    calls, st, sc, rd = plan.timings()
+    assert calls == 2 and st > 0 and sc > 0 and rd > 0
+    assert plan.timings()[0] == 0
+    plan.enable_timing(0)
+    run_gpu(w, dev, plan=plan, out=out)
+    assert plan.timings()[0] == 0
+    plan.close()

@@ -174,3 +174,4 @@ def test_stages_compose_to_forward():
     torch.cuda.synchronize()
     assert torch.equal(full.view(torch.int16), staged.view(torch.int16))
     plan.close()
+
