@@ -229,13 +229,11 @@ scan_bf16_kernel(const uint16_t* __restrict__ ainv_planes, const float* __restri
                                              n * 8 + 4 * (g % 2)]);
   };
   auto write_r = [&](int buf, int cw, float r0, float r1, float r2, float r3) {
-    uint32_t h0, l0, h1, l1, h2, l2, h3, l3;
-    split_bf16(r0, h0, l0);
-    split_bf16(r1, h1, l1);
-    split_bf16(r2, h2, l2);
-    split_bf16(r3, h3, l3);
-    *rs_out(buf, cw, 0) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
-    *rs_out(buf, cw, 1) = make_uint2(l0 | (l1 << 16), l2 | (l3 << 16));
+    uint32_t h01, l01, h23, l23;
+    split_bf16x2(r0, r1, h01, l01);
+    split_bf16x2(r2, r3, h23, l23);
+    *rs_out(buf, cw, 0) = make_uint2(h01, h23);
+    *rs_out(buf, cw, 1) = make_uint2(l01, l23);
   };
 
   // R_0 = lam * 0 + Bm_0
@@ -252,17 +250,25 @@ scan_bf16_kernel(const uint16_t* __restrict__ ainv_planes, const float* __restri
                   float4 (&bv_fill)[C::CW]) {
     const int buf = int(s & 1);
     load_slot(s + C::NSLOT - 1, a_fill, bv_fill);
+    // every R fragment of the step in one LDS round trip, then the MFMA chains
+    uint4 rf[C::CW][C::KS][2];
+#pragma unroll
+    for (int cw = 0; cw < C::CW; ++cw)
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        rf[cw][ks][0] = *rs_frag(buf, cw, 0, ks);
+        rf[cw][ks][1] = *rs_frag(buf, cw, 1, ks);
+      }
+    __builtin_amdgcn_sched_barrier(0);
     f32x4 x[C::CW];
 #pragma unroll
     for (int cw = 0; cw < C::CW; ++cw) {
       f32x4 hh = f32x4{}, hl = f32x4{}, lh = f32x4{};
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
-        const uint4 rh = *rs_frag(buf, cw, 0, ks);
-        const uint4 rl = *rs_frag(buf, cw, 1, ks);
-        hh = mfma16_bf16(a[ks][0], rh, hh);
-        hl = mfma16_bf16(a[ks][0], rl, hl);
-        lh = mfma16_bf16(a[ks][1], rh, lh);
+        hh = mfma16_bf16(a[ks][0], rf[cw][ks][0], hh);
+        hl = mfma16_bf16(a[ks][0], rf[cw][ks][1], hl);
+        lh = mfma16_bf16(a[ks][1], rf[cw][ks][0], lh);
       }
       x[cw] = hh + (hl + lh);
     }

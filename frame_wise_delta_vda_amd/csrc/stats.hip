@@ -277,14 +277,12 @@ stats_bf16_kernel(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v
     for (int c = 0; c < 4; ++c)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        uint32_t h0, l0, h1, l1, h2, l2, h3, l3;
-        split_bf16(-t[c][4 * q + 0], h0, l0);
-        split_bf16(-t[c][4 * q + 1], h1, l1);
-        split_bf16(-t[c][4 * q + 2], h2, l2);
-        split_bf16(-t[c][4 * q + 3], h3, l3);
+        uint32_t h01, l01, h23, l23;
+        split_bf16x2(-t[c][4 * q + 0], -t[c][4 * q + 1], h01, l01);
+        split_bf16x2(-t[c][4 * q + 2], -t[c][4 * q + 3], h23, l23);
         const int off = frag_index(32 * c + l32, 32 * wave + 8 * q + 4 * (lane >> 5), D);
-        *reinterpret_cast<uint2*>(hi_plane + off) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
-        *reinterpret_cast<uint2*>(lo_plane + off) = make_uint2(l0 | (l1 << 16), l2 | (l3 << 16));
+        *reinterpret_cast<uint2*>(hi_plane + off) = make_uint2(h01, h23);
+        *reinterpret_cast<uint2*>(lo_plane + off) = make_uint2(l01, l23);
       }
     return;
   }
@@ -320,11 +318,7 @@ stats_bf16_kernel(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v
     uint32_t hw[TS / 2], lw[TS / 2];
 #pragma unroll
     for (int j = 0; j < TS; j += 2) {
-      uint32_t h0, l0, h1, l1;
-      split_bf16(a[i][j], h0, l0);
-      split_bf16(a[i][j + 1], h1, l1);
-      hw[j / 2] = h0 | (h1 << 16);
-      lw[j / 2] = l0 | (l1 << 16);
+      split_bf16x2(a[i][j], a[i][j + 1], hw[j / 2], lw[j / 2]);
     }
     const int off = frag_index(tr * TS + i, tcol * TS, D);
     if constexpr (TS == 8) {

@@ -42,25 +42,28 @@ __device__ __forceinline__ int mfma32_row(int r, int lane) {
   return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
 }
 
-// float -> bfloat16 bits, round to nearest even; NaN stays NaN.
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
-  uint32_t u = __builtin_bit_cast(uint32_t, x);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+// float -> bfloat16, round to nearest even, NaN stays NaN: gfx950's packed conversion
+// (v_cvt_pk_bf16_f32), one instruction for two values and no branch.
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+
+// bits of (bf16(lo), bf16(hi)), lo in the low half
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const f32x2v v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2v));
 }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
-}
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) { return pack_bf16x2(x, 0.0f) & 0xffffu; }
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
   return __builtin_bit_cast(float, b << 16);
 }
 
-// Split x into bfloat16 hi + lo with x - hi - lo = O(2^-17 |x|): hi = rne(x), lo = rne(x - hi).
-__device__ __forceinline__ void split_bf16(float x, uint32_t& hi, uint32_t& lo) {
-  hi = f32_to_bf16_bits(x);
-  lo = f32_to_bf16_bits(x - bf16_bits_to_f32(hi));
+// Split two floats into bfloat16 hi + lo pairs, x - hi - lo = O(2^-17 |x|):
+// hi = rne(x), lo = rne(x - hi); each result packs (value a, value b).
+__device__ __forceinline__ void split_bf16x2(float a, float b, uint32_t& hi, uint32_t& lo) {
+  hi = pack_bf16x2(a, b);
+  lo = pack_bf16x2(a - bf16_bits_to_f32(hi & 0xffffu), b - bf16_bits_to_f32(hi >> 16));
 }
 
 typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
