@@ -147,6 +147,10 @@ struct StatsBf16 {
   static constexpr int NK = D / 32, NV = DV / 32, NC = NK + NV;
   static constexpr int RPW = 4 / NK;             // waves sharing one 32-row block of G
   static constexpr int CPW = (NC + RPW - 1) / RPW;  // 32x32 output tiles per wave
+  // d = 128: wave j accumulates column tile j of G and of Bm over all four row blocks
+  // (6 fragment reads per k-step instead of 9); other widths: wave row blocks as above
+  static constexpr bool COLW = D == 128;
+  static constexpr int ACC = COLW ? 8 : CPW;
   static constexpr int NSEG = (D + DV) / 8;      // 8-feature segments per token (K then V)
   static constexpr int BUF = (D + DV) * ROW;     // bf16 elements per staging buffer
   static constexpr int STAGE_BYTES = 2 * BUF * 2;
@@ -195,9 +199,9 @@ stats_bf16_kernel(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v
   const int rb = wave % C::NK;
   const int cofs = wave / C::NK;
 
-  f32x16 acc[C::CPW];
+  f32x16 acc[C::ACC];
 #pragma unroll
-  for (int j = 0; j < C::CPW; ++j) acc[j] = f32x16{};
+  for (int j = 0; j < C::ACC; ++j) acc[j] = f32x16{};
 
   const int64_t nchunks = (ntok + C::TC - 1) / C::TC;
   uint4 r[8];
@@ -233,15 +237,28 @@ stats_bf16_kernel(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v
 #pragma unroll
     for (int ks = 0; ks < C::TC / 16; ++ks) {
       const int col = ks * 16 + (lane >> 5) * 8;
-      const uint4 a = *reinterpret_cast<const uint4*>(kt + (rb * 32 + (lane & 31)) * C::ROW + col);
+      if constexpr (C::COLW) {
+        // acc[rb] = G(rb, wave), acc[4 + rb] = Bm(rb, wave)
+        const uint4 bk = *reinterpret_cast<const uint4*>(kt + (wave * 32 + (lane & 31)) * C::ROW + col);
+        uint4 bv = make_uint4(0, 0, 0, 0);
+        if (wave < C::NV) bv = *reinterpret_cast<const uint4*>(vt + (wave * 32 + (lane & 31)) * C::ROW + col);
 #pragma unroll
-      for (int jj = 0; jj < C::CPW; ++jj) {
-        const int c = jj * C::RPW + cofs;
-        if (c < C::NC) {
-          const uint16_t* bs = c < C::NK ? kt + (c * 32 + (lane & 31)) * C::ROW
-                                         : vt + ((c - C::NK) * 32 + (lane & 31)) * C::ROW;
-          const uint4 b = *reinterpret_cast<const uint4*>(bs + col);
-          acc[jj] = mfma32_bf16(a, b, acc[jj]);
+        for (int rbi = 0; rbi < 4; ++rbi) {
+          const uint4 a = *reinterpret_cast<const uint4*>(kt + (rbi * 32 + (lane & 31)) * C::ROW + col);
+          acc[rbi] = mfma32_bf16(a, bk, acc[rbi]);
+          if (wave < C::NV) acc[4 + rbi] = mfma32_bf16(a, bv, acc[4 + rbi]);
+        }
+      } else {
+        const uint4 a = *reinterpret_cast<const uint4*>(kt + (rb * 32 + (lane & 31)) * C::ROW + col);
+#pragma unroll
+        for (int jj = 0; jj < C::CPW; ++jj) {
+          const int c = jj * C::RPW + cofs;
+          if (c < C::NC) {
+            const uint16_t* bs = c < C::NK ? kt + (c * 32 + (lane & 31)) * C::ROW
+                                           : vt + ((c - C::NK) * 32 + (lane & 31)) * C::ROW;
+            const uint4 b = *reinterpret_cast<const uint4*>(bs + col);
+            acc[jj] = mfma32_bf16(a, b, acc[jj]);
+          }
         }
       }
     }
@@ -256,19 +273,29 @@ stats_bf16_kernel(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v
     // ---- epilogue (d = 128): Bm tiles to the workspace; lam I + G inverted in the
     // accumulators by the blocked sweep; A^{-1} = -(swept matrix) written out.
     const int l32 = lane & 31;
+    if (wave < C::NV) {
 #pragma unroll
-    for (int jj = C::NK; jj < C::CPW; ++jj)
-#pragma unroll
-      for (int e = 0; e < 16; ++e)
-        bmo[blk_index(rb * 32 + mfma32_row(e, lane), (jj - C::NK) * 32 + l32, D)] = acc[jj][e];
-    f32x16 t[4] = {acc[0], acc[1], acc[2], acc[3]};
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-      if (c == wave) {
+      for (int rbi = 0; rbi < 4; ++rbi)
 #pragma unroll
         for (int e = 0; e < 16; ++e)
-          if (mfma32_row(e, lane) == l32) t[c][e] += lam;
+          bmo[blk_index(rbi * 32 + mfma32_row(e, lane), wave * 32 + l32, D)] = acc[4 + rbi][e];
+    }
+    // G column block -> LDS -> G row block in the accumulator layout the sweep works on
+    float* gsm = reinterpret_cast<float*>(smem);
+#pragma unroll
+    for (int rbi = 0; rbi < 4; ++rbi)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) gsm[(rbi * 32 + mfma32_row(e, lane)) * C::GS + wave * 32 + l32] = acc[rbi][e];
+    __syncthreads();
+    f32x16 t[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int row = wave * 32 + mfma32_row(e, lane), colg = c * 32 + l32;
+        t[c][e] = gsm[row * C::GS + colg] + (row == colg ? lam : 0.0f);
       }
+    __syncthreads();
     static_assert(6 * 16 * kPbs * 4 <= C::MAIN_BYTES, "sweep buffers exceed the staging area");
     sweep_neg_inverse_128(t, reinterpret_cast<float*>(smem), wave, lane);
     // A^{-1} is symmetric: lane l's column j of tile c is row j of A^{-1}, and its
