@@ -73,25 +73,29 @@ __device__ __forceinline__ void sweep_neg_inverse_128(f32x16 (&t)[4], float* lds
     // lane 32 + kk by readlane.  Afterwards the panel holds W off the pivot columns and
     // S = -M[K,K]^{-1} on them.
     const int col = lane < 32 ? 32 * wave + lane : 16 * p + c16;
-    float m[16];
+    // The pivot column's own update (m -> m / pivot) is kept as a per-lane scale sc and
+    // applied once after the 16 steps: a lane stores its column divided by sc, and every
+    // later step's update m -= ck * (m[kk] / pivot) holds for the stored values as well.
+    float m[16], sc = 1.0f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) m[r] = 0.5f * (P[r * kPbs + col] + Pc[r * kPbs + col]);
 #pragma unroll
     for (int kk = 0; kk < 16; ++kk) {
-      float ck[16];
+      float ck[16];  // the pivot column, not yet pivoted, so stored unscaled
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         ck[r] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m[r]), 32 + kk));
       const float ip = __builtin_amdgcn_rcpf(ck[kk]);
       const bool isk = col == 16 * p + kk;
-      // off the pivot column: m - ck * (row k / pivot); on it (where m = ck): m / pivot
       const float rki = isk ? 0.0f : m[kk] * ip;
-      const float sc = isk ? ip : 1.0f;
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        if (r != kk) m[r] = __builtin_fmaf(-ck[r], rki, m[r]) * sc;
-      m[kk] = isk ? -ip : m[kk] * ip;
+        if (r != kk) m[r] = __builtin_fmaf(-ck[r], rki, m[r]);
+      m[kk] = isk ? -1.0f : m[kk] * ip;
+      sc = isk ? sc * ip : sc;
     }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) m[r] *= sc;
     // 3. this wave's 32 columns of the swept panel
     if (lane < 32) {
 #pragma unroll
