@@ -154,6 +154,8 @@ struct StatsBf16 {
   // d = 128: wave j accumulates column tile j of G and of Bm over all four row blocks
   // (6 fragment reads per k-step instead of 9); other widths: wave row blocks as above
   static constexpr bool COLW = D == 128;
+  // d = dv = 128: every thread loads, and waves split evenly between K and V
+  static constexpr bool DEEP = D == 128 && DV == 128;
   static constexpr int ACC = COLW ? 8 : CPW;
   static constexpr int NSEG = (D + DV) / 8;      // 8-feature segments per token (K then V)
   static constexpr int BUF = (D + DV) * ROW;     // bf16 elements per staging buffer
@@ -190,10 +192,11 @@ stats_bf16_kernel(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v
     ntok = n;
   }
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // loader role: token group tg (8 tokens), 8-feature segment seg of K (seg < D/8) or V
   const int tg = tid & 7, seg = tid >> 3;
-  const bool loader = seg < C::NSEG;
+  const bool loader = C::DEEP || seg < C::NSEG;
   const bool seg_is_k = seg < D / 8;
   const uint16_t* src = seg_is_k ? kp + seg * 8 : vp + (seg - D / 8) * 8;
   const int64_t src_stride = seg_is_k ? D : DV;
@@ -208,9 +211,8 @@ stats_bf16_kernel(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v
   for (int j = 0; j < C::ACC; ++j) acc[j] = f32x16{};
 
   const int64_t nchunks = (ntok + C::TC - 1) / C::TC;
-  uint4 r[8];
 
-  auto load_chunk = [&](int64_t ch) {
+  auto load_chunk = [&](int64_t ch, uint4 (&r)[8]) {
     const int64_t t0 = ch * C::TC + tg * 8;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -219,7 +221,7 @@ stats_bf16_kernel(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v
         r[i] = *reinterpret_cast<const uint4*>(src + (t0 + i) * src_stride);
     }
   };
-  auto store_chunk = [&](int buf) {
+  auto store_chunk = [&](int buf, const uint4 (&r)[8]) {
     if (!loader) return;
     uint4 c[8];
     transpose8x8_b16(r, c);
@@ -228,14 +230,7 @@ stats_bf16_kernel(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v
     for (int j = 0; j < 8; ++j) *reinterpret_cast<uint4*>(dst + j * C::ROW) = c[j];
   };
 
-  if (nchunks > 0) {
-    load_chunk(0);
-    store_chunk(0);
-  }
-  __syncthreads();
-  for (int64_t ch = 0; ch < nchunks; ++ch) {
-    const int buf = int(ch & 1);
-    if (ch + 1 < nchunks) load_chunk(ch + 1);
+  auto mult_chunk = [&](int buf) {
     const uint16_t* kt = stage + buf * C::BUF;
     const uint16_t* vt = kt + D * C::ROW;
 #pragma unroll
@@ -245,12 +240,12 @@ stats_bf16_kernel(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v
         // acc[rb] = G(rb, wave), acc[4 + rb] = Bm(rb, wave)
         const uint4 bk = *reinterpret_cast<const uint4*>(kt + (wave * 32 + (lane & 31)) * C::ROW + col);
         uint4 bv = make_uint4(0, 0, 0, 0);
-        if (wave < C::NV) bv = *reinterpret_cast<const uint4*>(vt + (wave * 32 + (lane & 31)) * C::ROW + col);
+        if (C::NV >= 4 || wave < C::NV) bv = *reinterpret_cast<const uint4*>(vt + (wave * 32 + (lane & 31)) * C::ROW + col);
 #pragma unroll
         for (int rbi = 0; rbi < 4; ++rbi) {
           const uint4 a = *reinterpret_cast<const uint4*>(kt + (rbi * 32 + (lane & 31)) * C::ROW + col);
           acc[rbi] = mfma32_bf16(a, bk, acc[rbi]);
-          if (wave < C::NV) acc[4 + rbi] = mfma32_bf16(a, bv, acc[4 + rbi]);
+          if (C::NV >= 4 || wave < C::NV) acc[4 + rbi] = mfma32_bf16(a, bv, acc[4 + rbi]);
         }
       } else {
         const uint4 a = *reinterpret_cast<const uint4*>(kt + (rb * 32 + (lane & 31)) * C::ROW + col);
@@ -266,8 +261,57 @@ stats_bf16_kernel(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v
         }
       }
     }
-    if (ch + 1 < nchunks) store_chunk(buf ^ 1);
+  };
+
+  if constexpr (C::DEEP) {
+    // Two chunks in flight per thread.  Waves 0-1 load K, waves 2-3 V (one 8-feature
+    // segment and 8 tokens per lane); the buffer descriptor spans the frame, so loads
+    // past its last token return zeros and a ragged or missing chunk multiplies in
+    // nothing.
+    const auto rs = make_rsrc(wave < 2 ? kp : vp, uint32_t(ntok * 128 * 2));
+    const uint32_t voff = uint32_t((tg * 8 * 128 + (seg & 15) * 8) * 2);
+    uint4 ra[8], rn[8];
+    auto load_deep = [&](int64_t ch, uint4 (&r)[8]) {
+      // chunk indices past the end stay at nchunks: their bytes are past the frame
+      const uint32_t base = voff + uint32_t((ch < nchunks ? ch : nchunks) * C::TC * 256);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) r[i] = buffer_load16<kCacheNt>(rs, base + uint32_t(i * 256));
+    };
+    load_deep(0, ra);
+    load_deep(1, rn);
+    store_chunk(0, ra);
     __syncthreads();
+    // The scheduling barriers keep each phase in order -- loads issued first, the
+    // transposes (which wait for the chunk loaded a phase earlier) last -- so that a
+    // chunk's loads have a whole phase of multiplies to land.
+    for (int64_t ch = 0; ch < nchunks; ch += 2) {
+      load_deep(ch + 2, ra);
+      __builtin_amdgcn_sched_barrier(0);
+      mult_chunk(0);
+      __builtin_amdgcn_sched_barrier(0);
+      store_chunk(1, rn);
+      __syncthreads();
+      load_deep(ch + 3, rn);
+      __builtin_amdgcn_sched_barrier(0);
+      mult_chunk(1);
+      __builtin_amdgcn_sched_barrier(0);
+      store_chunk(0, ra);
+      __syncthreads();
+    }
+  } else {
+    uint4 r[8];
+    if (nchunks > 0) {
+      load_chunk(0, r);
+      store_chunk(0, r);
+    }
+    __syncthreads();
+    for (int64_t ch = 0; ch < nchunks; ++ch) {
+      const int buf = int(ch & 1);
+      if (ch + 1 < nchunks) load_chunk(ch + 1, r);
+      mult_chunk(buf);
+      if (ch + 1 < nchunks) store_chunk(buf ^ 1, r);
+      __syncthreads();
+    }
   }
 
   float* bmo = bm + (bh * F1 + fi) * int64_t(D) * DV;

@@ -77,6 +77,8 @@ vda_status vda_plan_create(int64_t B, int64_t H, int64_t F, int64_t n, int64_t d
   if (!(std::isfinite(lambda) && lambda > 0.0f)) return VDA_ERROR_INVALID_VALUE;
   if (dtype != VDA_DTYPE_F32 && dtype != VDA_DTYPE_BF16) return VDA_ERROR_NOT_SUPPORTED;
   if (!supported_width(d) || !supported_width(dv)) return VDA_ERROR_NOT_SUPPORTED;
+  // a frame (or the text) is addressed with 32-bit byte offsets
+  if (n > vda::kMaxFrameTokens || T > vda::kMaxFrameTokens) return VDA_ERROR_NOT_SUPPORTED;
 
   // Every element count the kernels index must fit in int64; grids are 1-D.
   int64_t bh, frames, tok, elems, ws_frames, ws_elems, tmp;

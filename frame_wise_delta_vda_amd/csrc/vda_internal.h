@@ -7,6 +7,10 @@
 
 namespace vda {
 
+// Largest token count of one frame or of the text: a frame's K and V are read through
+// buffer descriptors with 32-bit byte offsets (up to 256 B per token, plus a chunk).
+constexpr int64_t kMaxFrameTokens = (int64_t(1) << 24) - 256;
+
 // Problem shape and float32 workspace of one plan.
 struct Problem {
   int64_t B, H, F, n, d, dv, T;

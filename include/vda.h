@@ -55,7 +55,7 @@ typedef enum {
 typedef enum {
   VDA_SUCCESS = 0,
   VDA_ERROR_INVALID_VALUE = 1,  /* bad size, lambda, NULL pointer, aliasing, wrong device */
-  VDA_ERROR_NOT_SUPPORTED = 2,  /* d or dv outside {32, 64, 128}, unknown dtype */
+  VDA_ERROR_NOT_SUPPORTED = 2,  /* d or dv outside {32, 64, 128}, unknown dtype, n or T too large */
   VDA_ERROR_MISALIGNED = 3,     /* a tensor pointer is not 16-byte aligned */
   VDA_ERROR_OUT_OF_MEMORY = 4,  /* workspace allocation failed */
   VDA_ERROR_DEVICE = 5          /* a HIP runtime call or kernel launch failed */
@@ -71,6 +71,7 @@ typedef enum {
 
 /* Create a plan for one problem shape.
  *   B, H, F, n, T >= 0: batch, heads, frames, spatial tokens per frame, text tokens.
+ *     n and T are at most 16776960 (2^24 - 256); larger gives NOT_SUPPORTED.
  *     B*H*F*n == 0 gives a plan whose forward pass has no output element: it does
  *     nothing, reads no pointer and returns VDA_SUCCESS.  T == 0 means no text: the
  *     text state is zero and text_k / text_v may be NULL.

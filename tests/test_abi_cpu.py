@@ -47,6 +47,8 @@ def _create(lib, *args):
     ((1, 1, 1, 1, 32, 32, 0, math.nan, 1), binding.VDA_ERROR_INVALID_VALUE),
     ((1, 1, 1, 1, 32, 32, 0, math.inf, 1), binding.VDA_ERROR_INVALID_VALUE),
     ((2**40, 2**40, 1, 1, 32, 32, 0, 1.0, 1), binding.VDA_ERROR_INVALID_VALUE),  # overflow
+    ((1, 1, 1, 2**24, 32, 32, 0, 1.0, 1), binding.VDA_ERROR_NOT_SUPPORTED),  # frame too long
+    ((1, 1, 1, 1, 32, 32, 2**24, 1.0, 1), binding.VDA_ERROR_NOT_SUPPORTED),  # text too long
 ])
 def test_plan_create_rejects_bad_arguments(lib, args, expected):
     st, h = _create(lib, *args)
