@@ -16,10 +16,10 @@ namespace {
 
 // bfloat16 path.  Persistent workgroups, each owning a contiguous range of 64-token
 // tiles (a tile never straddles two frames).  Wave w of a workgroup takes tokens
-// 16w..16w+15 of every tile and works alone -- there is no workgroup barrier per tile,
-// only when the frame changes:
-//  - W^T of the frame (bf16) is built once per workgroup in LDS and each wave keeps all
-//    of its 16x16x32 MFMA fragments in registers;
+// 16w..16w+15 of every tile and works alone -- there is no workgroup barrier at all:
+//  - at a frame change each wave forms all of its W^T operand fragments in registers
+//    from the two bf16 states, which the scan stores in exactly that operand order
+//    (state_index): one 16-byte load per state and fragment, mean in fp32, one rounding;
 //  - the wave's Q rows are loaded straight into MFMA operands (lane: token l%16, eight
 //    consecutive features), two tiles ahead;
 //  - O^T = W^T Q^T goes through a wave-private LDS patch so the stores are whole rows
@@ -31,14 +31,12 @@ struct ReadBf16 {
   static constexpr int TT = 64;                 // tokens per tile (16 per wave)
   static constexpr int KS = D / 32;             // k-steps of the 16x16x32 MFMA
   static constexpr int NBF = DV / 16;           // 16-feature output blocks
-  static constexpr int WROW = D + 8;            // bf16 per LDS row of W^T
   static constexpr int OWROW = DV + 8;          // bf16 per LDS row of a wave's O patch
   static constexpr int OCH = DV / 8;            // 16-byte chunks per output row
   static constexpr int ORPI = 64 / OCH;         // output rows per wave store instruction
   static constexpr int OST = 16 / ORPI;         // store instructions per wave per tile
-  static constexpr int WT_BYTES = DV * WROW * 2;
   static constexpr int OW_BYTES = 16 * OWROW * 2;  // per wave
-  static constexpr int LDS_BYTES = WT_BYTES + 4 * OW_BYTES;
+  static constexpr int LDS_BYTES = 4 * OW_BYTES;
   static_assert(OST >= 1, "value width too large for one wave store pass");
 };
 
@@ -46,15 +44,14 @@ constexpr int kReadoutWgPerCu = 2;
 
 template <int D, int DV>
 __global__ void __launch_bounds__(kThreads, 2)
-readout_bf16_kernel(const uint16_t* __restrict__ q, const float* __restrict__ xf,
-                    const float* __restrict__ xb, uint16_t* __restrict__ out, int64_t n,
+readout_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ xf,
+                    const uint16_t* __restrict__ xb, uint16_t* __restrict__ out, int64_t n,
                     int64_t total_tiles, int64_t tiles_per_frame, int64_t per_wg) {
   using C = ReadBf16<D, DV>;
   extern __shared__ __align__(16) unsigned char smem[];
-  uint16_t* wt = reinterpret_cast<uint16_t*>(smem);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  uint16_t* ow = reinterpret_cast<uint16_t*>(smem + C::WT_BYTES + wave * C::OW_BYTES);
+  uint16_t* ow = reinterpret_cast<uint16_t*>(smem + wave * C::OW_BYTES);
   const int c16 = lane & 15, g4 = lane >> 4;
   const int64_t t_first = blockIdx.x * per_wg;
   const int64_t t_last = (t_first + per_wg < total_tiles) ? t_first + per_wg : total_tiles;
@@ -81,26 +78,28 @@ readout_bf16_kernel(const uint16_t* __restrict__ q, const float* __restrict__ xf
   auto step = [&](int64_t tile, uint4 (&pf)[C::KS]) {
     const int64_t frame = tile / tiles_per_frame;
     if (frame != cur_frame) {
-      // W = (X_fwd + X_bwd) / 2 of the new frame, rounded to bf16, into LDS as W^T
-      __syncthreads();
-      const float* xff = xf + frame * int64_t(D) * DV;
-      const float* xbf = xb + frame * int64_t(D) * DV;
-      // the states are stored blocked: each float4 holds rows row..row+3 of one column
-      for (int i4 = tid; i4 < D * DV / 4; i4 += kThreads) {
-        const int blk = i4 >> 6, g = (i4 >> 4) & 3, col = (blk / (D / 16)) * 16 + (i4 & 15);
-        const int row = (blk % (D / 16)) * 16 + 4 * g;
-        const float4 a = reinterpret_cast<const float4*>(xff)[i4];
-        const float4 c = reinterpret_cast<const float4*>(xbf)[i4];
-        *reinterpret_cast<uint2*>(wt + col * C::WROW + row) =
-            make_uint2(pack_bf16x2(0.5f * (a.x + c.x), 0.5f * (a.y + c.y)),
-                       pack_bf16x2(0.5f * (a.z + c.z), 0.5f * (a.w + c.w)));
+      // W = (X_fwd + X_bwd) / 2 of the new frame, rounded once to bf16; fragment (nb, ks)
+      // of both states is the 1 KB at ((nb * KS + ks) * 64 + lane) * 8
+      const uint4* sf = reinterpret_cast<const uint4*>(xf + frame * int64_t(D) * DV) + lane;
+      const uint4* sb = reinterpret_cast<const uint4*>(xb + frame * int64_t(D) * DV) + lane;
+      // two output blocks at a time, so the loads in flight stay within the registers
+      constexpr int NG = C::NBF >= 2 ? 2 : 1;
+#pragma unroll
+      for (int nb0 = 0; nb0 < C::NBF; nb0 += NG) {
+        uint4 a[NG][C::KS], b[NG][C::KS];
+#pragma unroll
+        for (int i = 0; i < NG; ++i)
+#pragma unroll
+          for (int ks = 0; ks < C::KS; ++ks) {
+            a[i][ks] = sf[((nb0 + i) * C::KS + ks) * 64];
+            b[i][ks] = sb[((nb0 + i) * C::KS + ks) * 64];
+          }
+#pragma unroll
+        for (int i = 0; i < NG; ++i)
+#pragma unroll
+          for (int ks = 0; ks < C::KS; ++ks) wfr[nb0 + i][ks] = mean_bf16x8(a[i][ks], b[i][ks]);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __syncthreads();
-#pragma unroll
-      for (int nb = 0; nb < C::NBF; ++nb)
-#pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks)
-          wfr[nb][ks] = *reinterpret_cast<const uint4*>(wt + (16 * nb + c16) * C::WROW + 32 * ks + 8 * g4);
       cur_frame = frame;
     }
     const int64_t tok0 = (tile % tiles_per_frame) * C::TT + 16 * wave;
@@ -213,7 +212,8 @@ hipError_t launch_readout_t(const Problem& p, const void* q, void* out, hipStrea
       if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL(kern, dim3(unsigned(grid)), dim3(kThreads), C::LDS_BYTES, s,
-                       static_cast<const uint16_t*>(q), p.xf, p.xb, static_cast<uint16_t*>(out),
+                       static_cast<const uint16_t*>(q), reinterpret_cast<const uint16_t*>(p.xf),
+                       reinterpret_cast<const uint16_t*>(p.xb), static_cast<uint16_t*>(out),
                        p.n, total, tpf, per);
   } else {
     // one workgroup per frame, split only when there are too few frames to fill the chip

@@ -196,7 +196,7 @@ scan_bf16_kernel(const uint16_t* __restrict__ ainv_planes, const float* __restri
 
   const uint16_t* ainv_h = ainv_planes + bh * F1 * int64_t(2 * D * D);
   const float* bm_h = bm + bh * F1 * int64_t(D) * DV;
-  float* xo_h = (backward ? xb : xf) + bh * F * int64_t(D) * DV;
+  uint16_t* xo_h = reinterpret_cast<uint16_t*>(backward ? xb : xf) + bh * F * int64_t(D) * DV;
 
   // frame index (0 = text) of chain step s; steps past the end re-read the last frame
   auto frame_at = [&](int64_t s) -> int64_t {
@@ -273,11 +273,15 @@ scan_bf16_kernel(const uint16_t* __restrict__ ainv_planes, const float* __restri
       x[cw] = hh + (hl + lh);
     }
     if (s >= 1) {
-      // the states are read back only by the readout, so keep them out of the caches
-      float* dst = xo_h + (frame_at(s) - 1) * int64_t(D) * DV;
+      // The states leave the chain only for the readout, which rounds their mean to bf16
+      // for its MFMA: they are stored as bf16 in the readout's operand order (state_index),
+      // a lane's 4 rows as 8 bytes, and kept out of the caches.
+      uint16_t* dst = xo_h + (frame_at(s) - 1) * int64_t(D) * DV;
 #pragma unroll
       for (int cw = 0; cw < C::CW; ++cw)
-        __builtin_nontemporal_store(x[cw], reinterpret_cast<f32x4*>(dst + blk_index(row0, c0 + 16 * cw + n, D)));
+        __builtin_nontemporal_store(
+            u32x2{pack_bf16x2(x[cw][0], x[cw][1]), pack_bf16x2(x[cw][2], x[cw][3])},
+            reinterpret_cast<u32x2*>(dst + state_index(row0, c0 + 16 * cw + n, D)));
     }
     if (s < F) {
 #pragma unroll

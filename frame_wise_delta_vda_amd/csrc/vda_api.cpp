@@ -118,7 +118,8 @@ vda_status vda_plan_create(int64_t B, int64_t H, int64_t F, int64_t n, int64_t d
 
   const size_t ainv_n = size_t(ws_frames) * d * d;
   const size_t bm_n = size_t(ws_frames) * d * dv;
-  const size_t x_n = size_t(frames) * d * dv;
+  // states: float32 for float32 plans; bfloat16 (half the bytes) for bfloat16 plans
+  const size_t x_n = size_t(frames) * d * dv / (p.bf16 ? 2 : 1);
   const size_t total = (ainv_n + bm_n + 2 * x_n) * sizeof(float);
   if (total > 0) {
     void* ws = nullptr;

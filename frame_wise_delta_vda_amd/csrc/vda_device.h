@@ -106,6 +106,19 @@ __host__ __device__ constexpr int blk_index(int row, int col, int d) {
          (row & 3);
 }
 
+// Mean of two vectors of 8 bfloat16, (a + b) / 2 in fp32, rounded once to bfloat16.
+__device__ __forceinline__ uint4 mean_bf16x8(uint4 a, uint4 b) {
+  const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {b.x, b.y, b.z, b.w};
+  uint32_t r[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float lo = 0.5f * (__uint_as_float(aw[i] << 16) + __uint_as_float(bw[i] << 16));
+    const float hi = 0.5f * (__uint_as_float(aw[i] & 0xffff0000u) + __uint_as_float(bw[i] & 0xffff0000u));
+    r[i] = pack_bf16x2(lo, hi);
+  }
+  return make_uint4(r[0], r[1], r[2], r[3]);
+}
+
 // Fragment-ordered layout of a d x d bfloat16 plane (the hi and lo planes of Ainv for
 // the scan): the 16-row x 32-column operand block (row block r/16, column block c/32)
 // of a 16x16x32 MFMA is 1 KB contiguous, in lane order, lane 16*((c%32)/8) + r%16
@@ -116,11 +129,20 @@ __host__ __device__ constexpr int frag_index(int row, int col, int d) {
          (col & 7);
 }
 
+// Layout of a d x dv bfloat16 state for the readout: the transpose in fragment order,
+// so the operand block of W^T (16 value columns x 32 key rows) that a 16x16x32 MFMA of
+// the readout takes is 1 KB contiguous, lane 16*((r%32)/8) + c%16 holding rows
+// r..r+7 of column c.  Four consecutive rows (r%4 == 0) are 8 contiguous bytes.
+__host__ __device__ constexpr int state_index(int row, int col, int d) {
+  return frag_index(col, row, d);
+}
+
 // Raw buffer access: the descriptor (base, byte size) lives in SGPRs and must be
 // wave-uniform; the hardware range-checks every access against the size, so
 // out-of-range loads return zero and out-of-range stores are dropped, with no
 // branches around the memory instructions.
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kBufferFlags = 0x00020000;  // raw buffer, 32-bit data format
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {

@@ -20,8 +20,8 @@ struct Problem {
   // workspace (float32), frame index 0 = text, 1..F = frames
   float* ainv;      // [BH][F+1][d][d]
   float* bm;        // [BH][F+1][d][dv]
-  float* xf;        // [BH][F][d][dv]
-  float* xb;        // [BH][F][d][dv]
+  float* xf;        // [BH][F][d][dv]; bf16 plans: bf16 elements in state_index order
+  float* xb;        // [BH][F][d][dv]; likewise
 };
 
 // Each launcher enqueues one stage on `stream` and returns the launch status.

@@ -135,7 +135,7 @@ def vda_plan_workspace_bytes(plan) -> int:
 
 
 def vda_debug_workspace(plan):
-    """Device addresses (ainv, bm, x_fwd, x_bwd) of the plan's float32 workspace."""
+    """Device addresses (ainv, bm, x_fwd, x_bwd) in the plan's workspace (layouts: include/vda.h)."""
     ptrs = [ctypes.c_void_p() for _ in range(4)]
     _check(load_library().vda_debug_workspace(plan, *[ctypes.byref(p) for p in ptrs]),
            "vda_debug_workspace")

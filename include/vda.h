@@ -78,7 +78,7 @@ typedef enum {
  *   d, dv in {32, 64, 128}: key/query width and value width.
  *   lambda: the regulariser, finite and > 0, shared by the text and every frame.
  *   dtype: element type of all tensors.
- * The plan allocates its float32 workspace (hipMalloc) on the current device and
+ * The plan allocates its workspace (hipMalloc, one block) on the current device and
  * keeps it until vda_plan_destroy.  On error *plan_out is set to NULL.
  * Errors: INVALID_VALUE, NOT_SUPPORTED, OUT_OF_MEMORY, DEVICE. */
 vda_status vda_plan_create(int64_t B, int64_t H, int64_t F, int64_t n, int64_t d, int64_t dv,
@@ -140,10 +140,15 @@ const char* vda_status_string(vda_status s);
  *                           fragment-ordered: element (r, c) at
  *                           (((r/16 * d/32 + c/32) * 4 + (c%32)/8) * 16 + r%16) * 8 + c%8
  *   bm    [BH][F+1][d*dv]   K^T V, float32, blocked (below)
- *   x_fwd [BH][F][d*dv]     forward state after frame f (f = 1..F at index f-1), blocked
- *   x_bwd [BH][F][d*dv]     backward state after frame f, blocked
+ *   x_fwd [BH][F][d*dv]     forward state after frame f (f = 1..F at index f-1)
+ *   x_bwd [BH][F][d*dv]     backward state after frame f
  * Blocked layout of a d x dv matrix M: element (r, c) is at
  *   (((c/16 * d/16 + r/16) * 4 + (r%16)/4) * 16 + c%16) * 4 + r%4.
+ * The states are float32 and blocked for float32 plans.  For bfloat16 plans they are
+ * bfloat16 (the pointers then address d*dv bfloat16 per frame, not floats), rounded
+ * once from the float32 chain, with element (r, c) at
+ *   (((c/16 * d/32 + r/32) * 4 + (r%32)/8) * 16 + c%16) * 8 + r%8
+ * (the operand order of the readout's MFMA); the chain itself runs in float32.
  * The memory stays owned by the plan.  Any output pointer may be NULL. */
 vda_status vda_debug_workspace(vda_plan_t plan, const float** ainv, const float** bm,
                                const float** x_fwd, const float** x_bwd);

@@ -70,7 +70,8 @@ def test_workspace_size():
     w = _small()
     plan = binding.Plan(w.B, w.H, w.F, w.n, w.d, w.dv, w.T, w.lam, w.dtype)
     BH = w.B * w.H
-    expect = 4 * (BH * (w.F + 1) * (w.d * w.d + w.d * w.dv) + 2 * BH * w.F * w.d * w.dv)
+    state_bytes = 4 if w.dtype == "f32" else 2  # bf16 plans keep the states in bf16
+    expect = 4 * BH * (w.F + 1) * (w.d * w.d + w.d * w.dv) + state_bytes * 2 * BH * w.F * w.d * w.dv
     assert plan.workspace_bytes == expect
     plan.close()
 
