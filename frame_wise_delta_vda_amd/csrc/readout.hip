@@ -14,11 +14,13 @@
 namespace vda {
 namespace {
 
-// bfloat16 path.  Persistent workgroups, each owning a contiguous range of 64-token
-// tiles (a tile never straddles two frames).  Wave w of a workgroup takes tokens
-// 16w..16w+15 of every tile and works alone -- there is no workgroup barrier at all:
-//  - at a frame change each wave forms all of its W^T operand fragments in registers
-//    from the two bf16 states, which the scan stores in exactly that operand order
+// bfloat16 path.  One workgroup per frame (or per equal part of a frame when there
+// are too few frames to fill the chip), so W is formed once per frame and the
+// workgroups that run together stream neighbouring frames.  Wave w of a workgroup
+// takes tokens 16w..16w+15 of every 64-token tile and works alone -- there is no
+// workgroup barrier at all:
+//  - at the start each wave forms all of its W^T operand fragments in registers from
+//    the two bf16 states, which the scan stores in exactly that operand order
 //    (state_index): one 16-byte load per state and fragment, mean in fp32, one rounding;
 //  - the wave's Q rows are loaded straight into MFMA operands (lane: token l%16, eight
 //    consecutive features), two tiles ahead;
@@ -40,21 +42,21 @@ struct ReadBf16 {
   static_assert(OST >= 1, "value width too large for one wave store pass");
 };
 
-constexpr int kReadoutWgPerCu = 2;
-
 template <int D, int DV>
 __global__ void __launch_bounds__(kThreads, 2)
 readout_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ xf,
                     const uint16_t* __restrict__ xb, uint16_t* __restrict__ out, int64_t n,
-                    int64_t total_tiles, int64_t tiles_per_frame, int64_t per_wg) {
+                    int64_t tiles_per_frame, int64_t splits, int64_t tiles_per_split) {
   using C = ReadBf16<D, DV>;
   extern __shared__ __align__(16) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   uint16_t* ow = reinterpret_cast<uint16_t*>(smem + wave * C::OW_BYTES);
   const int c16 = lane & 15, g4 = lane >> 4;
-  const int64_t t_first = blockIdx.x * per_wg;
-  const int64_t t_last = (t_first + per_wg < total_tiles) ? t_first + per_wg : total_tiles;
+  const int64_t frame = blockIdx.x / splits;
+  const int64_t t_first = (blockIdx.x % splits) * tiles_per_split;
+  const int64_t t_last = (t_first + tiles_per_split < tiles_per_frame) ? t_first + tiles_per_split
+                                                                       : tiles_per_frame;
   if (t_first >= t_last) return;
 
   // rows of this wave's 16 tokens that lie inside the frame (0 past its end)
@@ -63,46 +65,44 @@ readout_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     return uint32_t(r < 0 ? 0 : (r < 16 ? r : 16));
   };
   auto load_q = [&](int64_t tile, uint4 (&dst)[C::KS]) {
-    const int64_t frame = tile / tiles_per_frame;
-    const int64_t tok0 = (tile % tiles_per_frame) * C::TT + 16 * wave;
+    const int64_t tok0 = tile * C::TT + 16 * wave;
     const auto rs = make_rsrc(q + (frame * n + tok0) * D, wave_rows(tok0) * D * 2);
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks)
       dst[ks] = buffer_load16<kCacheNt>(rs, uint32_t(c16 * D * 2 + (32 * ks + 8 * g4) * 2));
   };
 
-  int64_t cur_frame = -1;
-  uint4 wfr[C::NBF][C::KS];  // W^T fragments: rows = output features, k = input features
   uint4 pfa[C::KS], pfb[C::KS];
+  load_q(t_first, pfa);
+  load_q(t_first + 1 < t_last ? t_first + 1 : t_first, pfb);
+
+  // W = (X_fwd + X_bwd) / 2 of the frame, rounded once to bf16; fragment (nb, ks) of
+  // both states is the 1 KB at ((nb * KS + ks) * 64 + lane) * 8.  Two output blocks at a
+  // time, so the loads in flight stay within the registers.
+  uint4 wfr[C::NBF][C::KS];  // W^T fragments: rows = output features, k = input features
+  {
+    const uint4* sf = reinterpret_cast<const uint4*>(xf + frame * int64_t(D) * DV) + lane;
+    const uint4* sb = reinterpret_cast<const uint4*>(xb + frame * int64_t(D) * DV) + lane;
+    constexpr int NG = C::NBF >= 2 ? 2 : 1;
+#pragma unroll
+    for (int nb0 = 0; nb0 < C::NBF; nb0 += NG) {
+      uint4 a[NG][C::KS], b[NG][C::KS];
+#pragma unroll
+      for (int i = 0; i < NG; ++i)
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) {
+          a[i][ks] = sf[((nb0 + i) * C::KS + ks) * 64];
+          b[i][ks] = sb[((nb0 + i) * C::KS + ks) * 64];
+        }
+#pragma unroll
+      for (int i = 0; i < NG; ++i)
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) wfr[nb0 + i][ks] = mean_bf16x8(a[i][ks], b[i][ks]);
+    }
+  }
 
   auto step = [&](int64_t tile, uint4 (&pf)[C::KS]) {
-    const int64_t frame = tile / tiles_per_frame;
-    if (frame != cur_frame) {
-      // W = (X_fwd + X_bwd) / 2 of the new frame, rounded once to bf16; fragment (nb, ks)
-      // of both states is the 1 KB at ((nb * KS + ks) * 64 + lane) * 8
-      const uint4* sf = reinterpret_cast<const uint4*>(xf + frame * int64_t(D) * DV) + lane;
-      const uint4* sb = reinterpret_cast<const uint4*>(xb + frame * int64_t(D) * DV) + lane;
-      // two output blocks at a time, so the loads in flight stay within the registers
-      constexpr int NG = C::NBF >= 2 ? 2 : 1;
-#pragma unroll
-      for (int nb0 = 0; nb0 < C::NBF; nb0 += NG) {
-        uint4 a[NG][C::KS], b[NG][C::KS];
-#pragma unroll
-        for (int i = 0; i < NG; ++i)
-#pragma unroll
-          for (int ks = 0; ks < C::KS; ++ks) {
-            a[i][ks] = sf[((nb0 + i) * C::KS + ks) * 64];
-            b[i][ks] = sb[((nb0 + i) * C::KS + ks) * 64];
-          }
-#pragma unroll
-        for (int i = 0; i < NG; ++i)
-#pragma unroll
-          for (int ks = 0; ks < C::KS; ++ks) wfr[nb0 + i][ks] = mean_bf16x8(a[i][ks], b[i][ks]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      cur_frame = frame;
-    }
-    const int64_t tok0 = (tile % tiles_per_frame) * C::TT + 16 * wave;
+    const int64_t tok0 = tile * C::TT + 16 * wave;
     uint4 qf[C::KS];
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) qf[ks] = pf[ks];
@@ -127,8 +127,6 @@ readout_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     }
   };
 
-  load_q(t_first, pfa);
-  load_q(t_first + 1 < t_last ? t_first + 1 : t_first, pfb);
   for (int64_t tile = t_first; tile < t_last; tile += 2) {
     step(tile, pfa);
     if (tile + 1 < t_last) step(tile + 1, pfb);
@@ -200,21 +198,18 @@ hipError_t launch_readout_t(const Problem& p, const void* q, void* out, hipStrea
   if (p.bf16) {
     using C = ReadBf16<D, DV>;
     const int64_t tpf = (p.n + C::TT - 1) / C::TT;
-    const int64_t total = frames * tpf;
-    int64_t grid = kReadoutWgPerCu * int64_t(p.num_cus);  // persistent workgroups
-    if (grid > total) grid = total;
-    const int64_t per = (total + grid - 1) / grid;
-    grid = (total + per - 1) / per;
+    // one workgroup per frame; frames are split in equal parts only while there are
+    // fewer than four workgroups per compute unit and each part keeps 8+ tiles
+    int64_t splits = 1;
+    while (frames * splits < 4 * int64_t(p.num_cus) && tpf >= 16 * splits) splits *= 2;
+    const int64_t tps = (tpf + splits - 1) / splits;
+    splits = (tpf + tps - 1) / tps;
+    const int64_t grid = frames * splits;
     auto kern = readout_bf16_kernel<D, DV>;
-    if (C::LDS_BYTES > 65536) {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
-      if (e != hipSuccess) return e;
-    }
     hipLaunchKernelGGL(kern, dim3(unsigned(grid)), dim3(kThreads), C::LDS_BYTES, s,
                        static_cast<const uint16_t*>(q), reinterpret_cast<const uint16_t*>(p.xf),
                        reinterpret_cast<const uint16_t*>(p.xb), static_cast<uint16_t*>(out),
-                       p.n, total, tpf, per);
+                       p.n, tpf, splits, tps);
   } else {
     // one workgroup per frame, split only when there are too few frames to fill the chip
     int64_t splits = 1;

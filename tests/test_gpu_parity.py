@@ -70,6 +70,8 @@ SMALL = [
     ("bf16_32x128", dict(dtype="bf16", d=32, dv=128, n=65, T=0, F=2, B=1, H=1)),
     ("bf16_128x32", dict(dtype="bf16", d=128, dv=32, n=64, T=3, F=2, B=1, H=1)),
     ("bf16_128x128_no_text", dict(dtype="bf16", d=128, dv=128, n=64, T=0, F=3, B=1, H=1)),
+    # few frames: the readout splits each frame into 4 parts of 16, 16, 16 and 15 tiles
+    ("bf16_split_frames", dict(dtype="bf16", d=128, dv=128, n=4000, T=10, F=2, B=1, H=1)),
     ("bf16_n1", dict(dtype="bf16", d=64, dv=64, n=1, T=1, F=7, B=1, H=2)),
     ("bf16_F1", dict(dtype="bf16", d=128, dv=128, n=333, T=20, F=1, B=1, H=1)),
     ("f32_128x128", dict(dtype="f32", d=128, dv=128, n=150, T=9, F=3, B=1, H=2)),
