@@ -158,7 +158,10 @@ struct StatsBf16 {
   static constexpr bool DEEP = D == 128 && DV == 128;
   static constexpr int ACC = COLW ? 8 : CPW;
   static constexpr int NSEG = (D + DV) / 8;      // 8-feature segments per token (K then V)
-  static constexpr int BUF = (D + DV) * ROW;     // bf16 elements per staging buffer
+  // d = dv = 128 stage token-major instead: a row per token (K then V, padded to 576 B so
+  // the transposing LDS reads of four consecutive rows hit distinct banks)
+  static constexpr int TROW = D + DV + 32;
+  static constexpr int BUF = DEEP ? TC * TROW : (D + DV) * ROW;  // bf16 per staging buffer
   static constexpr int STAGE_BYTES = 2 * BUF * 2;
   static constexpr int GS = D + 4;               // floats per LDS row of G
   static constexpr int G_BYTES = D * GS * 4;
@@ -230,72 +233,116 @@ stats_bf16_kernel(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v
     for (int j = 0; j < 8; ++j) *reinterpret_cast<uint4*>(dst + j * C::ROW) = c[j];
   };
 
-  auto mult_chunk = [&](int buf) {
+  // one 16-token k-step of the chunk in LDS buffer buf
+  auto mult_kstep = [&](int buf, int ks) {
     const uint16_t* kt = stage + buf * C::BUF;
     const uint16_t* vt = kt + D * C::ROW;
+    const int col = ks * 16 + (lane >> 5) * 8;
+    if constexpr (C::COLW) {
+      // acc[rb] = G(rb, wave), acc[4 + rb] = Bm(rb, wave)
+      const uint4 bk = *reinterpret_cast<const uint4*>(kt + (wave * 32 + (lane & 31)) * C::ROW + col);
+      uint4 bv = make_uint4(0, 0, 0, 0);
+      if (C::NV >= 4 || wave < C::NV) bv = *reinterpret_cast<const uint4*>(vt + (wave * 32 + (lane & 31)) * C::ROW + col);
 #pragma unroll
-    for (int ks = 0; ks < C::TC / 16; ++ks) {
-      const int col = ks * 16 + (lane >> 5) * 8;
-      if constexpr (C::COLW) {
-        // acc[rb] = G(rb, wave), acc[4 + rb] = Bm(rb, wave)
-        const uint4 bk = *reinterpret_cast<const uint4*>(kt + (wave * 32 + (lane & 31)) * C::ROW + col);
-        uint4 bv = make_uint4(0, 0, 0, 0);
-        if (C::NV >= 4 || wave < C::NV) bv = *reinterpret_cast<const uint4*>(vt + (wave * 32 + (lane & 31)) * C::ROW + col);
+      for (int rbi = 0; rbi < 4; ++rbi) {
+        const uint4 a = *reinterpret_cast<const uint4*>(kt + (rbi * 32 + (lane & 31)) * C::ROW + col);
+        acc[rbi] = mfma32_bf16(a, bk, acc[rbi]);
+        if (C::NV >= 4 || wave < C::NV) acc[4 + rbi] = mfma32_bf16(a, bv, acc[4 + rbi]);
+      }
+    } else {
+      const uint4 a = *reinterpret_cast<const uint4*>(kt + (rb * 32 + (lane & 31)) * C::ROW + col);
 #pragma unroll
-        for (int rbi = 0; rbi < 4; ++rbi) {
-          const uint4 a = *reinterpret_cast<const uint4*>(kt + (rbi * 32 + (lane & 31)) * C::ROW + col);
-          acc[rbi] = mfma32_bf16(a, bk, acc[rbi]);
-          if (C::NV >= 4 || wave < C::NV) acc[4 + rbi] = mfma32_bf16(a, bv, acc[4 + rbi]);
-        }
-      } else {
-        const uint4 a = *reinterpret_cast<const uint4*>(kt + (rb * 32 + (lane & 31)) * C::ROW + col);
-#pragma unroll
-        for (int jj = 0; jj < C::CPW; ++jj) {
-          const int c = jj * C::RPW + cofs;
-          if (c < C::NC) {
-            const uint16_t* bs = c < C::NK ? kt + (c * 32 + (lane & 31)) * C::ROW
-                                           : vt + ((c - C::NK) * 32 + (lane & 31)) * C::ROW;
-            const uint4 b = *reinterpret_cast<const uint4*>(bs + col);
-            acc[jj] = mfma32_bf16(a, b, acc[jj]);
-          }
+      for (int jj = 0; jj < C::CPW; ++jj) {
+        const int c = jj * C::RPW + cofs;
+        if (c < C::NC) {
+          const uint16_t* bs = c < C::NK ? kt + (c * 32 + (lane & 31)) * C::ROW
+                                         : vt + ((c - C::NK) * 32 + (lane & 31)) * C::ROW;
+          const uint4 b = *reinterpret_cast<const uint4*>(bs + col);
+          acc[jj] = mfma32_bf16(a, b, acc[jj]);
         }
       }
     }
   };
+  auto mult_chunk = [&](int buf) {
+#pragma unroll
+    for (int ks = 0; ks < C::TC / 16; ++ks) mult_kstep(buf, ks);
+  };
 
   if constexpr (C::DEEP) {
-    // Two chunks in flight per thread.  Waves 0-1 load K, waves 2-3 V (one 8-feature
-    // segment and 8 tokens per lane); the buffer descriptor spans the frame, so loads
-    // past its last token return zeros and a ragged or missing chunk multiplies in
-    // nothing.
-    const auto rs = make_rsrc(wave < 2 ? kp : vp, uint32_t(ntok * 128 * 2));
-    const uint32_t voff = uint32_t((tg * 8 * 128 + (seg & 15) * 8) * 2);
+    // Two chunks in flight per thread, staged in LDS token-major, exactly as loaded.
+    // Waves 0-1 load K, waves 2-3 V; instruction i of a wave covers 4 whole token rows
+    // (lane: token 32 (wave % 2) + 4 i + lane / 16, 8 features from 8 (lane % 16)).  The
+    // buffer descriptor spans the frame, so loads past its last token return zeros and a
+    // ragged or missing chunk multiplies in nothing.
+    const int tok_l = 32 * (wave & 1) + (lane >> 4);
+    const auto rs = make_rsrc(wave < 2 ? kp : vp, uint32_t(ntok * 256));
+    const uint32_t voff = uint32_t(tok_l * 256 + (lane & 15) * 16);
+    uint16_t* const st_lane = stage + tok_l * C::TROW + (wave >> 1) * D + (lane & 15) * 8;
     uint4 ra[8], rn[8];
-    auto load_deep = [&](int64_t ch, uint4 (&r)[8]) {
+    auto chunk_base = [&](int64_t ch) -> uint32_t {
       // chunk indices past the end stay at nchunks: their bytes are past the frame
-      const uint32_t base = voff + uint32_t((ch < nchunks ? ch : nchunks) * C::TC * 256);
+      return voff + uint32_t((ch < nchunks ? ch : nchunks) * C::TC * 256);
+    };
+    auto load_deep = [&](int64_t ch, uint4 (&r)[8]) {
+      const uint32_t base = chunk_base(ch);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) r[i] = buffer_load16<kCacheNt>(rs, base + uint32_t(i * 256));
+      for (int i = 0; i < 8; ++i) r[i] = buffer_load16<kCacheNt>(rs, base + uint32_t(i * 1024));
+    };
+    auto store_rows = [&](int buf, const uint4 (&r)[8]) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4*>(st_lane + buf * C::BUF + 4 * i * C::TROW) = r[i];
+    };
+    // MFMA operand of 8 consecutive tokens of one feature from the token-major rows, by two
+    // transposing LDS reads (ds_read_b64_tr_b16).  In each 16-lane group the read hands
+    // lane 4a + b element b of the 4-element reads of lanes a, a+4, a+8, a+12; so lane l
+    // points at token 8 (l / 32) + (l % 16) / 4 (+4 for the second read) and features
+    // 16 ((l / 16) % 2) + 4 (l % 4), and receives feature l % 32 of 4 consecutive tokens.
+    const int fr_off = (8 * (lane >> 5) + ((lane & 15) >> 2)) * C::TROW + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    auto frag = [&](const uint16_t* rows, int f0) -> uint4 {
+      typedef short v4s __attribute__((ext_vector_type(4)));
+      typedef __attribute__((address_space(3))) v4s* lds_v4s;
+      const uint16_t* p = rows + fr_off + f0;
+      const v4s x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(p));
+      const v4s y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(p + 4 * C::TROW));
+      const uint2 xl = __builtin_bit_cast(uint2, x), yl = __builtin_bit_cast(uint2, y);
+      return make_uint4(xl.x, xl.y, yl.x, yl.y);
+    };
+    // acc[rb] = G(rb, wave), acc[4 + rb] = Bm(rb, wave) over one 16-token k-step
+    auto kstep_tm = [&](int buf, int ks) {
+      const uint16_t* rows = stage + buf * C::BUF + ks * 16 * C::TROW;
+      const uint4 bk = frag(rows, wave * 32);
+      const uint4 bv = frag(rows, D + wave * 32);
+#pragma unroll
+      for (int rbi = 0; rbi < 4; ++rbi) {
+        const uint4 a = frag(rows, rbi * 32);
+        acc[rbi] = mfma32_bf16(a, bk, acc[rbi]);
+        acc[4 + rbi] = mfma32_bf16(a, bv, acc[4 + rbi]);
+      }
+    };
+    // Multiply the chunk in LDS buffer buf while loading chunk ch into r.  The memory
+    // queue is usually full, so a load can stall its wave at issue; two loads go out
+    // before each k-step, and a stalled issue waits beside the previous k-step's MFMAs
+    // rather than ahead of all of them.
+    auto mult_load = [&](int buf, int64_t ch, uint4 (&r)[8]) {
+      const uint32_t base = chunk_base(ch);
+#pragma unroll
+      for (int ks = 0; ks < C::TC / 16; ++ks) {
+        r[2 * ks] = buffer_load16<kCacheNt>(rs, base + uint32_t(2 * ks * 1024));
+        r[2 * ks + 1] = buffer_load16<kCacheNt>(rs, base + uint32_t((2 * ks + 1) * 1024));
+        kstep_tm(buf, ks);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     };
     load_deep(0, ra);
     load_deep(1, rn);
-    store_chunk(0, ra);
+    store_rows(0, ra);
     __syncthreads();
-    // The scheduling barriers keep each phase in order -- loads issued first, the
-    // transposes (which wait for the chunk loaded a phase earlier) last -- so that a
-    // chunk's loads have a whole phase of multiplies to land.
     for (int64_t ch = 0; ch < nchunks; ch += 2) {
-      load_deep(ch + 2, ra);
-      __builtin_amdgcn_sched_barrier(0);
-      mult_chunk(0);
-      __builtin_amdgcn_sched_barrier(0);
-      store_chunk(1, rn);
+      mult_load(0, ch + 2, ra);
+      store_rows(1, rn);
       __syncthreads();
-      load_deep(ch + 3, rn);
-      __builtin_amdgcn_sched_barrier(0);
-      mult_chunk(1);
-      __builtin_amdgcn_sched_barrier(0);
-      store_chunk(0, ra);
+      mult_load(1, ch + 3, rn);
+      store_rows(0, ra);
       __syncthreads();
     }
   } else {
