@@ -26,7 +26,7 @@ namespace {
 //    consecutive features), two tiles ahead;
 //  - O^T = W^T Q^T goes through a wave-private LDS patch so the stores are whole rows
 //    (1 KB contiguous per wave instruction).
-// Q and O are streamed with the non-temporal cache policy, through buffer descriptors
+// Q is loaded and O stored with streaming cache policies, through buffer descriptors
 // bounded by the frame's last row, so ragged frame ends need no branch.
 template <int D, int DV>
 struct ReadBf16 {
@@ -122,7 +122,7 @@ readout_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
 #pragma unroll
     for (int j = 0; j < C::OST; ++j) {
       const int r = orow + j * C::ORPI;
-      buffer_store16<kCacheNt>(rs, uint32_t(r * DV * 2 + och * 16),
+      buffer_store16<kCacheStreamOut>(rs, uint32_t(r * DV * 2 + och * 16),
                                *reinterpret_cast<const uint4*>(ow + r * C::OWROW + och * 8));
     }
   };

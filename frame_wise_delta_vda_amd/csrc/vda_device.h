@@ -149,7 +149,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferFlags);
 }
 // Cache policy of a buffer access: kCacheNt marks data that is touched once (streamed).
-constexpr int kCacheDefault = 0, kCacheNt = 2;
+// kCacheStreamOut (SC1 | NT) is for streamed output: in the readout it stores ~1% faster
+// than NT alone and ~7% faster than the default policy.
+constexpr int kCacheDefault = 0, kCacheNt = 2, kCacheStreamOut = 16 | 2;
 template <int CPOL = kCacheDefault>
 __device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, CPOL));
