@@ -46,17 +46,28 @@ template <int D, int DV>
 __global__ void __launch_bounds__(kThreads, 2)
 readout_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ xf,
                     const uint16_t* __restrict__ xb, uint16_t* __restrict__ out, int64_t n,
-                    int64_t tiles_per_frame, int64_t splits, int64_t tiles_per_split) {
+                    int64_t tiles_per_frame, int64_t splits, int64_t tiles_per_split,
+                    int64_t head_blocks, int64_t tail_splits, int64_t tail_tiles_per_split) {
   using C = ReadBf16<D, DV>;
   extern __shared__ __align__(16) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   uint16_t* ow = reinterpret_cast<uint16_t*>(smem + wave * C::OW_BYTES);
   const int c16 = lane & 15, g4 = lane >> 4;
-  const int64_t frame = blockIdx.x / splits;
-  const int64_t t_first = (blockIdx.x % splits) * tiles_per_split;
-  const int64_t t_last = (t_first + tiles_per_split < tiles_per_frame) ? t_first + tiles_per_split
-                                                                       : tiles_per_frame;
+  // blocks past head_blocks take the frames of the last, partial round of resident
+  // workgroups in smaller parts, so the launch does not end on a few long workgroups
+  int64_t frame, t_first, tps;
+  if (blockIdx.x < head_blocks) {
+    frame = blockIdx.x / splits;
+    t_first = (blockIdx.x % splits) * tiles_per_split;
+    tps = tiles_per_split;
+  } else {
+    const int64_t i = blockIdx.x - head_blocks;
+    frame = head_blocks / splits + i / tail_splits;
+    t_first = (i % tail_splits) * tail_tiles_per_split;
+    tps = tail_tiles_per_split;
+  }
+  const int64_t t_last = (t_first + tps < tiles_per_frame) ? t_first + tps : tiles_per_frame;
   if (t_first >= t_last) return;
 
   // rows of this wave's 16 tokens that lie inside the frame (0 past its end)
@@ -204,12 +215,29 @@ hipError_t launch_readout_t(const Problem& p, const void* q, void* out, hipStrea
     while (frames * splits < 4 * int64_t(p.num_cus) && tpf >= 16 * splits) splits *= 2;
     const int64_t tps = (tpf + splits - 1) / splits;
     splits = (tpf + tps - 1) / tps;
-    const int64_t grid = frames * splits;
+    // Whole frames leave a last, partial round of R frames on S resident workgroups (two
+    // per CU); those R frames go in k equal parts so that round is about as wide as the
+    // others.
+    int64_t head_frames = frames, tail_splits = 1, tail_tps = tpf;
+    const int64_t slots = 2 * int64_t(p.num_cus);
+    const int64_t rem = frames % slots;
+    if (splits == 1 && frames > slots && rem > 0) {
+      int64_t k = slots / rem;
+      if (k > 4) k = 4;
+      if (tpf < 4 * k) k = tpf / 4;
+      if (k >= 2) {
+        tail_tps = (tpf + k - 1) / k;
+        tail_splits = (tpf + tail_tps - 1) / tail_tps;
+        head_frames = frames - rem;
+      }
+    }
+    const int64_t head_blocks = head_frames * splits;
+    const int64_t grid = head_blocks + (frames - head_frames) * tail_splits;
     auto kern = readout_bf16_kernel<D, DV>;
     hipLaunchKernelGGL(kern, dim3(unsigned(grid)), dim3(kThreads), C::LDS_BYTES, s,
                        static_cast<const uint16_t*>(q), reinterpret_cast<const uint16_t*>(p.xf),
                        reinterpret_cast<const uint16_t*>(p.xb), static_cast<uint16_t*>(out),
-                       p.n, tpf, splits, tps);
+                       p.n, tpf, splits, tps, head_blocks, tail_splits, tail_tps);
   } else {
     // one workgroup per frame, split only when there are too few frames to fill the chip
     int64_t splits = 1;

@@ -94,6 +94,17 @@ def test_small_shapes_parity(name, over):
     plan.close()
 
 
+def test_readout_last_round_in_parts():
+    """600 frames of 16 tiles on 512 resident readout workgroups (two per CU on 256 CUs):
+    frames 512..599 are read out in quarter frames.  Head 5 holds frames 500..599."""
+    w = W.WORKLOADS[3].replace(name="readout_tail_parts", H=6, F=100, n=1000, T=10, seed=77)
+    say("[gpu] readout tail parts")
+    dev = to_device(w, W.full_storage(w))
+    out, plan = run_gpu(w, dev)
+    _check_heads(w, out, [(0, 5), (0, 2)])
+    plan.close()
+
+
 def test_intermediates_match_oracle():
     """Workspace after a forward pass: Ainv_f (lam I + K_f^T K_f) = I, Bm_f = K_f^T V_f, and
     the forward/backward states against the oracle's."""
