@@ -204,9 +204,10 @@ readout_f32_kernel(const float* __restrict__ q, const float* __restrict__ xf,
 }
 
 template <int D, int DV>
-hipError_t launch_readout_t(const Problem& p, const void* q, void* out, hipStream_t s) {
+hipError_t launch_readout_t(const Problem& p, const void* q, void* out, hipStream_t s, bool prepare) {
   const int64_t frames = p.B * p.H * p.F;
   if (p.bf16) {
+    if (prepare) return hipSuccess;  // 17 KB of LDS: no attribute to set
     using C = ReadBf16<D, DV>;
     const int64_t tpf = (p.n + C::TT - 1) / C::TT;
     // one workgroup per frame; frames are split in equal parts only while there are
@@ -247,11 +248,10 @@ hipError_t launch_readout_t(const Problem& p, const void* q, void* out, hipStrea
     const int64_t grid = frames * splits;
     constexpr int lds = ReadF32<D, DV>::LDS_BYTES;
     auto kern = readout_f32_kernel<D, DV>;
-    if (lds > 65536) {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-      if (e != hipSuccess) return e;
-    }
+    if (prepare)
+      return lds > 65536 ? hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, lds)
+                         : hipSuccess;
     hipLaunchKernelGGL(kern, dim3(unsigned(grid)), dim3(kThreads), lds, s,
                        static_cast<const float*>(q), p.xf, p.xb, static_cast<float*>(out), p.F,
                        p.n, splits, tps);
@@ -263,7 +263,17 @@ hipError_t launch_readout_t(const Problem& p, const void* q, void* out, hipStrea
 
 hipError_t launch_readout(const Problem& p, const void* q, void* out, hipStream_t s) {
 #define VDA_CASE(DD, VV) \
-  if (p.d == DD && p.dv == VV) return launch_readout_t<DD, VV>(p, q, out, s);
+  if (p.d == DD && p.dv == VV) return launch_readout_t<DD, VV>(p, q, out, s, false);
+  VDA_CASE(32, 32) VDA_CASE(32, 64) VDA_CASE(32, 128)
+  VDA_CASE(64, 32) VDA_CASE(64, 64) VDA_CASE(64, 128)
+  VDA_CASE(128, 32) VDA_CASE(128, 64) VDA_CASE(128, 128)
+#undef VDA_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t prepare_readout(const Problem& p) {
+#define VDA_CASE(DD, VV) \
+  if (p.d == DD && p.dv == VV) return launch_readout_t<DD, VV>(p, nullptr, nullptr, nullptr, true);
   VDA_CASE(32, 32) VDA_CASE(32, 64) VDA_CASE(32, 128)
   VDA_CASE(64, 32) VDA_CASE(64, 64) VDA_CASE(64, 128)
   VDA_CASE(128, 32) VDA_CASE(128, 64) VDA_CASE(128, 128)

@@ -564,16 +564,15 @@ stats_f32_kernel(const float* __restrict__ k, const float* __restrict__ v,
 
 template <int D, int DV>
 hipError_t launch_stats_t(const Problem& p, const void* k, const void* v, const void* tk,
-                          const void* tv, hipStream_t s) {
+                          const void* tv, hipStream_t s, bool prepare) {
   const int64_t blocks = p.B * p.H * (p.F + 1);
   if (p.bf16) {
     constexpr int lds = StatsBf16<D, DV>::LDS_BYTES;
     auto kern = stats_bf16_kernel<D, DV>;
-    if (lds > 65536) {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-      if (e != hipSuccess) return e;
-    }
+    if (prepare)
+      return lds > 65536 ? hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, lds)
+                         : hipSuccess;
     hipLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(kThreads), lds, s,
                        static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
                        static_cast<const uint16_t*>(tk), static_cast<const uint16_t*>(tv), p.ainv,
@@ -581,11 +580,10 @@ hipError_t launch_stats_t(const Problem& p, const void* k, const void* v, const 
   } else {
     constexpr int lds = StatsF32<D, DV>::LDS_BYTES;
     auto kern = stats_f32_kernel<D, DV>;
-    if (lds > 65536) {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-      if (e != hipSuccess) return e;
-    }
+    if (prepare)
+      return lds > 65536 ? hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, lds)
+                         : hipSuccess;
     hipLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(kThreads), lds, s,
                        static_cast<const float*>(k), static_cast<const float*>(v),
                        static_cast<const float*>(tk), static_cast<const float*>(tv), p.ainv, p.bm,
@@ -599,7 +597,18 @@ hipError_t launch_stats_t(const Problem& p, const void* k, const void* v, const 
 hipError_t launch_stats(const Problem& p, const void* k, const void* v, const void* tk,
                         const void* tv, hipStream_t s) {
 #define VDA_CASE(DD, VV) \
-  if (p.d == DD && p.dv == VV) return launch_stats_t<DD, VV>(p, k, v, tk, tv, s);
+  if (p.d == DD && p.dv == VV) return launch_stats_t<DD, VV>(p, k, v, tk, tv, s, false);
+  VDA_CASE(32, 32) VDA_CASE(32, 64) VDA_CASE(32, 128)
+  VDA_CASE(64, 32) VDA_CASE(64, 64) VDA_CASE(64, 128)
+  VDA_CASE(128, 32) VDA_CASE(128, 64) VDA_CASE(128, 128)
+#undef VDA_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t prepare_stats(const Problem& p) {
+#define VDA_CASE(DD, VV) \
+  if (p.d == DD && p.dv == VV) \
+    return launch_stats_t<DD, VV>(p, nullptr, nullptr, nullptr, nullptr, nullptr, true);
   VDA_CASE(32, 32) VDA_CASE(32, 64) VDA_CASE(32, 128)
   VDA_CASE(64, 32) VDA_CASE(64, 64) VDA_CASE(64, 128)
   VDA_CASE(128, 32) VDA_CASE(128, 64) VDA_CASE(128, 128)

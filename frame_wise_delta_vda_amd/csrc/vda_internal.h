@@ -29,5 +29,10 @@ hipError_t launch_stats(const Problem& p, const void* k, const void* v, const vo
                         const void* tv, hipStream_t stream);
 hipError_t launch_scan(const Problem& p, hipStream_t stream);
 hipError_t launch_readout(const Problem& p, const void* q, void* out, hipStream_t stream);
+// Per-function attributes (dynamic LDS above 64 KB) of the kernels a plan launches, set
+// once at plan creation on the plan's device, so that launches make no other runtime
+// call (they can then be captured in a graph).
+hipError_t prepare_stats(const Problem& p);
+hipError_t prepare_readout(const Problem& p);
 
 }  // namespace vda

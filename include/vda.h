@@ -91,6 +91,9 @@ vda_status vda_plan_create(int64_t B, int64_t H, int64_t F, int64_t n, int64_t d
  * The plan's workspace is reused by every call, so at most one forward pass per
  * plan may be in flight; separate plans are independent.
  * Results are bitwise reproducible for the same inputs and plan.
+ * The call makes no runtime call on the stream but kernel launches (and timing events,
+ * when enabled), so it may be captured into a HIP graph; the plan's workspace stays at
+ * the same address for the plan's lifetime, and a replay reads the captured pointers.
  * Errors: INVALID_VALUE, MISALIGNED, DEVICE. */
 vda_status vda_forward(vda_plan_t plan, const void* q, const void* k, const void* v,
                        const void* text_k, const void* text_v, void* out, void* stream);
