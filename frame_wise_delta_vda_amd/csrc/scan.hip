@@ -23,6 +23,8 @@
 // the same way each step; Ainv R is taken as hi*hi + hi*lo + lo*hi, which leaves a
 // relative error of order 2^-16 per product (far below the bf16 rounding of the inputs
 // and output).  The operands of the next step are in flight while a step computes.
+// The states leave the chain only for the readout: float32 and blocked for float32
+// plans, bf16 in the readout's operand order for bfloat16 plans.
 #include "vda_device.h"
 #include "vda_internal.h"
 

@@ -11,10 +11,16 @@
 // One workgroup per (b, h, frame).  K and V stream once through LDS in chunks of
 // 64 tokens; G and Bm accumulate in MFMA registers (fp32).  The reduction runs
 // over tokens, so both MFMA operands need 8 consecutive tokens of one feature per
-// lane: each lane loads an 8-token x 8-feature block with 16-byte loads, transposes
-// it in registers (v_perm_b32) and stores it token-contiguous into LDS, from where
-// fragments are read with 16-byte LDS loads.  After the last chunk, G goes to LDS
-// and is inverted in place (Gauss-Jordan); Bm and Ainv go to the workspace.
+// lane:
+//  - d = dv = 128: chunks are staged in LDS token-major exactly as loaded, two chunks
+//    in flight per thread, and each operand is formed by two transposing LDS reads
+//    (ds_read_b64_tr_b16);
+//  - other widths: each lane loads an 8-token x 8-feature block with 16-byte loads,
+//    transposes it in registers (v_perm_b32) and stores it token-contiguous into LDS,
+//    from where operands are read with 16-byte LDS loads.
+// After the last chunk the workgroup inverts lam I + G: at d = 128 by a blocked
+// symmetric sweep on the MFMA accumulators, at smaller d by Gauss-Jordan in LDS.  Bm
+// and Ainv go to the workspace.
 #include "vda_device.h"
 #include "vda_internal.h"
 

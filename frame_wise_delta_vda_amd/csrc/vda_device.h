@@ -12,7 +12,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
-constexpr int kThreads = 256;  // 4 waves per workgroup in every kernel
+constexpr int kThreads = 256;  // 4 waves per workgroup (the bf16 scan alone uses d / 16 waves)
 constexpr int kXcds = 8;       // MI355X: 8 XCDs, workgroups dealt round-robin
 
 template <typename T>
