@@ -127,8 +127,8 @@ def run(args):
     q, k, v, tk, tv = (dev[x] for x in W.TENSORS)
 
     def step():
-        # one whole forward pass through the C ABI: the product call, with its own
-        # schedule (the scans may overlap the last statistics launch on a second stream)
+        # one whole forward pass through the C ABI: the product call (statistics, scans and
+        # readout, three launches on the current stream)
         plan.forward(q, k, v, tk, tv, out)
 
     print(f"[bench] {w.name}: warmup {args.warmup}", file=sys.stderr, flush=True)

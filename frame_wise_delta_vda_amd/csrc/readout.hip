@@ -154,7 +154,7 @@ struct ReadF32 {
 template <int D, int DV>
 __global__ void __launch_bounds__(kThreads)
 readout_f32_kernel(const float* __restrict__ q, const float* __restrict__ xf,
-                   const float* __restrict__ xb, float* __restrict__ out, int64_t F, int64_t n,
+                   const float* __restrict__ xb, float* __restrict__ out, int64_t n,
                    int64_t splits, int64_t tokens_per_split) {
   using C = ReadF32<D, DV>;
   extern __shared__ __align__(16) unsigned char smem[];
@@ -253,8 +253,8 @@ hipError_t launch_readout_t(const Problem& p, const void* q, void* out, hipStrea
                                                hipFuncAttributeMaxDynamicSharedMemorySize, lds)
                          : hipSuccess;
     hipLaunchKernelGGL(kern, dim3(unsigned(grid)), dim3(kThreads), lds, s,
-                       static_cast<const float*>(q), p.xf, p.xb, static_cast<float*>(out), p.F,
-                       p.n, splits, tps);
+                       static_cast<const float*>(q), p.xf, p.xb, static_cast<float*>(out), p.n,
+                       splits, tps);
   }
   return hipGetLastError();
 }
