@@ -171,7 +171,14 @@ struct ScanBf16Cfg {
   static constexpr int NCB = DV / (16 * CW);      // workgroups per chain
   static constexpr int NSLOT = 2;                 // operand ring: this step and the next
   static constexpr int CBE = 2 * KS * 4 * 16 * 8;  // R of one 16-column block: [hi/lo][ks][kg][n][8]
+  static constexpr int NUB = sym_blocks(D);       // stored 16 x 16 blocks of Ainv per plane
+  static constexpr int ABUF = 2 * NUB * 256;      // bf16 of one frame's two packed planes
+  static constexpr int APIECES = ABUF / 8;        // their 16-byte pieces
+  static constexpr int APT = (APIECES + THREADS - 1) / THREADS;  // pieces per thread
+  static constexpr int RSB = CW * CBE;            // bf16 of one R buffer
+  static constexpr int LDS_BYTES = (2 * ABUF + 2 * RSB) * 2;
   static_assert(DV % (16 * CW) == 0, "value width must be a multiple of 32");
+  static_assert(APIECES % 64 == 0 && THREADS % 64 == 0, "pieces must split into whole waves");
 };
 
 template <int D, int DV>
@@ -180,7 +187,9 @@ scan_bf16_kernel(const uint16_t* __restrict__ ainv_planes, const float* __restri
                  float* __restrict__ xf, float* __restrict__ xb, int64_t nchains, int64_t F,
                  float lam, int64_t grid) {
   using C = ScanBf16Cfg<D, DV>;
-  __shared__ __align__(16) uint16_t rs[2][C::CW * C::CBE];
+  extern __shared__ __align__(16) unsigned char smem[];
+  uint16_t* abuf = reinterpret_cast<uint16_t*>(smem);  // [2][ABUF]: packed Ainv planes of two steps
+  uint16_t* rsb = abuf + 2 * C::ABUF;                   // [2][RSB]: R of this step and the next
 
   const int64_t L = xcd_remap(blockIdx.x, grid);
   const int64_t chain = L / C::NCB;
@@ -205,30 +214,75 @@ scan_bf16_kernel(const uint16_t* __restrict__ ainv_planes, const float* __restri
     if (s > F) s = F;
     return (s == 0 || !backward) ? s : F + 1 - s;
   };
-  // slot t of the ring holds the Ainv rows of step t and the Bm that step t adds for t+1
-  uint4 A[C::NSLOT][C::KS][2];
-  float4 Bv[C::NSLOT][C::CW];
-  auto load_slot = [&](int64_t t, uint4 (&a)[C::KS][2], float4 (&bv)[C::CW]) {
-    const uint16_t* hi = ainv_h + frame_at(t) * int64_t(2 * D * D);
-    const uint16_t* lo = hi + D * D;
-    const float* bsrc = bm_h + frame_at(t + 1) * int64_t(D) * DV;
+
+  // Ainv of a step: the frame's packed planes (one contiguous run) are copied into an LDS
+  // buffer two steps ahead, and every wave forms its operand fragments from there one
+  // step ahead.  Blocks on and above the diagonal are read directly (lane: row n, 8
+  // consecutive columns); a block below it is the mirrored block read with the
+  // transposing LDS read: in each 16-lane group lane 4a + b receives element b of the
+  // 4-element reads of lanes a, a+4, a+8, a+12, so lane i points at row k + i/4 (+4 for
+  // the second read) and columns 4(i%4)..+3 of the mirrored block, and receives column
+  // i of 4 consecutive rows.
+  uint4 ast[C::APT];
+  auto stage_a = [&](int64_t t) {
+    const auto rsrc = make_rsrc(ainv_h + frame_at(t) * int64_t(2 * D * D), uint32_t(C::APIECES * 16));
+#pragma unroll
+    for (int i = 0; i < C::APT; ++i) ast[i] = buffer_load16(rsrc, uint32_t((i * C::THREADS + tid) * 16));
+  };
+  auto commit_a = [&](int b) {
+#pragma unroll
+    for (int i = 0; i < C::APT; ++i) {
+      const int piece = i * C::THREADS + tid;  // whole waves fall on either side of the end
+      if (piece < C::APIECES) *reinterpret_cast<uint4*>(abuf + b * C::ABUF + piece * 8) = ast[i];
+    }
+  };
+  auto tr_frag = [&](const uint16_t* blk, int kh) -> uint4 {
+    typedef short v4s __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) v4s* lds_v4s;
+    const uint16_t* p = blk + (8 * kh + (n >> 2)) * 16 + 4 * (n & 3);
+    const v4s x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(p));
+    const v4s y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(p + 64));
+    const uint2 xl = __builtin_bit_cast(uint2, x), yl = __builtin_bit_cast(uint2, y);
+    return make_uint4(xl.x, xl.y, yl.x, yl.y);
+  };
+  auto frags_a = [&](int b, uint4 (&a)[C::KS][2]) {
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
-      const int off = ((wave * C::KS + ks) * 64 + lane) * 8;  // frag_index(16 wave + n, 32 ks + 8 g, D)
-      a[ks][0] = *reinterpret_cast<const uint4*>(hi + off);
-      a[ks][1] = *reinterpret_cast<const uint4*>(lo + off);
+      const int bc = 2 * ks + (g >> 1);  // column block of this lane's half of the k-step
+      const int lo_b = wave < bc ? wave : bc, hi_b = wave < bc ? bc : wave;
+#pragma unroll
+      for (int pl = 0; pl < 2; ++pl) {
+        const uint16_t* blk = abuf + b * C::ABUF + pl * C::NUB * 256 + sym_block(lo_b, hi_b, D) * 256;
+        if (wave <= 2 * ks) {               // every lane on or above the diagonal
+          a[ks][pl] = *reinterpret_cast<const uint4*>(blk + n * 16 + 8 * (g & 1));
+        } else if (wave > 2 * ks + 1) {     // every lane below it
+          a[ks][pl] = tr_frag(blk, g & 1);
+        } else {                            // the diagonal block of one half, mirrored block of the other
+          const uint4 d = *reinterpret_cast<const uint4*>(blk + n * 16 + 8 * (g & 1));
+          const uint4 t = tr_frag(blk, g & 1);
+          a[ks][pl] = bc >= wave ? d : t;
+        }
+      }
     }
+  };
+
+  // slot t of the ring holds the Ainv fragments of step t and the Bm that step t adds for t+1
+  uint4 A[C::NSLOT][C::KS][2];
+  float4 Bv[C::NSLOT][C::CW];
+  auto load_bm = [&](int64_t t, float4 (&bv)[C::CW]) {
+    const float* bsrc = bm_h + frame_at(t + 1) * int64_t(D) * DV;
 #pragma unroll
     for (int cw = 0; cw < C::CW; ++cw)
       bv[cw] = *reinterpret_cast<const float4*>(bsrc + blk_index(row0, c0 + 16 * cw + n, D));
   };
   // R fragment (8 consecutive k of column n) and the 4-row output slot of a lane
   auto rs_frag = [&](int buf, int cw, int hl, int ks) -> const uint4* {
-    return reinterpret_cast<const uint4*>(&rs[buf][cw * C::CBE + ((hl * C::KS + ks) * 4 + g) * 128 + n * 8]);
+    return reinterpret_cast<const uint4*>(&rsb[buf * C::RSB + cw * C::CBE + ((hl * C::KS + ks) * 4 + g) * 128 + n * 8]);
   };
   auto rs_out = [&](int buf, int cw, int hl) -> uint2* {
-    return reinterpret_cast<uint2*>(&rs[buf][cw * C::CBE + ((hl * C::KS + wave / 2) * 4 + 2 * (wave % 2) + g / 2) * 128 +
-                                             n * 8 + 4 * (g % 2)]);
+    return reinterpret_cast<uint2*>(&rsb[buf * C::RSB + cw * C::CBE +
+                                         ((hl * C::KS + wave / 2) * 4 + 2 * (wave % 2) + g / 2) * 128 +
+                                         n * 8 + 4 * (g % 2)]);
   };
   auto write_r = [&](int buf, int cw, float r0, float r1, float r2, float r3) {
     uint32_t h01, l01, h23, l23;
@@ -244,14 +298,19 @@ scan_bf16_kernel(const uint16_t* __restrict__ ainv_planes, const float* __restri
     const float4 b4 = *reinterpret_cast<const float4*>(bm_h + blk_index(row0, c0 + 16 * cw + n, D));
     write_r(0, cw, b4.x, b4.y, b4.z, b4.w);
   }
-#pragma unroll
-  for (int t = 0; t < C::NSLOT - 1; ++t) load_slot(t, A[t], Bv[t]);
+  stage_a(0);
+  commit_a(0);
+  stage_a(1);
+  commit_a(1);
+  load_bm(0, Bv[0]);
   __syncthreads();
+  frags_a(0, A[0]);
 
   auto step = [&](int64_t s, uint4 (&a)[C::KS][2], float4 (&bv)[C::CW], uint4 (&a_fill)[C::KS][2],
                   float4 (&bv_fill)[C::CW]) {
     const int buf = int(s & 1);
-    load_slot(s + C::NSLOT - 1, a_fill, bv_fill);
+    stage_a(s + 2);  // lands during this step; goes to the LDS buffer that held step s
+    load_bm(s + 1, bv_fill);
     // every R fragment of the step in one LDS round trip, then the MFMA chains
     uint4 rf[C::CW][C::KS][2];
 #pragma unroll
@@ -291,6 +350,10 @@ scan_bf16_kernel(const uint16_t* __restrict__ ainv_planes, const float* __restri
         write_r(buf ^ 1, cw, __builtin_fmaf(lam, x[cw][0], bv[cw].x), __builtin_fmaf(lam, x[cw][1], bv[cw].y),
                 __builtin_fmaf(lam, x[cw][2], bv[cw].z), __builtin_fmaf(lam, x[cw][3], bv[cw].w));
     }
+    // next step's fragments (its planes were committed before the last barrier), then the
+    // planes of step s+2 into the buffer whose fragments were taken a step ago
+    frags_a(buf ^ 1, a_fill);
+    commit_a(buf);
     __syncthreads();
   };
 
@@ -304,16 +367,23 @@ scan_bf16_kernel(const uint16_t* __restrict__ ainv_planes, const float* __restri
 }
 
 template <int D, int DV>
-hipError_t launch_scan_t(const Problem& p, hipStream_t s) {
+hipError_t launch_scan_t(const Problem& p, hipStream_t s, bool prepare) {
   const int64_t nchains = 2 * p.B * p.H;
   if (p.bf16) {
     using C = ScanBf16Cfg<D, DV>;
+    auto kern = scan_bf16_kernel<D, DV>;
+    if (prepare)
+      return C::LDS_BYTES > 65536 ? hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                        hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                        C::LDS_BYTES)
+                                  : hipSuccess;
     const int64_t grid = ((nchains + kXcds - 1) / kXcds) * kXcds * C::NCB;
-    hipLaunchKernelGGL((scan_bf16_kernel<D, DV>), dim3(unsigned(grid)), dim3(C::THREADS), 0, s,
+    hipLaunchKernelGGL(kern, dim3(unsigned(grid)), dim3(C::THREADS), C::LDS_BYTES, s,
                        reinterpret_cast<const uint16_t*>(p.ainv), p.bm, p.xf, p.xb, nchains, p.F,
                        p.lam, grid);
   } else {
     using C = ScanCfg<D, DV>;
+    if (prepare) return hipSuccess;  // static LDS only
     const int64_t grid = ((nchains + kXcds - 1) / kXcds) * kXcds * C::NCB;
     hipLaunchKernelGGL((scan_kernel<D, DV>), dim3(unsigned(grid)), dim3(kThreads), 0, s, p.ainv,
                        p.bm, p.xf, p.xb, nchains, p.F, p.lam, grid);
@@ -325,7 +395,17 @@ hipError_t launch_scan_t(const Problem& p, hipStream_t s) {
 
 hipError_t launch_scan(const Problem& p, hipStream_t s) {
 #define VDA_CASE(DD, VV) \
-  if (p.d == DD && p.dv == VV) return launch_scan_t<DD, VV>(p, s);
+  if (p.d == DD && p.dv == VV) return launch_scan_t<DD, VV>(p, s, false);
+  VDA_CASE(32, 32) VDA_CASE(32, 64) VDA_CASE(32, 128)
+  VDA_CASE(64, 32) VDA_CASE(64, 64) VDA_CASE(64, 128)
+  VDA_CASE(128, 32) VDA_CASE(128, 64) VDA_CASE(128, 128)
+#undef VDA_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t prepare_scan(const Problem& p) {
+#define VDA_CASE(DD, VV) \
+  if (p.d == DD && p.dv == VV) return launch_scan_t<DD, VV>(p, nullptr, true);
   VDA_CASE(32, 32) VDA_CASE(32, 64) VDA_CASE(32, 128)
   VDA_CASE(64, 32) VDA_CASE(64, 64) VDA_CASE(64, 128)
   VDA_CASE(128, 32) VDA_CASE(128, 64) VDA_CASE(128, 128)

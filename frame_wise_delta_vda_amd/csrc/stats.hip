@@ -369,7 +369,7 @@ stats_bf16_kernel(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v
 
   float* bmo = bm + (bh * F1 + fi) * int64_t(D) * DV;
   uint16_t* hi_plane = reinterpret_cast<uint16_t*>(ainv + (bh * F1 + fi) * int64_t(D) * D);
-  uint16_t* lo_plane = hi_plane + D * D;
+  uint16_t* lo_plane = hi_plane + sym_blocks(D) * 256;
   if constexpr (D == 128) {
     // ---- epilogue (d = 128): Bm tiles to the workspace; lam I + G inverted in the
     // accumulators by the blocked sweep; A^{-1} = -(swept matrix) written out.
@@ -400,15 +400,18 @@ stats_bf16_kernel(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v
     static_assert(6 * 16 * kPbs * 4 <= C::MAIN_BYTES, "sweep buffers exceed the staging area");
     sweep_neg_inverse_128(t, reinterpret_cast<float*>(smem), wave, lane);
     // A^{-1} is symmetric: lane l's column j of tile c is row j of A^{-1}, and its
-    // registers 4q..4q+3 are 4 consecutive columns of that row (8 bytes per plane).
+    // registers 4q..4q+3 are 4 consecutive columns of that row (8 bytes per plane).  Only
+    // the 16 x 16 blocks on and above the diagonal are stored (sym_index).
 #pragma unroll
     for (int c = 0; c < 4; ++c)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
+        const int row = 32 * c + l32, col = 32 * wave + 8 * q + 4 * (lane >> 5);
+        if ((row >> 4) > (col >> 4)) continue;
         uint32_t h01, l01, h23, l23;
         split_bf16x2(-t[c][4 * q + 0], -t[c][4 * q + 1], h01, l01);
         split_bf16x2(-t[c][4 * q + 2], -t[c][4 * q + 3], h23, l23);
-        const int off = frag_index(32 * c + l32, 32 * wave + 8 * q + 4 * (lane >> 5), D);
+        const int off = sym_index(row, col, D);
         *reinterpret_cast<uint2*>(hi_plane + off) = make_uint2(h01, h23);
         *reinterpret_cast<uint2*>(lo_plane + off) = make_uint2(l01, l23);
       }
@@ -436,19 +439,20 @@ stats_bf16_kernel(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v
   float a[D / 16][D / 16];
   spd_inverse_gj<D>(gsm, C::GS, lam, rowv, colv, a);
   // A^{-1} as two bfloat16 planes, hi then lo (hi + lo = A^{-1} to ~2^-17 relative), for
-  // the split-bf16 MFMA products of the scan; same bytes as one float32 matrix.  The
-  // planes are fragment-ordered (frag_index): a thread's TS consecutive columns of a row
-  // stay contiguous, so each row goes out as one TS*2-byte store per plane.
+  // the split-bf16 MFMA products of the scan.  Only the 16 x 16 blocks on and above the
+  // diagonal are stored (sym_index, row-major blocks): a thread's TS consecutive columns of
+  // a row stay contiguous, so each row goes out as one TS*2-byte store per plane.
   constexpr int TS = D / 16;
   const int tr = tid >> 4, tcol = tid & 15;
 #pragma unroll
   for (int i = 0; i < TS; ++i) {
+    if (((tr * TS + i) >> 4) > ((tcol * TS) >> 4)) continue;
     uint32_t hw[TS / 2], lw[TS / 2];
 #pragma unroll
     for (int j = 0; j < TS; j += 2) {
       split_bf16x2(a[i][j], a[i][j + 1], hw[j / 2], lw[j / 2]);
     }
-    const int off = frag_index(tr * TS + i, tcol * TS, D);
+    const int off = sym_index(tr * TS + i, tcol * TS, D);
     if constexpr (TS == 8) {
       *reinterpret_cast<uint4*>(hi_plane + off) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
       *reinterpret_cast<uint4*>(lo_plane + off) = make_uint4(lw[0], lw[1], lw[2], lw[3]);

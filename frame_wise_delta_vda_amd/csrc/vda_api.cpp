@@ -140,7 +140,8 @@ vda_status vda_plan_create(int64_t B, int64_t H, int64_t F, int64_t n, int64_t d
   plan->timed_calls = 0;
   plan->timing_events = nullptr;
   // kernel attributes once, here, so that a forward pass makes no runtime call but launches
-  if (vda::prepare_stats(p) != hipSuccess || vda::prepare_readout(p) != hipSuccess) {
+  if (vda::prepare_stats(p) != hipSuccess || vda::prepare_scan(p) != hipSuccess ||
+      vda::prepare_readout(p) != hipSuccess) {
     (void)hipGetLastError();
     if (plan->workspace != nullptr) (void)hipFree(plan->workspace);
     delete plan;

@@ -129,6 +129,19 @@ __host__ __device__ constexpr int frag_index(int row, int col, int d) {
          (col & 7);
 }
 
+// Packed upper triangle of a symmetric d x d bfloat16 plane (A^{-1} is symmetric): the
+// 16 x 16 blocks (R, C) with R <= C, block (R, C) at index R*NB - R*(R-1)/2 + (C - R)
+// for NB = d/16, each block row-major (element (r, c) of the block at 16 r + c).
+// Block (R, C) with R > C is the transpose of block (C, R).
+__host__ __device__ constexpr int sym_blocks(int d) { return (d / 16) * (d / 16 + 1) / 2; }
+__host__ __device__ constexpr int sym_block(int R, int C, int d) {
+  return R * (d / 16) - R * (R - 1) / 2 + (C - R);
+}
+// element (row, col) of the plane, for row / 16 <= col / 16
+__host__ __device__ constexpr int sym_index(int row, int col, int d) {
+  return sym_block(row >> 4, col >> 4, d) * 256 + (row & 15) * 16 + (col & 15);
+}
+
 // Layout of a d x dv bfloat16 state for the readout: the transpose in fragment order,
 // so the operand block of W^T (16 value columns x 32 key rows) that a 16x16x32 MFMA of
 // the readout takes is 1 KB contiguous, lane 16*((r%32)/8) + c%16 holding rows

@@ -33,6 +33,7 @@ hipError_t launch_readout(const Problem& p, const void* q, void* out, hipStream_
 // once at plan creation on the plan's device, so that launches make no other runtime
 // call (they can then be captured in a graph).
 hipError_t prepare_stats(const Problem& p);
+hipError_t prepare_scan(const Problem& p);
 hipError_t prepare_readout(const Problem& p);
 
 }  // namespace vda

@@ -137,11 +137,13 @@ const char* vda_status_string(vda_status s);
 /* Device pointers into the plan's workspace, for checking intermediate results
  * after a synchronised forward pass.  Layouts, with BH = B*H and frame index 0 for
  * the text and 1..F for the frames:
- *   ainv  [BH][F+1][d][d]   (lam I + K^T K)^{-1}: float32 row-major for float32 plans; for
- *                           bfloat16 plans each frame's d*d*4 bytes hold two bfloat16
- *                           planes of d*d, hi then lo, with hi + lo = the inverse, each
- *                           fragment-ordered: element (r, c) at
- *                           (((r/16 * d/32 + c/32) * 4 + (c%32)/8) * 16 + r%16) * 8 + c%8
+ *   ainv  [BH][F+1][d][d]   (lam I + K^T K)^{-1}: float32 row-major for float32 plans.  For
+ *                           bfloat16 plans each frame's d*d*4 bytes start with two
+ *                           bfloat16 planes, hi then lo, with hi + lo = the inverse; the
+ *                           inverse is symmetric and a plane stores only its 16 x 16 blocks
+ *                           (R, C) with R <= C, NB = d/16 of them per side: block (R, C) at
+ *                           index R*NB - R*(R-1)/2 + (C - R), 256 elements each, row-major;
+ *                           a plane is NB*(NB+1)/2 * 256 elements
  *   bm    [BH][F+1][d*dv]   K^T V, float32, blocked (below)
  *   x_fwd [BH][F][d*dv]     forward state after frame f (f = 1..F at index f-1)
  *   x_bwd [BH][F][d*dv]     backward state after frame f

@@ -129,13 +129,22 @@ def test_intermediates_match_oracle():
                 return t.cpu().numpy().view(np.uint16)
             return t.cpu().numpy().astype(np.float64)
 
-        ainv = fetch(ainv_p, (BH, F1, d, d))
-        if w.dtype == "bf16":  # per frame two fragment-ordered bfloat16 planes, hi then lo
-            u16 = ainv.astype(np.float32).view(np.uint16).reshape(BH, F1, 2, d // 16, d // 32, 4, 16, 8)
-            # [rb][cb][c%32/8][r%16][c%8] -> [rb][r%16][cb][c%32/8][c%8] (layout in include/vda.h)
-            u16 = np.transpose(u16, (0, 1, 2, 3, 6, 4, 5, 7)).reshape(BH, F1, 2, d, d)
-            ainv = (W.bf16_bits_to_float32(u16[:, :, 0]).astype(np.float64) +
-                    W.bf16_bits_to_float32(u16[:, :, 1]).astype(np.float64))
+        if w.dtype == "f32":
+            ainv = fetch(ainv_p, (BH, F1, d, d))
+        else:
+            # per frame two bfloat16 planes, hi then lo, each the packed upper triangle of
+            # 16 x 16 row-major blocks: block (R, C), R <= C, at R*NB - R*(R-1)/2 + C - R
+            nb = d // 16
+            nub = nb * (nb + 1) // 2
+            u16 = fetch(ainv_p, (BH, F1, 2 * d * d), torch.int16)[:, :, :2 * nub * 256]
+            planes = W.bf16_bits_to_float32(u16.reshape(BH, F1, 2, nub, 16, 16)).astype(np.float64)
+            blocks = planes[:, :, 0] + planes[:, :, 1]
+            ainv = np.zeros((BH, F1, d, d))
+            for R in range(nb):
+                for Cb in range(R, nb):
+                    blk = blocks[:, :, R * nb - R * (R - 1) // 2 + Cb - R]
+                    ainv[:, :, 16 * R:16 * R + 16, 16 * Cb:16 * Cb + 16] = blk
+                    ainv[:, :, 16 * Cb:16 * Cb + 16, 16 * R:16 * R + 16] = np.swapaxes(blk, -1, -2)
         def unblock(a):  # [..., d*dv] blocked -> [..., d, dv] row-major (layout in include/vda.h)
             lead = a.shape[:-1]
             a = a.reshape(lead + (dv // 16, d // 16, 4, 16, 4))
