@@ -46,7 +46,7 @@ def source_hash(kernel: str) -> str:
 
 def algorithmic(w):
     """Bytes and flops the method itself requires, per launch of each stage."""
-    es = w.elem_bytes
+    es, eo = w.elem_bytes, w.out_bytes  # input and output element bytes
     BH = w.B * w.H
     tok = BH * (w.F * w.n + w.T)
     vid = BH * w.F * w.n
@@ -54,7 +54,7 @@ def algorithmic(w):
         "stats": {"bytes": tok * (w.d + w.dv) * es,
                   "flops": tok * (2 * w.d * w.d + 2 * w.d * w.dv) + BH * (w.F + 1) * 2 * w.d ** 3},
         "scan": {"bytes": 0, "flops": 2 * BH * (w.F + 1) * 2 * w.d * w.d * w.dv},
-        "readout": {"bytes": vid * (w.d + w.dv) * es, "flops": vid * 2 * w.d * w.dv},
+        "readout": {"bytes": vid * (w.d * es + w.dv * eo), "flops": vid * 2 * w.d * w.dv},
     }
 
 
@@ -105,6 +105,7 @@ def to_device(w, arrays):
     import torch
     dev = {}
     for k, a in arrays.items():
+        # bfloat16 as torch bfloat16, FP8 e4m3 codes as uint8, float32 as is
         t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if w.dtype == "bf16" \
             else torch.from_numpy(a)
         dev[k] = t.to("cuda")
@@ -122,7 +123,8 @@ def run(args):
     dev = to_device(w, arrays)
     if args.no_cpu_baseline:
         del arrays
-    out = torch.empty(w.shapes()["out"], dtype=dev["q"].dtype, device="cuda")
+    out = torch.empty(w.shapes()["out"], device="cuda",
+                      dtype=torch.float32 if w.dtype == "f32" else torch.bfloat16)
     plan = binding.Plan(w.B, w.H, w.F, w.n, w.d, w.dv, w.T, w.lam, w.dtype)
     q, k, v, tk, tv = (dev[x] for x in W.TENSORS)
 
@@ -182,9 +184,10 @@ def run(args):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": w.dtype,
+        # arithmetic type of the path: FP8 inputs are converted to bfloat16 on load
+        "dtype": "f32" if w.dtype == "f32" else "bf16",
         "data": "synthetic",
-        "config": {"workload": w.name, "B": w.B, "H": w.H, "F": w.F, "n": w.n, "d": w.d, "dv": w.dv,
+        "config": {"workload": w.name, "input_dtype": w.dtype, "B": w.B, "H": w.H, "F": w.F, "n": w.n, "d": w.d, "dv": w.dv,
                    "T": w.T, "lambda": w.lam, "video_tokens_per_step": w.video_tokens,
                    "alg_bytes_per_step": w.algorithmic_bytes(),
                    "whole_step_GB/s": round(w.algorithmic_bytes() / (ms_step * 1e-3) / 1e9, 1)},

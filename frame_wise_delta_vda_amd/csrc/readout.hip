@@ -8,6 +8,8 @@
 //
 // float32 path: one workgroup per frame (or token range), W kept in fp32 in LDS,
 // 32x32x2 fp32 MFMA, operands loaded straight from HBM.
+#include <type_traits>
+
 #include "vda_device.h"
 #include "vda_internal.h"
 
@@ -27,7 +29,13 @@ namespace {
 //  - O^T = W^T Q^T goes through a wave-private LDS patch so the stores are whole rows
 //    (1 KB contiguous per wave instruction).
 // Q is loaded and O stored with streaming cache policies, through buffer descriptors
-// bounded by the frame's last row, so ragged frame ends need no branch.
+// bounded by the frame's last row, so ragged frame ends need no branch.  FP8 e4m3 Q
+// (In = uint8_t) is converted to bfloat16 just before its MFMA; the output is bfloat16
+// either way.  At d >= 64 a lane loads 16 consecutive FP8 features at once and feeds
+// them to two k-steps (features 16 (g + 4 m) .. +15 to k-steps 2m and 2m + 1, g = lane /
+// 16), which keeps the loads as wide as the bfloat16 ones; the scan stores the states
+// of such plans with their rows in the same order (paired_row), so the W fragments are
+// loaded exactly as for bfloat16.  8-byte loads of one k-step each were 25% slower.
 template <int D, int DV>
 struct ReadBf16 {
   static constexpr int TT = 64;                 // tokens per tile (16 per wave)
@@ -42,13 +50,19 @@ struct ReadBf16 {
   static_assert(OST >= 1, "value width too large for one wave store pass");
 };
 
-template <int D, int DV>
+template <int D, int DV, typename In>
 __global__ void __launch_bounds__(kThreads, 2)
-readout_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ xf,
+readout_bf16_kernel(const In* __restrict__ q, const uint16_t* __restrict__ xf,
                     const uint16_t* __restrict__ xb, uint16_t* __restrict__ out, int64_t n,
                     int64_t tiles_per_frame, int64_t splits, int64_t tiles_per_split,
                     int64_t head_blocks, int64_t tail_splits, int64_t tail_tiles_per_split) {
   using C = ReadBf16<D, DV>;
+  constexpr int EB = int(sizeof(In));  // bytes per Q element
+  constexpr bool PAIR = EB == 1 && C::KS >= 2;  // one FP8 load feeds two k-steps
+  constexpr int NQL = PAIR ? C::KS / 2 : C::KS;  // Q loads per lane and tile
+  // a Q load: 8 bfloat16 features (16 bytes), 16 FP8 features (16 bytes) or, at d = 32,
+  // 8 FP8 features (8 bytes)
+  using QRaw = typename std::conditional<EB == 1 && !PAIR, uint2, uint4>::type;
   extern __shared__ __align__(16) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -75,15 +89,18 @@ readout_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     const int64_t r = n - tok0;
     return uint32_t(r < 0 ? 0 : (r < 16 ? r : 16));
   };
-  auto load_q = [&](int64_t tile, uint4 (&dst)[C::KS]) {
+  auto load_q = [&](int64_t tile, QRaw (&dst)[NQL]) {
     const int64_t tok0 = tile * C::TT + 16 * wave;
-    const auto rs = make_rsrc(q + (frame * n + tok0) * D, wave_rows(tok0) * D * 2);
+    const auto rs = make_rsrc(q + (frame * n + tok0) * D, wave_rows(tok0) * D * EB);
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks)
-      dst[ks] = buffer_load16<kCacheNt>(rs, uint32_t(c16 * D * 2 + (32 * ks + 8 * g4) * 2));
+    for (int i = 0; i < NQL; ++i) {
+      if constexpr (PAIR) dst[i] = buffer_load16<kCacheNt>(rs, uint32_t(c16 * D + 16 * (g4 + 4 * i)));
+      else if constexpr (EB == 1) dst[i] = buffer_load8<kCacheNt>(rs, uint32_t(c16 * D + 32 * i + 8 * g4));
+      else dst[i] = buffer_load16<kCacheNt>(rs, uint32_t((c16 * D + 32 * i + 8 * g4) * 2));
+    }
   };
 
-  uint4 pfa[C::KS], pfb[C::KS];
+  QRaw pfa[NQL], pfb[NQL];
   load_q(t_first, pfa);
   load_q(t_first + 1 < t_last ? t_first + 1 : t_first, pfb);
 
@@ -112,11 +129,20 @@ readout_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     }
   }
 
-  auto step = [&](int64_t tile, uint4 (&pf)[C::KS]) {
+  auto step = [&](int64_t tile, QRaw (&pf)[NQL]) {
     const int64_t tok0 = tile * C::TT + 16 * wave;
     uint4 qf[C::KS];
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) qf[ks] = pf[ks];
+    for (int i = 0; i < NQL; ++i) {
+      if constexpr (PAIR) {
+        qf[2 * i] = e4m3x8_to_bf16x8(make_uint2(pf[i].x, pf[i].y));
+        qf[2 * i + 1] = e4m3x8_to_bf16x8(make_uint2(pf[i].z, pf[i].w));
+      } else if constexpr (EB == 1) {
+        qf[i] = e4m3x8_to_bf16x8(pf[i]);
+      } else {
+        qf[i] = pf[i];
+      }
+    }
     load_q(tile + 2 < t_last ? tile + 2 : t_last - 1, pf);  // unconditional: no phi, no copy
     // O^T block nb: the lane holds token c16, output features 16 nb + 4 g4 + 0..3
 #pragma unroll
@@ -234,11 +260,15 @@ hipError_t launch_readout_t(const Problem& p, const void* q, void* out, hipStrea
     }
     const int64_t head_blocks = head_frames * splits;
     const int64_t grid = head_blocks + (frames - head_frames) * tail_splits;
-    auto kern = readout_bf16_kernel<D, DV>;
-    hipLaunchKernelGGL(kern, dim3(unsigned(grid)), dim3(kThreads), C::LDS_BYTES, s,
-                       static_cast<const uint16_t*>(q), reinterpret_cast<const uint16_t*>(p.xf),
-                       reinterpret_cast<const uint16_t*>(p.xb), static_cast<uint16_t*>(out),
-                       p.n, tpf, splits, tps, head_blocks, tail_splits, tail_tps);
+    auto launch = [&](auto kern, auto in) {
+      using In = decltype(in);
+      hipLaunchKernelGGL(kern, dim3(unsigned(grid)), dim3(kThreads), C::LDS_BYTES, s,
+                         static_cast<const In*>(q), reinterpret_cast<const uint16_t*>(p.xf),
+                         reinterpret_cast<const uint16_t*>(p.xb), static_cast<uint16_t*>(out),
+                         p.n, tpf, splits, tps, head_blocks, tail_splits, tail_tps);
+    };
+    if (p.fp8) launch(readout_bf16_kernel<D, DV, uint8_t>, uint8_t{});
+    else launch(readout_bf16_kernel<D, DV, uint16_t>, uint16_t{});
   } else {
     // one workgroup per frame, split only when there are too few frames to fill the chip
     int64_t splits = 1;

@@ -24,7 +24,8 @@
 // relative error of order 2^-16 per product (far below the bf16 rounding of the inputs
 // and output).  The operands of the next step are in flight while a step computes.
 // The states leave the chain only for the readout: float32 and blocked for float32
-// plans, bf16 in the readout's operand order for bfloat16 plans.
+// plans, bf16 in the readout's operand order for bfloat16 plans (rows in the paired
+// order when the inputs are FP8 and d >= 64).
 #include "vda_device.h"
 #include "vda_internal.h"
 
@@ -185,7 +186,7 @@ template <int D, int DV>
 __global__ void __launch_bounds__(4 * D)
 scan_bf16_kernel(const uint16_t* __restrict__ ainv_planes, const float* __restrict__ bm,
                  float* __restrict__ xf, float* __restrict__ xb, int64_t nchains, int64_t F,
-                 float lam, int64_t grid) {
+                 float lam, int64_t grid, bool paired) {
   using C = ScanBf16Cfg<D, DV>;
   extern __shared__ __align__(16) unsigned char smem[];
   uint16_t* abuf = reinterpret_cast<uint16_t*>(smem);  // [2][ABUF]: packed Ainv planes of two steps
@@ -204,6 +205,8 @@ scan_bf16_kernel(const uint16_t* __restrict__ ainv_planes, const float* __restri
   const int n = lane & 15, g = lane >> 4;
   const int c0 = cb * 16 * C::CW;
   const int row0 = wave * 16 + 4 * g;  // first of the 4 output rows of this lane
+  // where those rows go in the stored state (FP8 plans: the paired row order)
+  const int srow0 = paired ? paired_row(row0) : row0;
 
   const uint16_t* ainv_h = ainv_planes + bh * F1 * int64_t(2 * D * D);
   const float* bm_h = bm + bh * F1 * int64_t(D) * DV;
@@ -342,7 +345,7 @@ scan_bf16_kernel(const uint16_t* __restrict__ ainv_planes, const float* __restri
       for (int cw = 0; cw < C::CW; ++cw)
         __builtin_nontemporal_store(
             u32x2{pack_bf16x2(x[cw][0], x[cw][1]), pack_bf16x2(x[cw][2], x[cw][3])},
-            reinterpret_cast<u32x2*>(dst + state_index(row0, c0 + 16 * cw + n, D)));
+            reinterpret_cast<u32x2*>(dst + state_index(srow0, c0 + 16 * cw + n, D)));
     }
     if (s < F) {
 #pragma unroll
@@ -380,7 +383,7 @@ hipError_t launch_scan_t(const Problem& p, hipStream_t s, bool prepare) {
     const int64_t grid = ((nchains + kXcds - 1) / kXcds) * kXcds * C::NCB;
     hipLaunchKernelGGL(kern, dim3(unsigned(grid)), dim3(C::THREADS), C::LDS_BYTES, s,
                        reinterpret_cast<const uint16_t*>(p.ainv), p.bm, p.xf, p.xb, nchains, p.F,
-                       p.lam, grid);
+                       p.lam, grid, p.fp8 && D >= 64);
   } else {
     using C = ScanCfg<D, DV>;
     if (prepare) return hipSuccess;  // static LDS only

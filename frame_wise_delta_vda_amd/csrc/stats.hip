@@ -21,6 +21,8 @@
 // After the last chunk the workgroup inverts lam I + G: at d = 128 by a blocked
 // symmetric sweep on the MFMA accumulators, at smaller d by Gauss-Jordan in LDS.  Bm
 // and Ainv go to the workspace.
+#include <type_traits>
+
 #include "vda_device.h"
 #include "vda_internal.h"
 
@@ -175,21 +177,24 @@ struct StatsBf16 {
   static constexpr int LDS_BYTES = MAIN_BYTES + 4 * D * 4;  // + pivot row/col buffers
 };
 
-template <int D, int DV>
+// In: uint16_t (bfloat16 inputs) or uint8_t (FP8 e4m3 inputs, converted to bfloat16 as
+// they are written to LDS, so everything after the staging is the same).
+template <int D, int DV, typename In>
 __global__ void __launch_bounds__(kThreads, 2)
-stats_bf16_kernel(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-                  const uint16_t* __restrict__ tk, const uint16_t* __restrict__ tv,
+stats_bf16_kernel(const In* __restrict__ k, const In* __restrict__ v,
+                  const In* __restrict__ tk, const In* __restrict__ tv,
                   float* __restrict__ ainv, float* __restrict__ bm,
                   int64_t F, int64_t n, int64_t T, float lam) {
   using C = StatsBf16<D, DV>;
+  constexpr bool FP8 = sizeof(In) == 1;
   extern __shared__ __align__(16) unsigned char smem[];
   uint16_t* stage = reinterpret_cast<uint16_t*>(smem);
 
   const int64_t F1 = F + 1;
   const int64_t fi = blockIdx.x % F1;          // 0 = text, 1..F = frames
   const int64_t bh = blockIdx.x / F1;
-  const uint16_t* kp;
-  const uint16_t* vp;
+  const In* kp;
+  const In* vp;
   int64_t ntok;
   if (fi == 0) {
     kp = tk + bh * T * D;
@@ -207,7 +212,7 @@ stats_bf16_kernel(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v
   const int tg = tid & 7, seg = tid >> 3;
   const bool loader = C::DEEP || seg < C::NSEG;
   const bool seg_is_k = seg < D / 8;
-  const uint16_t* src = seg_is_k ? kp + seg * 8 : vp + (seg - D / 8) * 8;
+  const In* src = seg_is_k ? kp + seg * 8 : vp + (seg - D / 8) * 8;
   const int64_t src_stride = seg_is_k ? D : DV;
   const int lds_row0 = seg * 8;  // transposed rows 8*seg .. 8*seg+7 (K rows, then V rows)
 
@@ -221,19 +226,27 @@ stats_bf16_kernel(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v
 
   const int64_t nchunks = (ntok + C::TC - 1) / C::TC;
 
-  auto load_chunk = [&](int64_t ch, uint4 (&r)[8]) {
+  // 8 features of one token: 16 bytes (bfloat16) or 8 (FP8)
+  using Raw = typename std::conditional<FP8, uint2, uint4>::type;
+  auto load_chunk = [&](int64_t ch, Raw (&r)[8]) {
     const int64_t t0 = ch * C::TC + tg * 8;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      r[i] = make_uint4(0, 0, 0, 0);
+      if constexpr (FP8) r[i] = make_uint2(0, 0);
+      else r[i] = make_uint4(0, 0, 0, 0);
       if (loader && t0 + i < ntok)
-        r[i] = *reinterpret_cast<const uint4*>(src + (t0 + i) * src_stride);
+        r[i] = *reinterpret_cast<const Raw*>(src + (t0 + i) * src_stride);
     }
   };
-  auto store_chunk = [&](int buf, const uint4 (&r)[8]) {
+  auto store_chunk = [&](int buf, const Raw (&r)[8]) {
     if (!loader) return;
-    uint4 c[8];
-    transpose8x8_b16(r, c);
+    uint4 x[8], c[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if constexpr (FP8) x[i] = e4m3x8_to_bf16x8(r[i]);
+      else x[i] = r[i];
+    }
+    transpose8x8_b16(x, c);
     uint16_t* dst = stage + buf * C::BUF + lds_row0 * C::ROW + tg * 8;
 #pragma unroll
     for (int j = 0; j < 8; ++j) *reinterpret_cast<uint4*>(dst + j * C::ROW) = c[j];
@@ -275,28 +288,42 @@ stats_bf16_kernel(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v
   };
 
   if constexpr (C::DEEP) {
-    // Two chunks in flight per thread, staged in LDS token-major, exactly as loaded.
-    // Waves 0-1 load K, waves 2-3 V; instruction i of a wave covers 4 whole token rows
-    // (lane: token 32 (wave % 2) + 4 i + lane / 16, 8 features from 8 (lane % 16)).  The
-    // buffer descriptor spans the frame, so loads past its last token return zeros and a
-    // ragged or missing chunk multiplies in nothing.
-    const int tok_l = 32 * (wave & 1) + (lane >> 4);
-    const auto rs = make_rsrc(wave < 2 ? kp : vp, uint32_t(ntok * 256));
-    const uint32_t voff = uint32_t(tok_l * 256 + (lane & 15) * 16);
-    uint16_t* const st_lane = stage + tok_l * C::TROW + (wave >> 1) * D + (lane & 15) * 8;
-    uint4 ra[8], rn[8];
+    // Two chunks in flight per thread, staged in LDS token-major, as loaded (FP8 codes
+    // converted to bfloat16 on the way).  Waves 0-1 load K, waves 2-3 V, with 16-byte
+    // loads; a token row is 256 bytes (bfloat16) or 128 (FP8), so instruction i of a wave
+    // covers 4 or 8 whole rows (lane: token 32 (wave % 2) + TPL i + lane / LPR, bytes
+    // 16 (lane % LPR) of the row).  The buffer descriptor spans the frame, so loads past
+    // its last token return zeros and a ragged or missing chunk multiplies in nothing.
+    constexpr int ROWB = 128 * int(sizeof(In));  // bytes per token row of K or V
+    constexpr int LPR = ROWB / 16;               // lanes per row
+    constexpr int TPL = 64 / LPR;                // rows per load instruction
+    constexpr int NLD = 32 / TPL;                // loads per chunk per lane
+    constexpr int FPL = 16 / int(sizeof(In));    // features per lane and load
+    const int tok_l = 32 * (wave & 1) + lane / LPR;
+    const auto rs = make_rsrc(wave < 2 ? kp : vp, uint32_t(ntok * ROWB));
+    const uint32_t voff = uint32_t(tok_l * ROWB + (lane % LPR) * 16);
+    uint16_t* const st_lane = stage + tok_l * C::TROW + (wave >> 1) * D + (lane % LPR) * FPL;
+    uint4 ra[NLD], rn[NLD];
     auto chunk_base = [&](int64_t ch) -> uint32_t {
       // chunk indices past the end stay at nchunks: their bytes are past the frame
-      return voff + uint32_t((ch < nchunks ? ch : nchunks) * C::TC * 256);
+      return voff + uint32_t((ch < nchunks ? ch : nchunks) * C::TC * ROWB);
     };
-    auto load_deep = [&](int64_t ch, uint4 (&r)[8]) {
+    auto load_deep = [&](int64_t ch, uint4 (&r)[NLD]) {
       const uint32_t base = chunk_base(ch);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) r[i] = buffer_load16<kCacheNt>(rs, base + uint32_t(i * 1024));
+      for (int i = 0; i < NLD; ++i) r[i] = buffer_load16<kCacheNt>(rs, base + uint32_t(i * TPL * ROWB));
     };
-    auto store_rows = [&](int buf, const uint4 (&r)[8]) {
+    auto store_rows = [&](int buf, const uint4 (&r)[NLD]) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4*>(st_lane + buf * C::BUF + 4 * i * C::TROW) = r[i];
+      for (int i = 0; i < NLD; ++i) {
+        uint16_t* dst = st_lane + buf * C::BUF + TPL * i * C::TROW;
+        if constexpr (FP8) {
+          *reinterpret_cast<uint4*>(dst) = e4m3x8_to_bf16x8(make_uint2(r[i].x, r[i].y));
+          *reinterpret_cast<uint4*>(dst + 8) = e4m3x8_to_bf16x8(make_uint2(r[i].z, r[i].w));
+        } else {
+          *reinterpret_cast<uint4*>(dst) = r[i];
+        }
+      }
     };
     // MFMA operand of 8 consecutive tokens of one feature from the token-major rows, by two
     // transposing LDS reads (ds_read_b64_tr_b16).  In each 16-lane group the read hands
@@ -326,15 +353,17 @@ stats_bf16_kernel(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v
       }
     };
     // Multiply the chunk in LDS buffer buf while loading chunk ch into r.  The memory
-    // queue is usually full, so a load can stall its wave at issue; two loads go out
-    // before each k-step, and a stalled issue waits beside the previous k-step's MFMAs
-    // rather than ahead of all of them.
-    auto mult_load = [&](int buf, int64_t ch, uint4 (&r)[8]) {
+    // queue is usually full, so a load can stall its wave at issue; the loads are spread
+    // over the k-steps (two or one before each), and a stalled issue waits beside the
+    // previous k-step's MFMAs rather than ahead of all of them.
+    constexpr int LPK = NLD / (C::TC / 16);  // loads per k-step
+    auto mult_load = [&](int buf, int64_t ch, uint4 (&r)[NLD]) {
       const uint32_t base = chunk_base(ch);
 #pragma unroll
       for (int ks = 0; ks < C::TC / 16; ++ks) {
-        r[2 * ks] = buffer_load16<kCacheNt>(rs, base + uint32_t(2 * ks * 1024));
-        r[2 * ks + 1] = buffer_load16<kCacheNt>(rs, base + uint32_t((2 * ks + 1) * 1024));
+#pragma unroll
+        for (int j = 0; j < LPK; ++j)
+          r[LPK * ks + j] = buffer_load16<kCacheNt>(rs, base + uint32_t((LPK * ks + j) * TPL * ROWB));
         kstep_tm(buf, ks);
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -352,7 +381,7 @@ stats_bf16_kernel(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v
       __syncthreads();
     }
   } else {
-    uint4 r[8];
+    Raw r[8];
     if (nchunks > 0) {
       load_chunk(0, r);
       store_chunk(0, r);
@@ -578,15 +607,20 @@ hipError_t launch_stats_t(const Problem& p, const void* k, const void* v, const 
   const int64_t blocks = p.B * p.H * (p.F + 1);
   if (p.bf16) {
     constexpr int lds = StatsBf16<D, DV>::LDS_BYTES;
-    auto kern = stats_bf16_kernel<D, DV>;
-    if (prepare)
-      return lds > 65536 ? hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, lds)
-                         : hipSuccess;
-    hipLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(kThreads), lds, s,
-                       static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
-                       static_cast<const uint16_t*>(tk), static_cast<const uint16_t*>(tv), p.ainv,
-                       p.bm, p.F, p.n, p.T, p.lam);
+    auto launch = [&](auto kern, auto in) -> hipError_t {
+      using In = decltype(in);
+      if (prepare)
+        return lds > 65536 ? hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, lds)
+                           : hipSuccess;
+      hipLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(kThreads), lds, s,
+                         static_cast<const In*>(k), static_cast<const In*>(v),
+                         static_cast<const In*>(tk), static_cast<const In*>(tv), p.ainv, p.bm, p.F,
+                         p.n, p.T, p.lam);
+      return hipGetLastError();
+    };
+    return p.fp8 ? launch(stats_bf16_kernel<D, DV, uint8_t>, uint8_t{})
+                 : launch(stats_bf16_kernel<D, DV, uint16_t>, uint16_t{});
   } else {
     constexpr int lds = StatsF32<D, DV>::LDS_BYTES;
     auto kern = stats_f32_kernel<D, DV>;

@@ -75,7 +75,8 @@ vda_status vda_plan_create(int64_t B, int64_t H, int64_t F, int64_t n, int64_t d
   *plan_out = nullptr;
   if (B < 0 || H < 0 || F < 0 || n < 0 || T < 0) return VDA_ERROR_INVALID_VALUE;
   if (!(std::isfinite(lambda) && lambda > 0.0f)) return VDA_ERROR_INVALID_VALUE;
-  if (dtype != VDA_DTYPE_F32 && dtype != VDA_DTYPE_BF16) return VDA_ERROR_NOT_SUPPORTED;
+  if (dtype != VDA_DTYPE_F32 && dtype != VDA_DTYPE_BF16 && dtype != VDA_DTYPE_FP8_E4M3)
+    return VDA_ERROR_NOT_SUPPORTED;
   if (!supported_width(d) || !supported_width(dv)) return VDA_ERROR_NOT_SUPPORTED;
   // a frame (or the text) is addressed with 32-bit byte offsets
   if (n > vda::kMaxFrameTokens || T > vda::kMaxFrameTokens) return VDA_ERROR_NOT_SUPPORTED;
@@ -111,14 +112,15 @@ vda_status vda_plan_create(int64_t B, int64_t H, int64_t F, int64_t n, int64_t d
   }
   p.B = B; p.H = H; p.F = F; p.n = n; p.d = d; p.dv = dv; p.T = T;
   p.lam = lambda;
-  p.bf16 = (dtype == VDA_DTYPE_BF16);
+  p.bf16 = (dtype != VDA_DTYPE_F32);  // FP8 inputs run the bfloat16 path after conversion
+  p.fp8 = (dtype == VDA_DTYPE_FP8_E4M3);
   p.ainv = p.bm = p.xf = p.xb = nullptr;
   plan->workspace = nullptr;
   plan->workspace_bytes = 0;
 
   const size_t ainv_n = size_t(ws_frames) * d * d;
   const size_t bm_n = size_t(ws_frames) * d * dv;
-  // states: float32 for float32 plans; bfloat16 (half the bytes) for bfloat16 plans
+  // states: float32 for float32 plans; bfloat16 (half the bytes) for the others
   const size_t x_n = size_t(frames) * d * dv / (p.bf16 ? 2 : 1);
   const size_t total = (ainv_n + bm_n + 2 * x_n) * sizeof(float);
   if (total > 0) {
@@ -188,10 +190,12 @@ vda_status vda_forward_stages(vda_plan_t plan, unsigned stages, const void* q, c
   const vda::Problem& p = plan->p;
   // No output element: nothing to compute and no pointer is read.
   if (p.B == 0 || p.H == 0 || p.F == 0 || p.n == 0) return VDA_SUCCESS;
-  const size_t es = p.bf16 ? 2 : 4;
+  const size_t es = p.fp8 ? 1 : p.bf16 ? 2 : 4;  // input element bytes
+  const size_t eo = p.bf16 ? 2 : 4;              // output element bytes
   const size_t bh = size_t(p.B) * size_t(p.H);
   const size_t qk_bytes = bh * size_t(p.F) * size_t(p.n) * size_t(p.d) * es;
-  const size_t vo_bytes = bh * size_t(p.F) * size_t(p.n) * size_t(p.dv) * es;
+  const size_t v_bytes = bh * size_t(p.F) * size_t(p.n) * size_t(p.dv) * es;
+  const size_t o_bytes = bh * size_t(p.F) * size_t(p.n) * size_t(p.dv) * eo;
   const size_t tk_bytes = bh * size_t(p.T) * size_t(p.d) * es;
   const size_t tv_bytes = bh * size_t(p.T) * size_t(p.dv) * es;
   const bool do_stats = stages & VDA_STAGE_STATS;
@@ -205,15 +209,15 @@ vda_status vda_forward_stages(vda_plan_t plan, unsigned stages, const void* q, c
     size_t bytes;
     bool used;
   } args[6] = {{q, qk_bytes, do_read},         {k, qk_bytes, do_stats},
-               {v, vo_bytes, do_stats},        {text_k, tk_bytes, do_stats},
-               {text_v, tv_bytes, do_stats},   {out, vo_bytes, do_read}};
+               {v, v_bytes, do_stats},         {text_k, tk_bytes, do_stats},
+               {text_v, tv_bytes, do_stats},   {out, o_bytes, do_read}};
   for (const Arg& a : args) {
     if (!a.used || a.bytes == 0) continue;
     if (a.ptr == nullptr) return VDA_ERROR_INVALID_VALUE;
     if (!aligned16(a.ptr)) return VDA_ERROR_MISALIGNED;
   }
-  if (do_read && vo_bytes > 0) {
-    Range o{reinterpret_cast<uintptr_t>(out), reinterpret_cast<uintptr_t>(out) + vo_bytes};
+  if (do_read && o_bytes > 0) {
+    Range o{reinterpret_cast<uintptr_t>(out), reinterpret_cast<uintptr_t>(out) + o_bytes};
     for (int i = 0; i < 5; ++i) {
       if (args[i].ptr == nullptr || args[i].bytes == 0) continue;
       Range r{reinterpret_cast<uintptr_t>(args[i].ptr),

@@ -98,6 +98,21 @@ __device__ __forceinline__ void transpose8x8_b16(const uint4 (&in)[8], uint4 (&o
   }
 }
 
+// OCP FP8 e4m3 -> bfloat16.  Every e4m3 value is exact in bfloat16 (3 mantissa bits,
+// exponents 2^-9 .. 2^8), and gfx950 converts two codes per instruction
+// (v_cvt_scalef32_pk_bf16_fp8, scale 1: the codes' own values; the NaN codes give NaN).
+// Codes 0 and 1 of `w` (HI = false) or 2 and 3 (HI = true) -> bits of (bf16, bf16), low
+// first.
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+// 8 codes (byte i of the pair = element i) -> 8 bfloat16, element order kept
+__device__ __forceinline__ uint4 e4m3x8_to_bf16x8(uint2 x) {
+  return make_uint4(e4m3x2_to_bf16x2<false>(x.x), e4m3x2_to_bf16x2<true>(x.x),
+                    e4m3x2_to_bf16x2<false>(x.y), e4m3x2_to_bf16x2<true>(x.y));
+}
+
 // Blocked layout of a d x dv float32 matrix in the workspace (Bm and the states X):
 // 16-column blocks, then 16-row blocks, then the lane pattern of a 16x16 MFMA tile,
 // [row/4 within the tile][column][row%4], so each lane of a tile owns 4 contiguous floats.
@@ -149,6 +164,17 @@ __host__ __device__ constexpr int sym_index(int row, int col, int d) {
 __host__ __device__ constexpr int state_index(int row, int col, int d) {
   return frag_index(col, row, d);
 }
+// Row order of the states of plans with FP8 inputs (d >= 64): the readout feeds each
+// lane two k-steps from one 16-byte load of 16 consecutive FP8 query features, so state
+// row r = [r/64][g][h][r%8] (g = (r/16)%4, h = (r/8)%2) must sit where the plain order
+// keeps row [r/64][h][g][r%8]: bit 3 of the row moves above bits 4-5.  Rows 4i..4i+3
+// stay contiguous.
+__host__ __device__ constexpr int paired_row(int r) {
+  return (r & ~0x38) | ((r & 0x08) << 2) | ((r & 0x30) >> 1);
+}
+__host__ __device__ constexpr int state_index_paired(int row, int col, int d) {
+  return frag_index(col, paired_row(row), d);
+}
 
 // Raw buffer access: the descriptor (base, byte size) lives in SGPRs and must be
 // wave-uniform; the hardware range-checks every access against the size, so
@@ -168,6 +194,10 @@ constexpr int kCacheDefault = 0, kCacheNt = 2, kCacheStreamOut = 16 | 2;
 template <int CPOL = kCacheDefault>
 __device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, CPOL));
+}
+template <int CPOL = kCacheDefault>
+__device__ __forceinline__ uint2 buffer_load8(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)byte_off, 0, CPOL));
 }
 template <int CPOL = kCacheDefault>
 __device__ __forceinline__ void buffer_store16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, uint4 v) {

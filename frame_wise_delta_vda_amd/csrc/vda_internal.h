@@ -15,7 +15,8 @@ constexpr int64_t kMaxFrameTokens = (int64_t(1) << 24) - 256;
 struct Problem {
   int64_t B, H, F, n, d, dv, T;
   float lam;
-  bool bf16;        // element type of q, k, v, text and out
+  bool bf16;        // bfloat16 path: bfloat16 out and states (set for FP8 inputs as well)
+  bool fp8;         // q, k, v and text are OCP FP8 e4m3 codes (bfloat16 path otherwise)
   int num_cus;      // compute units of the plan's device (sizes persistent grids)
   // workspace (float32), frame index 0 = text, 1..F = frames
   float* ainv;      // [BH][F+1][d][d]

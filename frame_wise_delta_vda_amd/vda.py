@@ -16,7 +16,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("VDA_LIBRARY", os.path.join(HERE, "libvda.so"))
 HEADER = os.path.join(os.path.dirname(HERE), "include", "vda.h")
 
-VDA_DTYPE_F32, VDA_DTYPE_BF16 = 0, 1
+VDA_DTYPE_F32, VDA_DTYPE_BF16, VDA_DTYPE_FP8_E4M3 = 0, 1, 2
+DTYPES = {"f32": VDA_DTYPE_F32, "bf16": VDA_DTYPE_BF16, "fp8": VDA_DTYPE_FP8_E4M3}
 STATUS = {0: "VDA_SUCCESS", 1: "VDA_ERROR_INVALID_VALUE", 2: "VDA_ERROR_NOT_SUPPORTED",
           3: "VDA_ERROR_MISALIGNED", 4: "VDA_ERROR_OUT_OF_MEMORY", 5: "VDA_ERROR_DEVICE"}
 VDA_SUCCESS, VDA_ERROR_INVALID_VALUE, VDA_ERROR_NOT_SUPPORTED = 0, 1, 2
@@ -106,9 +107,9 @@ def vda_status_string(status: int) -> str:
 
 
 def vda_plan_create(B, H, F, n, d, dv, T, lam, dtype) -> int:
-    """Returns the plan handle (an int).  dtype: VDA_DTYPE_F32 / VDA_DTYPE_BF16 or "f32"/"bf16"."""
+    """Returns the plan handle (an int).  dtype: a VDA_DTYPE_* value or "f32", "bf16", "fp8"."""
     if isinstance(dtype, str):
-        dtype = {"f32": VDA_DTYPE_F32, "bf16": VDA_DTYPE_BF16}[dtype]
+        dtype = DTYPES[dtype]
     h = ctypes.c_void_p()
     _check(load_library().vda_plan_create(B, H, F, n, d, dv, T, ctypes.c_float(lam), dtype,
                                           ctypes.byref(h)), "vda_plan_create")
@@ -186,9 +187,11 @@ class Plan:
         return vda_plan_workspace_bytes(self.handle)
 
     def out_like(self, q):
+        """Output tensor for inputs like q: float32 for float32 plans, else bfloat16."""
         import torch
         s = self.shape
-        return torch.empty((s["B"], s["H"], s["F"], s["n"], s["dv"]), dtype=q.dtype, device=q.device)
+        dt = torch.float32 if self.dtype in ("f32", VDA_DTYPE_F32) else torch.bfloat16
+        return torch.empty((s["B"], s["H"], s["F"], s["n"], s["dv"]), dtype=dt, device=q.device)
 
     def forward(self, q, k, v, text_k, text_v, out=None, stream=None):
         if out is None:

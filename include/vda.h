@@ -26,8 +26,8 @@
  *    crosses this boundary.
  *  - All tensors are device pointers into the memory of the GPU that was current
  *    when the plan was created, contiguous and row-major, in the plan's dtype
- *    (float32, or bfloat16 as raw 16-bit words), 16-byte aligned.  The caller owns
- *    them; the library never frees or keeps them past the call.
+ *    (vda_dtype), 16-byte aligned.  The caller owns them; the library never frees or
+ *    keeps them past the call.
  *  - Layouts (head-major, one contiguous n x d slab per (b,h,frame)):
  *      q, k   [B][H][F][n][d]      v, out [B][H][F][n][dv]
  *      text_k [B][H][T][d]         text_v [B][H][T][dv]
@@ -45,11 +45,17 @@ extern "C" {
 
 typedef struct vda_plan_s* vda_plan_t;
 
-/* Element type of q, k, v, text_k, text_v and out.  Accumulation, the state and
- * the solves are float32 in both cases. */
+/* Element types.  Accumulation and the solves are float32 in every case.
+ *   F32:      q, k, v, text_k, text_v and out are float32.
+ *   BF16:     all six are bfloat16, as raw 16-bit words.
+ *   FP8_E4M3: q, k, v, text_k and text_v are OCP FP8 E4M3 codes, one byte each (sign,
+ *             4 exponent bits with bias 7, 3 mantissa bits; largest magnitude 448; no
+ *             infinities; S.1111.111 is NaN); out is bfloat16.  Every code's value is
+ *             exact in bfloat16, and from there the pass is the BF16 one. */
 typedef enum {
   VDA_DTYPE_F32 = 0,
-  VDA_DTYPE_BF16 = 1
+  VDA_DTYPE_BF16 = 1,
+  VDA_DTYPE_FP8_E4M3 = 2
 } vda_dtype;
 
 typedef enum {
@@ -77,7 +83,7 @@ typedef enum {
  *     text state is zero and text_k / text_v may be NULL.
  *   d, dv in {32, 64, 128}: key/query width and value width.
  *   lambda: the regulariser, finite and > 0, shared by the text and every frame.
- *   dtype: element type of all tensors.
+ *   dtype: element types of the tensors (vda_dtype).
  * The plan allocates its workspace (hipMalloc, one block) on the current device and
  * keeps it until vda_plan_destroy.  On error *plan_out is set to NULL.
  * Errors: INVALID_VALUE, NOT_SUPPORTED, OUT_OF_MEMORY, DEVICE. */
@@ -138,7 +144,7 @@ const char* vda_status_string(vda_status s);
  * after a synchronised forward pass.  Layouts, with BH = B*H and frame index 0 for
  * the text and 1..F for the frames:
  *   ainv  [BH][F+1][d][d]   (lam I + K^T K)^{-1}: float32 row-major for float32 plans.  For
- *                           bfloat16 plans each frame's d*d*4 bytes start with two
+ *                           bfloat16 and FP8 plans each frame's d*d*4 bytes start with two
  *                           bfloat16 planes, hi then lo, with hi + lo = the inverse; the
  *                           inverse is symmetric and a plane stores only its 16 x 16 blocks
  *                           (R, C) with R <= C, NB = d/16 of them per side: block (R, C) at
@@ -149,11 +155,13 @@ const char* vda_status_string(vda_status s);
  *   x_bwd [BH][F][d*dv]     backward state after frame f
  * Blocked layout of a d x dv matrix M: element (r, c) is at
  *   (((c/16 * d/16 + r/16) * 4 + (r%16)/4) * 16 + c%16) * 4 + r%4.
- * The states are float32 and blocked for float32 plans.  For bfloat16 plans they are
+ * The states are float32 and blocked for float32 plans.  For the others they are
  * bfloat16 (the pointers then address d*dv bfloat16 per frame, not floats), rounded
  * once from the float32 chain, with element (r, c) at
  *   (((c/16 * d/32 + r/32) * 4 + (r%32)/8) * 16 + c%16) * 8 + r%8
- * (the operand order of the readout's MFMA); the chain itself runs in float32.
+ * (the operand order of the readout's MFMA); the chain itself runs in float32.  For FP8
+ * plans with d >= 64, r in that formula is the row with bit 3 moved above bits 4-5:
+ *   (row & ~0x38) | ((row & 0x08) << 2) | ((row & 0x30) >> 1).
  * The memory stays owned by the plan.  Any output pointer may be NULL. */
 vda_status vda_debug_workspace(vda_plan_t plan, const float** ainv, const float** bm,
                                const float** x_fwd, const float** x_bwd);

@@ -125,3 +125,32 @@ def test_timing_of_whole_passes():
     run_gpu(w, dev, plan=plan, out=out)
     assert plan.timings()[0] == 0
     plan.close()
+
+
+def test_fp8_plan_sizes_and_nan_codes():
+    """FP8 plans: inputs are one byte per element, the output and the workspace are the
+    bfloat16 plan's, and a NaN code (S.1111.111) in one key reaches the output."""
+    w = W.WORKLOADS[6].replace(H=1, F=3, n=100, T=8, d=64, dv=64)
+    say("[gpu] fp8 sizes and NaN codes")
+    plan = binding.Plan(w.B, w.H, w.F, w.n, w.d, w.dv, w.T, w.lam, w.dtype)
+    assert plan.workspace_bytes == 4 * (w.F + 1) * (w.d * w.d + w.d * w.dv) + 2 * 2 * w.F * w.d * w.dv
+    arrs = W.full_storage(w, threads=1)
+    arrs["k"] = arrs["k"].copy()
+    arrs["k"][0, 0, 1, 7, 2] = 0x7F  # frame 2 of 3 (index 1)
+    dev = to_device(w, arrs)
+    # a bfloat16-sized output argument is what the plan writes; q of the wrong byte size is
+    # not detectable, but a misaligned one is
+    out = torch.zeros(w.shapes()["out"], dtype=torch.bfloat16, device="cuda")
+    lib = binding.load_library()
+    s = torch.cuda.current_stream().cuda_stream
+    P = lambda t: t.data_ptr()
+    qv = dev["q"].view(-1)
+    assert lib.vda_forward(plan.handle, P(qv) + 8, P(dev["k"]), P(dev["v"]), P(dev["text_k"]),
+                           P(dev["text_v"]), P(out), s) == binding.VDA_ERROR_MISALIGNED
+    plan.forward(dev["q"], dev["k"], dev["v"], dev["text_k"], dev["text_v"], out)
+    torch.cuda.synchronize()
+    o = out_to_float64(out)[0, 0]
+    # frame 1's statistics are NaN; the forward chain carries that to frames 1..2 and the
+    # backward chain to frames 0..1, so every frame reads out NaN
+    assert np.isnan(o).all()
+    plan.close()

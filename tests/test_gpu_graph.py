@@ -16,13 +16,14 @@ pytestmark = pytest.mark.gpu
     (3, dict(H=2, F=5, n=333, T=20)),                 # bf16 d = dv = 128
     (2, dict(H=2, F=4, n=200, T=9)),                  # bf16 d = dv = 64
     (1, dict(H=2, F=3, n=100, T=16)),                 # fp32 d = dv = 32
+    (6, dict(H=2, F=5, n=333, T=20)),                 # FP8 inputs, d = dv = 128
 ])
 def test_forward_replays_in_a_graph(idx, over):
     w = W.WORKLOADS[idx].replace(name=f"graph_{idx}", **over)
     say(f"[gpu] graph replay {w.name}")
     dev = to_device(w, W.full_storage(w, threads=1))
     eager, plan = run_gpu(w, dev)
-    ints = torch.int16 if w.dtype == "bf16" else torch.int32
+    ints = torch.int32 if w.dtype == "f32" else torch.int16
 
     out = torch.empty_like(eager)
     side = torch.cuda.Stream()
@@ -43,8 +44,12 @@ def test_forward_replays_in_a_graph(idx, over):
         assert torch.equal(out.view(ints), eager.view(ints)), f"replay {i}"
 
     # new input values in the captured buffers: the replay follows them
-    dev["v"].mul_(-0.5)
-    dev["q"].mul_(2.0)
+    if w.dtype == "fp8":  # e4m3 codes: negate v, reverse the features of q
+        dev["v"].bitwise_xor_(0x80)
+        dev["q"].copy_(dev["q"].flip(-1))
+    else:
+        dev["v"].mul_(-0.5)
+        dev["q"].mul_(2.0)
     ref2, _ = run_gpu(w, dev, plan=plan)
     ref2 = ref2.clone()
     for i in range(2):

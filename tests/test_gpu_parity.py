@@ -1,6 +1,6 @@
 """GPU parity: the HIP library (through its C ABI) against the float64 oracle, on the
 same seeded, identically rounded inputs.  Bar: max per-(b,h,frame) relative Frobenius
-error <= 1e-4 for float32 workloads and <= 1e-2 for bfloat16 workloads."""
+error <= 1e-4 for float32 workloads and <= 1e-2 for bfloat16 and FP8 (e4m3) workloads."""
 import numpy as np
 import pytest
 import torch
@@ -46,7 +46,7 @@ def test_named_workload_full_parity(idx):
     plan.close()
 
 
-@pytest.mark.parametrize("idx", [3, 4, 5])
+@pytest.mark.parametrize("idx", [3, 4, 5, 6])
 def test_named_workload_sampled_parity(idx):
     """Full-size problem in the launch configuration the benchmark times; the oracle
     recomputes three whole (b,h) slices, every other slice is checked for finiteness."""
@@ -79,6 +79,17 @@ SMALL = [
     ("f32_32x64", dict(dtype="f32", d=32, dv=64, n=33, T=40, F=3, B=1, H=1)),
     ("bf16_lowrank_lam_small", dict(dtype="bf16", d=128, dv=128, n=300, T=16, F=6, B=1, H=1,
                                     kind="lowrank", lam=0.05)),
+    # FP8 e4m3 inputs: the d = dv = 128 staging (16-byte loads of 16 codes) and the others
+    # (8-byte loads of 8 codes), ragged chunks and tiles, split frames
+    ("fp8_128x128_ragged", dict(dtype="fp8", d=128, dv=128, n=200, T=37, F=5, B=2, H=2)),
+    ("fp8_64x128", dict(dtype="fp8", d=64, dv=128, n=130, T=5, F=4, B=1, H=3)),
+    ("fp8_128x64", dict(dtype="fp8", d=128, dv=64, n=97, T=64, F=3, B=1, H=2)),
+    ("fp8_32x32", dict(dtype="fp8", d=32, dv=32, n=300, T=1, F=6, B=1, H=2)),
+    ("fp8_128x128_no_text", dict(dtype="fp8", d=128, dv=128, n=64, T=0, F=3, B=1, H=1)),
+    ("fp8_split_frames", dict(dtype="fp8", d=128, dv=128, n=4000, T=10, F=2, B=1, H=1)),
+    ("fp8_n1", dict(dtype="fp8", d=64, dv=64, n=1, T=1, F=7, B=1, H=2)),
+    ("fp8_lowrank_lam_small", dict(dtype="fp8", d=128, dv=128, n=300, T=16, F=6, B=1, H=1,
+                                   kind="lowrank", lam=0.05)),
 ]
 
 
@@ -110,7 +121,9 @@ def test_intermediates_match_oracle():
     the forward/backward states against the oracle's."""
     for w in (W.WORKLOADS[1], W.WORKLOADS[2].replace(H=2, F=5, n=200, T=30),
               W.WORKLOADS[3].replace(H=1, F=4, n=300, T=20),
-              W.WORKLOADS[2].replace(H=1, F=3, n=100, T=8, d=32, dv=128)):
+              W.WORKLOADS[2].replace(H=1, F=3, n=100, T=8, d=32, dv=128),
+              W.WORKLOADS[6].replace(H=1, F=4, n=300, T=20),
+              W.WORKLOADS[6].replace(H=1, F=3, n=100, T=8, d=64, dv=32)):
         say(f"[gpu] intermediates {w.name}")
         dev = to_device(w, W.full_storage(w, threads=1))
         out, plan = run_gpu(w, dev)
@@ -160,6 +173,9 @@ def test_intermediates_match_oracle():
             def unfrag_state(u16):  # [c/16][r/32][(r%32)/8][c%16][r%8] -> [r][c] (include/vda.h)
                 a = u16.reshape(BH, w.F, dv // 16, d // 32, 4, 16, 8)
                 a = np.transpose(a, (0, 1, 3, 4, 6, 2, 5)).reshape(BH, w.F, d, dv)
+                if w.dtype == "fp8" and d >= 64:  # row r is stored at position paired(r)
+                    r = np.arange(d)
+                    a = a[:, :, (r & ~0x38) | ((r & 0x08) << 2) | ((r & 0x30) >> 1), :]
                 return W.bf16_bits_to_float32(a).astype(np.float64)
             xf = unfrag_state(fetch(xf_p, (BH, w.F, d * dv), torch.int16))
             xb = unfrag_state(fetch(xb_p, (BH, w.F, d * dv), torch.int16))
@@ -210,3 +226,20 @@ def test_stages_compose_to_forward():
     assert torch.equal(full.view(torch.int16), staged.view(torch.int16))
     plan.close()
 
+
+
+@pytest.mark.parametrize("d,dv", [(128, 128), (64, 128), (128, 32), (32, 64)])
+def test_fp8_plan_equals_bf16_plan_on_the_same_values(d, dv):
+    """Every e4m3 value is exact in bfloat16, and the FP8 plan converts right after loading,
+    so on the same values it must give the bfloat16 plan's output bit for bit."""
+    w8 = W.WORKLOADS[6].replace(H=2, F=3, n=333, T=21, d=d, dv=dv)
+    w16 = w8.replace(dtype="bf16")
+    say(f"[gpu] fp8 == bf16 d={d} dv={dv}")
+    codes = W.full_storage(w8, threads=1)
+    as_bf16 = {k: W.float32_to_bf16_bits(W.e4m3_codes_to_float32(c)) for k, c in codes.items()}
+    out8, p8 = run_gpu(w8, to_device(w8, codes))
+    out16, p16 = run_gpu(w16, to_device(w16, as_bf16))
+    assert out8.dtype == torch.bfloat16
+    assert torch.equal(out8.view(torch.int16), out16.view(torch.int16))
+    p8.close()
+    p16.close()

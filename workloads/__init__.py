@@ -22,8 +22,10 @@ with ``seed`` the workload's seed; all draws are float32 in this order:
   text_k ~ N(0,1) [T,d], text_v ~ N(0,1) [T,dv].
 
 Every row of k and text_k is scaled to unit L2 norm in float32.  For bfloat16
-workloads every tensor is then rounded to bfloat16 with round-to-nearest-even;
-the oracle receives those rounded values upcast exactly.
+workloads every tensor is then rounded to bfloat16 with round-to-nearest-even; for
+fp8 workloads the inputs are rounded to OCP FP8 e4m3 (round-to-nearest-even, magnitudes
+above 448 saturate to 448) and the output is bfloat16.  The oracle receives the rounded
+values upcast exactly.
 """
 from __future__ import annotations
 
@@ -49,7 +51,7 @@ class Workload:
     dv: int
     T: int
     lam: float
-    dtype: str            # "f32" or "bf16": storage type of q,k,v,text_k,text_v and out
+    dtype: str            # "f32", "bf16" or "fp8": storage type of q,k,v,text_k,text_v
     seed: int
     kind: str = "gaussian"  # "gaussian" or "lowrank"
     rank: int = 16
@@ -61,6 +63,12 @@ class Workload:
 
     @property
     def elem_bytes(self) -> int:
+        """Bytes per input element."""
+        return {"f32": 4, "bf16": 2, "fp8": 1}[self.dtype]
+
+    @property
+    def out_bytes(self) -> int:
+        """Bytes per output element: float32 for float32 workloads, else bfloat16."""
         return 4 if self.dtype == "f32" else 2
 
     def shapes(self) -> Dict[str, tuple]:
@@ -71,8 +79,8 @@ class Workload:
     def algorithmic_bytes(self) -> int:
         """Bytes the method must move: q, k, v, text read once and out written once."""
         B, H, F, n, d, dv, T = self.B, self.H, self.F, self.n, self.d, self.dv, self.T
-        elems = B * H * (F * n * (2 * d + 2 * dv) + T * (d + dv))
-        return elems * self.elem_bytes
+        inputs = B * H * (F * n * (2 * d + dv) + T * (d + dv))
+        return inputs * self.elem_bytes + B * H * F * n * dv * self.out_bytes
 
     def replace(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -90,6 +98,9 @@ WORKLOADS: Dict[int, Workload] = {
                 dtype="bf16", seed=4, grid=(32, 32)),
     5: Workload("ill_conditioned_bf16", B=4, H=16, F=45, n=2016, d=128, dv=128, T=128,
                 lam=0.1, dtype="bf16", seed=5, kind="lowrank", rank=16, grid=(56, 36)),
+    # the 768p shape with FP8 (e4m3) inputs and a bfloat16 output
+    6: Workload("768p_fp8", B=1, H=24, F=90, n=4032, d=128, dv=128, T=256, lam=1.0,
+                dtype="fp8", seed=6, grid=(84, 48)),
 }
 
 
@@ -115,6 +126,41 @@ def float32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
 def bf16_bits_to_float32(b: np.ndarray) -> np.ndarray:
     """Exact widening of bfloat16 bits to float32."""
     return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+# ----------------------------------------------------------------------------
+# FP8 e4m3 storage helpers (OCP 8-bit format: 1 sign bit, 4 exponent bits with bias 7,
+# 3 mantissa bits; subnormals below 2^-6; no infinities; S.1111.111 is NaN; the largest
+# finite magnitude is 448)
+# ----------------------------------------------------------------------------
+
+def float32_to_e4m3_codes(x: np.ndarray) -> np.ndarray:
+    """Round to e4m3, to nearest with ties to even; magnitudes above 448 saturate to 448.
+    Inputs here are finite.  Returns the uint8 codes."""
+    x = np.asarray(x, dtype=np.float32)
+    a = np.abs(x).astype(np.float64)
+    neg = np.signbit(x)
+    # binade of a (normal range 2^-6 .. 2^8; below 2^-6 the subnormal quantum 2^-9 applies)
+    e = np.clip(np.floor(np.log2(np.where(a > 0, a, 1.0))), -6, 8)
+    quantum = np.exp2(e - 3)
+    r = np.minimum(np.round(a / quantum) * quantum, 448.0)  # np.round: ties to even
+    e2 = np.clip(np.floor(np.log2(np.where(r > 0, r, 1.0))), -6, 8)
+    normal = r >= 2.0 ** -6
+    exp_field = np.where(normal, e2 + 7, 0)
+    man_field = np.where(normal, r / np.exp2(e2) * 8 - 8, r / 2.0 ** -9)
+    code = (neg.astype(np.uint32) << 7) | (exp_field.astype(np.uint32) << 3) | man_field.astype(np.uint32)
+    return code.astype(np.uint8)
+
+
+def e4m3_codes_to_float32(c: np.ndarray) -> np.ndarray:
+    """Exact value of e4m3 codes as float32 (NaN for the NaN codes)."""
+    c = np.asarray(c, dtype=np.uint8).astype(np.int64)
+    s = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 15
+    m = c & 7
+    v = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    v = np.where((e == 15) & (m == 7), np.nan, v)
+    return (s * v).astype(np.float32)
 
 
 def _rownorm(x: np.ndarray) -> np.ndarray:
@@ -156,9 +202,11 @@ def head_float32(w: Workload, b: int, h: int) -> Dict[str, np.ndarray]:
 
 
 def to_storage(w: Workload, x: np.ndarray) -> np.ndarray:
-    """float32 -> storage array (float32 or uint16 bfloat16 bits)."""
+    """float32 -> storage array (float32, uint16 bfloat16 bits or uint8 e4m3 codes)."""
     if w.dtype == "f32":
         return np.ascontiguousarray(x, dtype=np.float32)
+    if w.dtype == "fp8":
+        return float32_to_e4m3_codes(x)
     return float32_to_bf16_bits(x)
 
 
@@ -166,6 +214,8 @@ def storage_to_float64(w: Workload, s: np.ndarray) -> np.ndarray:
     """Storage array -> the exact values as float64 (what the oracle receives)."""
     if w.dtype == "f32":
         return np.asarray(s, dtype=np.float32).astype(np.float64)
+    if w.dtype == "fp8":
+        return e4m3_codes_to_float32(s).astype(np.float64)
     return bf16_bits_to_float32(s).astype(np.float64)
 
 
@@ -180,7 +230,7 @@ def head_float64(w: Workload, b: int, h: int) -> Dict[str, np.ndarray]:
 
 
 def storage_dtype(w: Workload):
-    return np.float32 if w.dtype == "f32" else np.uint16
+    return {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8}[w.dtype]
 
 
 def full_storage(w: Workload, threads: Optional[int] = None) -> Dict[str, np.ndarray]:
