@@ -14,10 +14,12 @@
 // lane:
 //  - d = dv = 128: chunks are staged in LDS token-major exactly as loaded, two chunks
 //    in flight per thread, and each operand is formed by two transposing LDS reads
-//    (ds_read_b64_tr_b16);
-//  - other widths: each lane loads an 8-token x 8-feature block with 16-byte loads,
-//    transposes it in registers (v_perm_b32) and stores it token-contiguous into LDS,
-//    from where operands are read with 16-byte LDS loads.
+//    (ds_read_b64_tr_b16); with FP8 inputs the codes stay FP8 in LDS, operands come from
+//    transposing 8-bit reads (ds_read_b64_tr_b8) and G and Bm run on the FP8 MFMA;
+//  - other widths: each lane loads an 8-token x 8-feature block with 16-byte loads (8-byte
+//    loads of FP8 codes, converted exactly to bfloat16), transposes it in registers
+//    (v_perm_b32) and stores it token-contiguous into LDS, from where operands are read
+//    with 16-byte LDS loads.
 // After the last chunk the workgroup inverts lam I + G: at d = 128 by a blocked
 // symmetric sweep on the MFMA accumulators, at smaller d by Gauss-Jordan in LDS.  Bm
 // and Ainv go to the workspace.
@@ -170,7 +172,11 @@ struct StatsBf16 {
   // the transposing LDS reads of four consecutive rows hit distinct banks)
   static constexpr int TROW = D + DV + 32;
   static constexpr int BUF = DEEP ? TC * TROW : (D + DV) * ROW;  // bf16 per staging buffer
-  static constexpr int STAGE_BYTES = 2 * BUF * 2;
+  // d = dv = 128 with FP8 inputs: raw codes, 128-token chunks, rows of 288 bytes
+  static constexpr int TC8 = 128;
+  static constexpr int TROW8 = 288;
+  static constexpr int BUF8 = TC8 * TROW8;       // bytes per FP8 staging buffer
+  static constexpr int STAGE_BYTES = cmax(2 * BUF * 2, DEEP ? 2 * BUF8 : 0);
   static constexpr int GS = D + 4;               // floats per LDS row of G
   static constexpr int G_BYTES = D * GS * 4;
   static constexpr int MAIN_BYTES = cmax(STAGE_BYTES, G_BYTES);
@@ -287,43 +293,113 @@ stats_bf16_kernel(const In* __restrict__ k, const In* __restrict__ v,
     for (int ks = 0; ks < C::TC / 16; ++ks) mult_kstep(buf, ks);
   };
 
-  if constexpr (C::DEEP) {
-    // Two chunks in flight per thread, staged in LDS token-major, as loaded (FP8 codes
-    // converted to bfloat16 on the way).  Waves 0-1 load K, waves 2-3 V, with 16-byte
-    // loads; a token row is 256 bytes (bfloat16) or 128 (FP8), so instruction i of a wave
-    // covers 4 or 8 whole rows (lane: token 32 (wave % 2) + TPL i + lane / LPR, bytes
-    // 16 (lane % LPR) of the row).  The buffer descriptor spans the frame, so loads past
-    // its last token return zeros and a ragged or missing chunk multiplies in nothing.
-    constexpr int ROWB = 128 * int(sizeof(In));  // bytes per token row of K or V
-    constexpr int LPR = ROWB / 16;               // lanes per row
-    constexpr int TPL = 64 / LPR;                // rows per load instruction
-    constexpr int NLD = 32 / TPL;                // loads per chunk per lane
-    constexpr int FPL = 16 / int(sizeof(In));    // features per lane and load
-    const int tok_l = 32 * (wave & 1) + lane / LPR;
-    const auto rs = make_rsrc(wave < 2 ? kp : vp, uint32_t(ntok * ROWB));
-    const uint32_t voff = uint32_t(tok_l * ROWB + (lane % LPR) * 16);
-    uint16_t* const st_lane = stage + tok_l * C::TROW + (wave >> 1) * D + (lane % LPR) * FPL;
-    uint4 ra[NLD], rn[NLD];
+  if constexpr (C::DEEP && FP8) {
+    // FP8 codes are staged as loaded, token-major, in 128-token chunks (rows of TROW8
+    // bytes: K then V, 256 bytes + 32 of padding so the transposing reads of a 32-lane half
+    // hit 64 distinct banks), and G and Bm run on the 32x32x64 FP8 MFMA: e4m3 products are
+    // exact and accumulate in fp32, as on the bfloat16 MFMA, at twice its rate and with half
+    // the LDS bytes.  Waves 0-1 load K, waves 2-3 V; instruction i of a wave covers 8 whole
+    // 128-byte rows (lane: token 64 (wave % 2) + 8 i + lane / 8, bytes 16 (lane % 8)).  Loads
+    // past the frame's last token return zeros.
+    const int64_t nch8 = (ntok + C::TC8 - 1) / C::TC8;
+    uint8_t* const stage8 = reinterpret_cast<uint8_t*>(smem);
+    const int tok_l = 64 * (wave & 1) + (lane >> 3);
+    const auto rs = make_rsrc(wave < 2 ? kp : vp, uint32_t(ntok * 128));
+    const uint32_t voff = uint32_t(tok_l * 128 + (lane & 7) * 16);
+    uint8_t* const st_lane = stage8 + tok_l * C::TROW8 + (wave >> 1) * 128 + (lane & 7) * 16;
+    uint4 ra[8], rn[8];
     auto chunk_base = [&](int64_t ch) -> uint32_t {
-      // chunk indices past the end stay at nchunks: their bytes are past the frame
-      return voff + uint32_t((ch < nchunks ? ch : nchunks) * C::TC * ROWB);
+      // chunk indices past the end stay at nch8: their bytes are past the frame
+      return voff + uint32_t((ch < nch8 ? ch : nch8) * C::TC8 * 128);
     };
-    auto load_deep = [&](int64_t ch, uint4 (&r)[NLD]) {
+    auto load8 = [&](int64_t ch, uint4 (&r)[8]) {
       const uint32_t base = chunk_base(ch);
 #pragma unroll
-      for (int i = 0; i < NLD; ++i) r[i] = buffer_load16<kCacheNt>(rs, base + uint32_t(i * TPL * ROWB));
+      for (int i = 0; i < 8; ++i) r[i] = buffer_load16<kCacheNt>(rs, base + uint32_t(i * 1024));
     };
-    auto store_rows = [&](int buf, const uint4 (&r)[NLD]) {
+    auto store8 = [&](int buf, const uint4 (&r)[8]) {
 #pragma unroll
-      for (int i = 0; i < NLD; ++i) {
-        uint16_t* dst = st_lane + buf * C::BUF + TPL * i * C::TROW;
-        if constexpr (FP8) {
-          *reinterpret_cast<uint4*>(dst) = e4m3x8_to_bf16x8(make_uint2(r[i].x, r[i].y));
-          *reinterpret_cast<uint4*>(dst + 8) = e4m3x8_to_bf16x8(make_uint2(r[i].z, r[i].w));
-        } else {
-          *reinterpret_cast<uint4*>(dst) = r[i];
-        }
+      for (int i = 0; i < 8; ++i)
+        *reinterpret_cast<uint4*>(st_lane + buf * C::BUF8 + 8 * i * C::TROW8) = r[i];
+    };
+    // FP8 MFMA operand: feature f0 + l % 32 of tokens 32 (l / 32) + 0..31, byte 8q + j holding
+    // token 32 (l / 32) + 8q + j, by four transposing 8-bit LDS reads (ds_read_b64_tr_b8).  In
+    // each 16-lane group that read hands lane i element i % 8 of the 8-byte reads of lanes
+    // i / 8, i / 8 + 2, ..., i / 8 + 14; so lane L of group g points at token
+    // 32 (g / 2) + 8q + L / 2 and bytes 16 (g % 2) + 8 (L % 2) of the 32-feature block, and
+    // receives one feature of 8 consecutive tokens.
+    const int fr8 = (32 * (lane >> 5) + ((lane & 15) >> 1)) * C::TROW8 + 16 * ((lane >> 4) & 1) + 8 * (lane & 1);
+    auto frag8 = [&](const uint8_t* rows, int f0) -> i32x8 {
+      typedef int v2i __attribute__((ext_vector_type(2)));
+      typedef __attribute__((address_space(3))) v2i* lds_v2i;
+      const uint8_t* p = rows + fr8 + f0;
+      i32x8 r;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const v2i x = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i)(p + 8 * q * C::TROW8));
+        r[2 * q] = x[0];
+        r[2 * q + 1] = x[1];
       }
+      return r;
+    };
+    // acc[rb] = G(rb, wave), acc[4 + rb] = Bm(rb, wave) over one 64-token k-step
+    auto kstep8 = [&](int buf, int ks) {
+      const uint8_t* rows = stage8 + buf * C::BUF8 + ks * 64 * C::TROW8;
+      const i32x8 bk = frag8(rows, wave * 32);
+      const i32x8 bv = frag8(rows, 128 + wave * 32);
+#pragma unroll
+      for (int rbi = 0; rbi < 4; ++rbi) {
+        const i32x8 a = frag8(rows, rbi * 32);
+        acc[rbi] = mfma32_fp8(a, bk, acc[rbi]);
+        acc[4 + rbi] = mfma32_fp8(a, bv, acc[4 + rbi]);
+      }
+    };
+    // multiply the chunk in buffer buf while loading chunk ch (4 loads before each k-step)
+    auto mult_load8 = [&](int buf, int64_t ch, uint4 (&r)[8]) {
+      const uint32_t base = chunk_base(ch);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) r[4 * ks + j] = buffer_load16<kCacheNt>(rs, base + uint32_t((4 * ks + j) * 1024));
+        kstep8(buf, ks);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    load8(0, ra);
+    load8(1, rn);
+    store8(0, ra);
+    __syncthreads();
+    for (int64_t ch = 0; ch < nch8; ch += 2) {
+      mult_load8(0, ch + 2, ra);
+      store8(1, rn);
+      __syncthreads();
+      mult_load8(1, ch + 3, rn);
+      store8(0, ra);
+      __syncthreads();
+    }
+  } else if constexpr (C::DEEP) {
+    // Two chunks in flight per thread, staged in LDS token-major, exactly as loaded.
+    // Waves 0-1 load K, waves 2-3 V; instruction i of a wave covers 4 whole token rows
+    // (lane: token 32 (wave % 2) + 4 i + lane / 16, 8 features from 8 (lane % 16)).  The
+    // buffer descriptor spans the frame, so loads past its last token return zeros and a
+    // ragged or missing chunk multiplies in nothing.
+    const int tok_l = 32 * (wave & 1) + (lane >> 4);
+    const auto rs = make_rsrc(wave < 2 ? kp : vp, uint32_t(ntok * 256));
+    const uint32_t voff = uint32_t(tok_l * 256 + (lane & 15) * 16);
+    uint16_t* const st_lane = stage + tok_l * C::TROW + (wave >> 1) * D + (lane & 15) * 8;
+    uint4 ra[8], rn[8];
+    auto chunk_base = [&](int64_t ch) -> uint32_t {
+      // chunk indices past the end stay at nchunks: their bytes are past the frame
+      return voff + uint32_t((ch < nchunks ? ch : nchunks) * C::TC * 256);
+    };
+    auto load_deep = [&](int64_t ch, uint4 (&r)[8]) {
+      const uint32_t base = chunk_base(ch);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) r[i] = buffer_load16<kCacheNt>(rs, base + uint32_t(i * 1024));
+    };
+    auto store_rows = [&](int buf, const uint4 (&r)[8]) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4*>(st_lane + buf * C::BUF + 4 * i * C::TROW) = r[i];
     };
     // MFMA operand of 8 consecutive tokens of one feature from the token-major rows, by two
     // transposing LDS reads (ds_read_b64_tr_b16).  In each 16-lane group the read hands
@@ -353,17 +429,15 @@ stats_bf16_kernel(const In* __restrict__ k, const In* __restrict__ v,
       }
     };
     // Multiply the chunk in LDS buffer buf while loading chunk ch into r.  The memory
-    // queue is usually full, so a load can stall its wave at issue; the loads are spread
-    // over the k-steps (two or one before each), and a stalled issue waits beside the
-    // previous k-step's MFMAs rather than ahead of all of them.
-    constexpr int LPK = NLD / (C::TC / 16);  // loads per k-step
-    auto mult_load = [&](int buf, int64_t ch, uint4 (&r)[NLD]) {
+    // queue is usually full, so a load can stall its wave at issue; two loads go out
+    // before each k-step, and a stalled issue waits beside the previous k-step's MFMAs
+    // rather than ahead of all of them.
+    auto mult_load = [&](int buf, int64_t ch, uint4 (&r)[8]) {
       const uint32_t base = chunk_base(ch);
 #pragma unroll
       for (int ks = 0; ks < C::TC / 16; ++ks) {
-#pragma unroll
-        for (int j = 0; j < LPK; ++j)
-          r[LPK * ks + j] = buffer_load16<kCacheNt>(rs, base + uint32_t((LPK * ks + j) * TPL * ROWB));
+        r[2 * ks] = buffer_load16<kCacheNt>(rs, base + uint32_t(2 * ks * 1024));
+        r[2 * ks + 1] = buffer_load16<kCacheNt>(rs, base + uint32_t((2 * ks + 1) * 1024));
         kstep_tm(buf, ks);
         __builtin_amdgcn_sched_barrier(0);
       }

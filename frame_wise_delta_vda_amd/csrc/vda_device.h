@@ -26,6 +26,16 @@ __device__ __forceinline__ f32x16 mfma32_bf16(uint4 a, uint4 b, f32x16 c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// 32x32x64 FP8 (OCP e4m3) MFMA, fp32 accumulate (scale operands 0: no block scaling).
+// Lane l holds row (A) / column (B) l%32 and 32 k values, one per byte; byte p of lane l
+// of A multiplies byte p of the lane of B with the same l/32, so A and B formed by the same
+// procedure contract over the same 64 k values in whatever order they are held.  Result
+// layout as for mfma32_bf16.  Products of e4m3 values are exact in fp32.
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ f32x16 mfma32_fp8(i32x8 a, i32x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
 // 32x32x2 fp32 MFMA.  Lane l holds A[l%32][l/32] and B[l/32][l%32]; result
 // layout as for mfma32_bf16.
 __device__ __forceinline__ f32x16 mfma32_f32(float a, float b, f32x16 c) {

@@ -229,17 +229,24 @@ def test_stages_compose_to_forward():
 
 
 @pytest.mark.parametrize("d,dv", [(128, 128), (64, 128), (128, 32), (32, 64)])
-def test_fp8_plan_equals_bf16_plan_on_the_same_values(d, dv):
-    """Every e4m3 value is exact in bfloat16, and the FP8 plan converts right after loading,
-    so on the same values it must give the bfloat16 plan's output bit for bit."""
+def test_fp8_plan_matches_bf16_plan_on_the_same_values(d, dv):
+    """Every e4m3 value is exact in bfloat16.  Where the FP8 plan converts right after
+    loading, it must give the bfloat16 plan's output bit for bit; at d = dv = 128 its
+    statistics run on the FP8 MFMA (exact products, fp32 sums in another order), so there
+    the outputs agree to the rounding of the bfloat16 output."""
     w8 = W.WORKLOADS[6].replace(H=2, F=3, n=333, T=21, d=d, dv=dv)
     w16 = w8.replace(dtype="bf16")
-    say(f"[gpu] fp8 == bf16 d={d} dv={dv}")
+    say(f"[gpu] fp8 vs bf16 d={d} dv={dv}")
     codes = W.full_storage(w8, threads=1)
     as_bf16 = {k: W.float32_to_bf16_bits(W.e4m3_codes_to_float32(c)) for k, c in codes.items()}
     out8, p8 = run_gpu(w8, to_device(w8, codes))
     out16, p16 = run_gpu(w16, to_device(w16, as_bf16))
     assert out8.dtype == torch.bfloat16
-    assert torch.equal(out8.view(torch.int16), out16.view(torch.int16))
+    if (d, dv) == (128, 128):
+        e = frame_errors(out_to_float64(out8), out_to_float64(out16))
+        say(f"  max rel diff {e.max():.3e}")
+        assert e.max() <= 2.0 ** -9
+    else:
+        assert torch.equal(out8.view(torch.int16), out16.view(torch.int16))
     p8.close()
     p16.close()
