@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the VDA forward pass on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 768p_bf16]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 768p_bf16] [--gated]
 
 One step = one whole forward pass (statistics, scans, readout) over one batch of
 seeded synthetic input already resident in HBM.  Prints ONE JSON line with the
@@ -32,6 +32,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
 KERNEL_SOURCES = {"stats": "stats.hip", "scan": "scan.hip", "readout": "readout.hip"}
 KERNEL_SYMBOLS = {"stats": "stats_bf16_kernel", "scan": "scan_bf16_kernel", "readout": "readout_bf16_kernel"}
+GATED_READOUT_SYMBOL = "readout_gated_kernel"  # the readout with the gated epilogue (--gated)
 COPY_PROBE_BYTES = 1 << 30
 
 
@@ -44,17 +45,23 @@ def source_hash(kernel: str) -> str:
     return h.hexdigest()[:16]
 
 
-def algorithmic(w):
-    """Bytes and flops the method itself requires, per launch of each stage."""
+def algorithmic(w, gated=False):
+    """Bytes and flops the method itself requires, per launch of each stage.  With the gated
+    epilogue the readout also reads the per-head weights and computes the two projections
+    (O W_g^T and O W_o^T, dv x dv per token) on top of O = Q W."""
     es, eo = w.elem_bytes, w.out_bytes  # input and output element bytes
     BH = w.B * w.H
     tok = BH * (w.F * w.n + w.T)
     vid = BH * w.F * w.n
+    readout = {"bytes": vid * (w.d * es + w.dv * eo), "flops": vid * 2 * w.d * w.dv}
+    if gated:
+        readout = {"bytes": readout["bytes"] + w.H * (2 * w.dv * w.dv * 2 + w.dv * 4),
+                   "flops": readout["flops"] + vid * 2 * 2 * w.dv * w.dv}
     return {
         "stats": {"bytes": tok * (w.d + w.dv) * es,
                   "flops": tok * (2 * w.d * w.d + 2 * w.d * w.dv) + BH * (w.F + 1) * 2 * w.d ** 3},
         "scan": {"bytes": 0, "flops": 2 * BH * (w.F + 1) * 2 * w.d * w.d * w.dv},
-        "readout": {"bytes": vid * (w.d * es + w.dv * eo), "flops": vid * 2 * w.d * w.dv},
+        "readout": readout,
     }
 
 
@@ -75,8 +82,9 @@ def read_traffic(workload_name):
     return out
 
 
-def cpu_baseline(w, arrays, budget_s=20.0, max_heads=None):
-    """Time the float64 oracle on whole (b,h) slices of the same inputs until ~budget_s."""
+def cpu_baseline(w, arrays, budget_s=20.0, max_heads=None, gate=None):
+    """Time the float64 oracle on whole (b,h) slices of the same inputs until ~budget_s
+    (with the gated epilogue when gate holds the weights as float64)."""
     import numpy as np
     import threadpoolctl
     import oracle
@@ -89,7 +97,11 @@ def cpu_baseline(w, arrays, budget_s=20.0, max_heads=None):
     for b, h in heads:
         x = {k: W.storage_to_float64(w, arrays[k][b, h]) for k in W.TENSORS}
         t0 = time.perf_counter()
-        oracle.vda_forward_head(x["q"], x["k"], x["v"], x["text_k"], x["text_v"], w.lam)
+        if gate is None:
+            oracle.vda_forward_head(x["q"], x["k"], x["v"], x["text_k"], x["text_v"], w.lam)
+        else:
+            oracle.vda_forward_gated_head(x["q"], x["k"], x["v"], x["text_k"], x["text_v"], w.lam,
+                                          gate["w_gate"][h], gate["b_gate"][h], gate["w_out"][h])
         spent += time.perf_counter() - t0
         done += 1
         if spent >= budget_s:
@@ -127,11 +139,21 @@ def run(args):
                       dtype=torch.float32 if w.dtype == "f32" else torch.bfloat16)
     plan = binding.Plan(w.B, w.H, w.F, w.n, w.d, w.dv, w.T, w.lam, w.dtype)
     q, k, v, tk, tv = (dev[x] for x in W.TENSORS)
+    gate = None
+    if args.gated:
+        import numpy as np
+        gate = W.gate_weights(w)
+        bits = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+        wg, wo = bits(gate["w_gate"]), bits(gate["w_out"])
+        bg = torch.from_numpy(np.ascontiguousarray(gate["b_gate"])).cuda()
 
     def step():
         # one whole forward pass through the C ABI: the product call (statistics, scans and
-        # readout, three launches on the current stream)
-        plan.forward(q, k, v, tk, tv, out)
+        # readout, three launches on the current stream), with or without the gated epilogue
+        if gate is None:
+            plan.forward(q, k, v, tk, tv, out)
+        else:
+            plan.forward_gated(q, k, v, tk, tv, wg, bg, wo, out)
 
     print(f"[bench] {w.name}: warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -155,8 +177,9 @@ def run(args):
     print(f"[bench] {w.name}: {ms_step:.3f} ms/step; " +
           ", ".join(f"{n} {kern_ms[n]:.3f} ms" for n in names), file=sys.stderr, flush=True)
 
-    alg = algorithmic(w)
-    traffic = read_traffic(w.name)
+    alg = algorithmic(w, args.gated)
+    prof_name = w.name + ("_gated" if args.gated else "")
+    traffic = read_traffic(prof_name)
     kernels = {}
     for n in names:
         ms = kern_ms[n]
@@ -187,7 +210,8 @@ def run(args):
         # arithmetic type of the path: FP8 inputs are converted to bfloat16 on load
         "dtype": "f32" if w.dtype == "f32" else "bf16",
         "data": "synthetic",
-        "config": {"workload": w.name, "input_dtype": w.dtype, "B": w.B, "H": w.H, "F": w.F, "n": w.n, "d": w.d, "dv": w.dv,
+        "config": {"workload": w.name, "input_dtype": w.dtype,
+                   "epilogue": "sigmoid gate and output projection per head" if args.gated else "none", "B": w.B, "H": w.H, "F": w.F, "n": w.n, "d": w.d, "dv": w.dv,
                    "T": w.T, "lambda": w.lam, "video_tokens_per_step": w.video_tokens,
                    "alg_bytes_per_step": w.algorithmic_bytes(),
                    "whole_step_GB/s": round(w.algorithmic_bytes() / (ms_step * 1e-3) / 1e9, 1)},
@@ -198,7 +222,8 @@ def run(args):
     del dev, out
     if not args.no_cpu_baseline:
         print(f"[bench] {w.name}: timing the oracle on host cores", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(w, arrays, budget_s=args.cpu_budget)
+        result["cpu_baseline"] = cpu_baseline(w, arrays, budget_s=args.cpu_budget,
+                                              gate=W.gate_weights_float64(w, gate) if gate else None)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
@@ -255,6 +280,7 @@ def summarize_pmc(args):
     import workloads as W
     fetch_csv, write_csv, cfetch_csv, cwrite_csv = args.summarize_pmc
     w = W.by_name(args.workload)
+    prof_name = w.name + ("_gated" if args.gated else "")
     fetch = _pmc_per_kernel(fetch_csv, "FETCH_SIZE")
     write = _pmc_per_kernel(write_csv, "WRITE_SIZE")
     cf = _pmc_per_kernel(cfetch_csv, "FETCH_SIZE")
@@ -262,13 +288,15 @@ def summarize_pmc(args):
     copy_name = max(cf, key=cf.get)
     f_scale = COPY_PROBE_BYTES / (cf[copy_name] * 1024.0)
     w_scale = COPY_PROBE_BYTES / (cw[copy_name] * 1024.0)
-    alg = algorithmic(w)
-    print(f"# HBM traffic per launch, {w.name}, from rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE")
+    alg = algorithmic(w, args.gated)
+    print(f"# HBM traffic per launch, {prof_name}, from rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE")
     print(f"# command: {args.command}")
     print(f"# calibration: copy probe '{short_name(copy_name)[:50]}' over {COPY_PROBE_BYTES} B read + "
           f"{COPY_PROBE_BYTES} B written reads FETCH_SIZE {cf[copy_name]:.0f} KiB, WRITE_SIZE "
           f"{cw[copy_name]:.0f} KiB -> scale fetch x{f_scale:.4f}, write x{w_scale:.4f}")
     for kern, sym in KERNEL_SYMBOLS.items():
+        if kern == "readout" and args.gated:
+            sym = GATED_READOUT_SYMBOL
         names = [n for n in fetch if sym in n]
         if not names:
             continue
@@ -287,6 +315,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="768p_bf16")
+    ap.add_argument("--gated", action="store_true",
+                    help="run the pass with the gated fusion epilogue (seeded synthetic weights)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-probe", action="store_true")

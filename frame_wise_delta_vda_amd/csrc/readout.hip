@@ -170,6 +170,221 @@ readout_bf16_kernel(const In* __restrict__ q, const uint16_t* __restrict__ xf,
   }
 }
 
+// Gated readout: the readout followed by the linear branch's gated fusion epilogue
+// (aiezz page, section 03, and laicaila page, "technical principles": bullet "gated
+// fusion" -- each branch gets a content-dependent sigmoid gate and its own output
+// projection before the branches merge).  Per head h, with W_g, W_o (dv x dv, [output
+// feature][input feature]) and b_g:
+//   Y_f = sigmoid(O_f W_g^T + b_g) * (O_f W_o^T),   O_f = Q_f W_f
+// Both products fold into the frame's state: O_f W_o^T = Q_f (W_f W_o^T), so per token the
+// epilogue is two readout products instead of one and O never leaves the registers.
+//  - Per frame the workgroup builds W_f^T = (X_fwd + X_bwd)^T / 2 in LDS (bf16, value
+//    feature rows), then every wave folds its share: W'_g = W_f W_g^T and W'_o = W_f W_o^T
+//    for its half of the output features, on the 16x16x32 MFMA with W_f as the A operand
+//    (transposing LDS reads) and the weight rows as B (16-byte loads).  The fold's A rows
+//    are taken in the order that leaves each lane's accumulators holding exactly the
+//    readout's operand fragments of W'^T (4 input features from each of two row tiles), so
+//    no lane exchange is needed.
+//  - Waves split 2 x 2: wave w takes tokens 16 (w % 2)..+15 of each 32-token tile and output
+//    features (DV / 2)(w / 2)..+DV/2-1, so the two folded matrices fit in the registers the
+//    plain readout uses for W.  Q is loaded as in the plain readout (the two waves of a
+//    token half read the same rows; the second read hits the caches).
+//  - Y goes through a wave-private LDS patch; a store instruction writes whole half rows.
+template <int D, int DV>
+struct ReadGated {
+  static constexpr int TT = 32;                 // tokens per tile (16 per token half)
+  static constexpr int KS = D / 32;             // readout k-steps (input features)
+  static constexpr int FH = DV / 2;             // output features per wave
+  static constexpr int NBW = FH / 16;           // 16-feature output blocks per wave
+  static constexpr int KC = DV / 32;            // fold k-steps (value features)
+  static constexpr int NT = D / 16;             // 16-row tiles of W' (input features)
+  static constexpr int NFR = (DV / 16) * KS;    // state fragments per frame
+  static constexpr int WTROW = D + 8;           // bf16 per LDS row of W_f^T
+  static constexpr int WT_BYTES = DV * WTROW * 2;
+  static constexpr int OWROW = FH + 8;          // bf16 per LDS row of a wave's Y patch
+  static constexpr int OCH = FH / 8;            // 16-byte chunks per half row
+  static constexpr int ORPI = 64 / OCH < 16 ? 64 / OCH : 16;  // rows per store instruction
+  static constexpr int OST = 16 / ORPI;         // store instructions per wave per tile
+  static constexpr int OW_BYTES = 16 * OWROW * 2;
+  static constexpr int LDS_BYTES = WT_BYTES + 4 * OW_BYTES;
+  static_assert(NBW >= 1 && KC >= 1, "value width must be at least 32");
+};
+
+template <int D, int DV, typename In>
+__global__ void __launch_bounds__(kThreads, 2)
+readout_gated_kernel(const In* __restrict__ q, const uint16_t* __restrict__ xf,
+                     const uint16_t* __restrict__ xb, const uint16_t* __restrict__ w_gate,
+                     const float* __restrict__ b_gate, const uint16_t* __restrict__ w_out,
+                     uint16_t* __restrict__ out, int64_t n, int64_t F, int64_t H,
+                     int64_t tiles_per_frame, int64_t splits, int64_t tiles_per_split,
+                     int64_t head_blocks, int64_t tail_splits, int64_t tail_tiles_per_split) {
+  using C = ReadGated<D, DV>;
+  constexpr int EB = int(sizeof(In));
+  constexpr bool PAIR = EB == 1 && C::KS >= 2;
+  constexpr int NQL = PAIR ? C::KS / 2 : C::KS;
+  using QRaw = typename std::conditional<EB == 1 && !PAIR, uint2, uint4>::type;
+  extern __shared__ __align__(16) unsigned char smem[];
+  uint16_t* wt = reinterpret_cast<uint16_t*>(smem);  // W_f^T [DV][WTROW]
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int th = wave & 1, fh = wave >> 1;
+  uint16_t* ow = reinterpret_cast<uint16_t*>(smem + C::WT_BYTES + wave * C::OW_BYTES);
+  const int c16 = lane & 15, g4 = lane >> 4;
+  int64_t frame, t_first, tps;
+  if (blockIdx.x < head_blocks) {
+    frame = blockIdx.x / splits;
+    t_first = (blockIdx.x % splits) * tiles_per_split;
+    tps = tiles_per_split;
+  } else {
+    const int64_t i = blockIdx.x - head_blocks;
+    frame = head_blocks / splits + i / tail_splits;
+    t_first = (i % tail_splits) * tail_tiles_per_split;
+    tps = tail_tiles_per_split;
+  }
+  const int64_t t_last = (t_first + tps < tiles_per_frame) ? t_first + tps : tiles_per_frame;
+  if (t_first >= t_last) return;
+  const int64_t head = (frame / F) % H;
+
+  // input feature held at slot m of k-step ks by lane group g, for the Q operand and the
+  // states alike (FP8 plans at d >= 64 pair k-steps; see the plain readout)
+  auto qmap = [&](int ks, int g, int m) -> int {
+    return PAIR ? 16 * (g + 4 * (ks >> 1)) + 8 * (ks & 1) + m : 32 * ks + 8 * g + m;
+  };
+
+  // ---- W_f^T = (X_fwd + X_bwd)^T / 2 into LDS: fragment (nb, ks) of the stored states
+  // holds rows 16 nb + lane % 16 of W^T and input features qmap(ks, lane / 16, 0..7)
+  {
+    const uint4* sf = reinterpret_cast<const uint4*>(xf + frame * int64_t(D) * DV) + lane;
+    const uint4* sb = reinterpret_cast<const uint4*>(xb + frame * int64_t(D) * DV) + lane;
+    for (int fr = wave; fr < C::NFR; fr += 4) {
+      const int nb = fr / C::KS, ks = fr % C::KS;
+      const uint4 m = mean_bf16x8(sf[fr * 64], sb[fr * 64]);
+      *reinterpret_cast<uint4*>(wt + (16 * nb + c16) * C::WTROW + qmap(ks, g4, 0)) = m;
+    }
+  }
+  __syncthreads();
+
+  // ---- fold: wfr[0] = (W_f W_g^T)^T, wfr[1] = (W_f W_o^T)^T fragments of this wave's
+  // output blocks.  Row slot 16t + s of the fold's A operand is input feature
+  // qmap(t / 2, s / 4, 4 (t % 2) + s % 4), so lane (j, g) of accumulator tile t holds the
+  // features of slots 4 (t % 2) .. +3 of k-step t / 2 for lane group g: half a fragment.
+  uint4 wfr[2][C::NBW][C::KS];
+  {
+    // A operand from W_f^T by two transposing reads (ds_read_b64_tr_b16): lane L of a
+    // 16-lane group points at value feature (row) 32 kc + 8 g + L / 4 (+4) and input
+    // features qmap(t / 2, L % 4, 4 (t % 2)) .. +3, and receives 8 consecutive value
+    // features of input feature i(lane % 16).
+    auto fold_a = [&](int t, int kc) -> uint4 {
+      typedef short v4s __attribute__((ext_vector_type(4)));
+      typedef __attribute__((address_space(3))) v4s* lds_v4s;
+      const uint16_t* p = wt + (32 * kc + 8 * g4 + (c16 >> 2)) * C::WTROW + qmap(t >> 1, c16 & 3, 4 * (t & 1));
+      const v4s x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(p));
+      const v4s y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(p + 4 * C::WTROW));
+      const uint2 xl = __builtin_bit_cast(uint2, x), yl = __builtin_bit_cast(uint2, y);
+      return make_uint4(xl.x, xl.y, yl.x, yl.y);
+    };
+#pragma unroll
+    for (int mtx = 0; mtx < 2; ++mtx) {
+      const uint16_t* wl = (mtx == 0 ? w_gate : w_out) + head * DV * DV;
+#pragma unroll
+      for (int jb = 0; jb < C::NBW; ++jb) {
+        const int j = 16 * (fh * C::NBW + jb) + c16;  // output feature of this lane
+        uint4 bw[C::KC];
+#pragma unroll
+        for (int kc = 0; kc < C::KC; ++kc)
+          bw[kc] = *reinterpret_cast<const uint4*>(wl + j * DV + 32 * kc + 8 * g4);
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) {
+          uint32_t wd[4];
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) {
+            f32x4 acc = f32x4{};
+#pragma unroll
+            for (int kc = 0; kc < C::KC; ++kc) acc = mfma16_bf16(fold_a(2 * ks + h2, kc), bw[kc], acc);
+            wd[2 * h2] = pack_bf16x2(acc[0], acc[1]);
+            wd[2 * h2 + 1] = pack_bf16x2(acc[2], acc[3]);
+          }
+          wfr[mtx][jb][ks] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+        }
+        // compiler fence: re-read the A operands for the next block instead of keeping all
+        // of them live across the fold (which would not fit beside wfr)
+        asm volatile("" ::: "memory");
+      }
+    }
+  }
+  float bias[C::NBW][4];
+#pragma unroll
+  for (int jb = 0; jb < C::NBW; ++jb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) bias[jb][r] = b_gate[head * DV + 16 * (fh * C::NBW + jb) + 4 * g4 + r];
+
+  auto wave_rows = [&](int64_t tok0) -> uint32_t {
+    const int64_t r = n - tok0;
+    return uint32_t(r < 0 ? 0 : (r < 16 ? r : 16));
+  };
+  auto load_q = [&](int64_t tile, QRaw (&dst)[NQL]) {
+    const int64_t tok0 = tile * C::TT + 16 * th;
+    const auto rs = make_rsrc(q + (frame * n + tok0) * D, wave_rows(tok0) * D * EB);
+#pragma unroll
+    for (int i = 0; i < NQL; ++i) {
+      if constexpr (PAIR) dst[i] = buffer_load16(rs, uint32_t(c16 * D + 16 * (g4 + 4 * i)));
+      else if constexpr (EB == 1) dst[i] = buffer_load8(rs, uint32_t(c16 * D + 32 * i + 8 * g4));
+      else dst[i] = buffer_load16(rs, uint32_t((c16 * D + 32 * i + 8 * g4) * 2));
+    }
+  };
+  QRaw pfa[NQL], pfb[NQL];
+  load_q(t_first, pfa);
+  load_q(t_first + 1 < t_last ? t_first + 1 : t_first, pfb);
+
+  auto step = [&](int64_t tile, QRaw (&pf)[NQL]) {
+    const int64_t tok0 = tile * C::TT + 16 * th;
+    uint4 qf[C::KS];
+#pragma unroll
+    for (int i = 0; i < NQL; ++i) {
+      if constexpr (PAIR) {
+        qf[2 * i] = e4m3x8_to_bf16x8(make_uint2(pf[i].x, pf[i].y));
+        qf[2 * i + 1] = e4m3x8_to_bf16x8(make_uint2(pf[i].z, pf[i].w));
+      } else if constexpr (EB == 1) {
+        qf[i] = e4m3x8_to_bf16x8(pf[i]);
+      } else {
+        qf[i] = pf[i];
+      }
+    }
+    load_q(tile + 2 < t_last ? tile + 2 : t_last - 1, pf);
+    // Y^T block jb: the lane holds token c16, output features 16 (fh NBW + jb) + 4 g4 + 0..3
+#pragma unroll
+    for (int jb = 0; jb < C::NBW; ++jb) {
+      f32x4 ga = f32x4{}, pa = f32x4{};
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        ga = mfma16_bf16(wfr[0][jb][ks], qf[ks], ga);
+        pa = mfma16_bf16(wfr[1][jb][ks], qf[ks], pa);
+      }
+      float y[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        y[r] = pa[r] * __builtin_amdgcn_rcpf(1.0f + __expf(-(ga[r] + bias[jb][r])));
+      *reinterpret_cast<uint2*>(ow + c16 * C::OWROW + 16 * jb + 4 * g4) =
+          make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
+    }
+    const auto rs = make_rsrc(out + (frame * n + tok0) * DV, wave_rows(tok0) * DV * 2);
+    const int orow = lane / C::OCH, och = lane % C::OCH;
+    if (orow < C::ORPI) {
+#pragma unroll
+      for (int j = 0; j < C::OST; ++j) {
+        const int r = orow + j * C::ORPI;
+        buffer_store16<kCacheStreamOut>(rs, uint32_t(r * DV * 2 + fh * C::FH * 2 + och * 16),
+                                        *reinterpret_cast<const uint4*>(ow + r * C::OWROW + och * 8));
+      }
+    }
+  };
+
+  for (int64_t tile = t_first; tile < t_last; tile += 2) {
+    step(tile, pfa);
+    if (tile + 1 < t_last) step(tile + 1, pfb);
+  }
+}
+
 template <int D, int DV>
 struct ReadF32 {
   static constexpr int WROW = DV + 4;
@@ -229,43 +444,54 @@ readout_f32_kernel(const float* __restrict__ q, const float* __restrict__ xf,
   }
 }
 
+// Grid of the bfloat16 readouts: one workgroup per frame; frames are split in equal
+// parts only while there are fewer than four workgroups per compute unit and each part
+// keeps 8+ tiles.  Whole frames leave a last, partial round of R frames on S resident
+// workgroups (two per CU); those R frames go in k equal parts so that round is about as
+// wide as the others.
+struct ReadGrid {
+  int64_t tpf, splits, tps, head_blocks, tail_splits, tail_tps, grid;
+};
+ReadGrid readout_grid(int64_t frames, int64_t tpf, int num_cus) {
+  ReadGrid g;
+  g.tpf = tpf;
+  int64_t splits = 1;
+  while (frames * splits < 4 * int64_t(num_cus) && tpf >= 16 * splits) splits *= 2;
+  g.tps = (tpf + splits - 1) / splits;
+  g.splits = (tpf + g.tps - 1) / g.tps;
+  int64_t head_frames = frames;
+  g.tail_splits = 1;
+  g.tail_tps = tpf;
+  const int64_t slots = 2 * int64_t(num_cus);
+  const int64_t rem = frames % slots;
+  if (g.splits == 1 && frames > slots && rem > 0) {
+    int64_t k = slots / rem;
+    if (k > 4) k = 4;
+    if (tpf < 4 * k) k = tpf / 4;
+    if (k >= 2) {
+      g.tail_tps = (tpf + k - 1) / k;
+      g.tail_splits = (tpf + g.tail_tps - 1) / g.tail_tps;
+      head_frames = frames - rem;
+    }
+  }
+  g.head_blocks = head_frames * g.splits;
+  g.grid = g.head_blocks + (frames - head_frames) * g.tail_splits;
+  return g;
+}
+
 template <int D, int DV>
 hipError_t launch_readout_t(const Problem& p, const void* q, void* out, hipStream_t s, bool prepare) {
   const int64_t frames = p.B * p.H * p.F;
   if (p.bf16) {
     if (prepare) return hipSuccess;  // 17 KB of LDS: no attribute to set
     using C = ReadBf16<D, DV>;
-    const int64_t tpf = (p.n + C::TT - 1) / C::TT;
-    // one workgroup per frame; frames are split in equal parts only while there are
-    // fewer than four workgroups per compute unit and each part keeps 8+ tiles
-    int64_t splits = 1;
-    while (frames * splits < 4 * int64_t(p.num_cus) && tpf >= 16 * splits) splits *= 2;
-    const int64_t tps = (tpf + splits - 1) / splits;
-    splits = (tpf + tps - 1) / tps;
-    // Whole frames leave a last, partial round of R frames on S resident workgroups (two
-    // per CU); those R frames go in k equal parts so that round is about as wide as the
-    // others.
-    int64_t head_frames = frames, tail_splits = 1, tail_tps = tpf;
-    const int64_t slots = 2 * int64_t(p.num_cus);
-    const int64_t rem = frames % slots;
-    if (splits == 1 && frames > slots && rem > 0) {
-      int64_t k = slots / rem;
-      if (k > 4) k = 4;
-      if (tpf < 4 * k) k = tpf / 4;
-      if (k >= 2) {
-        tail_tps = (tpf + k - 1) / k;
-        tail_splits = (tpf + tail_tps - 1) / tail_tps;
-        head_frames = frames - rem;
-      }
-    }
-    const int64_t head_blocks = head_frames * splits;
-    const int64_t grid = head_blocks + (frames - head_frames) * tail_splits;
+    const ReadGrid gr = readout_grid(frames, (p.n + C::TT - 1) / C::TT, p.num_cus);
     auto launch = [&](auto kern, auto in) {
       using In = decltype(in);
-      hipLaunchKernelGGL(kern, dim3(unsigned(grid)), dim3(kThreads), C::LDS_BYTES, s,
+      hipLaunchKernelGGL(kern, dim3(unsigned(gr.grid)), dim3(kThreads), C::LDS_BYTES, s,
                          static_cast<const In*>(q), reinterpret_cast<const uint16_t*>(p.xf),
                          reinterpret_cast<const uint16_t*>(p.xb), static_cast<uint16_t*>(out),
-                         p.n, tpf, splits, tps, head_blocks, tail_splits, tail_tps);
+                         p.n, gr.tpf, gr.splits, gr.tps, gr.head_blocks, gr.tail_splits, gr.tail_tps);
     };
     if (p.fp8) launch(readout_bf16_kernel<D, DV, uint8_t>, uint8_t{});
     else launch(readout_bf16_kernel<D, DV, uint16_t>, uint16_t{});
@@ -289,6 +515,27 @@ hipError_t launch_readout_t(const Problem& p, const void* q, void* out, hipStrea
   return hipGetLastError();
 }
 
+
+template <int D, int DV>
+hipError_t launch_readout_gated_t(const Problem& p, const void* q, const GateWeights& gw, void* out,
+                                  hipStream_t s, bool prepare) {
+  if (!p.bf16) return hipErrorInvalidValue;
+  using C = ReadGated<D, DV>;
+  if (prepare) return hipSuccess;  // under 64 KB of LDS: no attribute to set
+  const ReadGrid gr = readout_grid(p.B * p.H * p.F, (p.n + C::TT - 1) / C::TT, p.num_cus);
+  auto launch = [&](auto kern, auto in) {
+    using In = decltype(in);
+    hipLaunchKernelGGL(kern, dim3(unsigned(gr.grid)), dim3(kThreads), C::LDS_BYTES, s,
+                       static_cast<const In*>(q), reinterpret_cast<const uint16_t*>(p.xf),
+                       reinterpret_cast<const uint16_t*>(p.xb),
+                       static_cast<const uint16_t*>(gw.w_gate), static_cast<const float*>(gw.b_gate),
+                       static_cast<const uint16_t*>(gw.w_out), static_cast<uint16_t*>(out), p.n, p.F,
+                       p.H, gr.tpf, gr.splits, gr.tps, gr.head_blocks, gr.tail_splits, gr.tail_tps);
+  };
+  if (p.fp8) launch(readout_gated_kernel<D, DV, uint8_t>, uint8_t{});
+  else launch(readout_gated_kernel<D, DV, uint16_t>, uint16_t{});
+  return hipGetLastError();
+}
 }  // namespace
 
 hipError_t launch_readout(const Problem& p, const void* q, void* out, hipStream_t s) {
@@ -304,6 +551,21 @@ hipError_t launch_readout(const Problem& p, const void* q, void* out, hipStream_
 hipError_t prepare_readout(const Problem& p) {
 #define VDA_CASE(DD, VV) \
   if (p.d == DD && p.dv == VV) return launch_readout_t<DD, VV>(p, nullptr, nullptr, nullptr, true);
+  VDA_CASE(32, 32) VDA_CASE(32, 64) VDA_CASE(32, 128)
+  VDA_CASE(64, 32) VDA_CASE(64, 64) VDA_CASE(64, 128)
+  VDA_CASE(128, 32) VDA_CASE(128, 64) VDA_CASE(128, 128)
+#undef VDA_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace vda
+
+namespace vda {
+
+hipError_t launch_readout_gated(const Problem& p, const void* q, const GateWeights& gw, void* out,
+                                hipStream_t s) {
+#define VDA_CASE(DD, VV) \
+  if (p.d == DD && p.dv == VV) return launch_readout_gated_t<DD, VV>(p, q, gw, out, s, false);
   VDA_CASE(32, 32) VDA_CASE(32, 64) VDA_CASE(32, 128)
   VDA_CASE(64, 32) VDA_CASE(64, 64) VDA_CASE(64, 128)
   VDA_CASE(128, 32) VDA_CASE(128, 64) VDA_CASE(128, 128)

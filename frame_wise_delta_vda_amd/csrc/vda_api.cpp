@@ -182,9 +182,14 @@ vda_status vda_debug_workspace(vda_plan_t plan, const float** ainv, const float*
   return VDA_SUCCESS;
 }
 
-vda_status vda_forward_stages(vda_plan_t plan, unsigned stages, const void* q, const void* k,
-                              const void* v, const void* text_k, const void* text_v, void* out,
-                              void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks and enqueues the selected stages; gate != nullptr runs the gated readout.
+vda_status enqueue(vda_plan_t plan, unsigned stages, const void* q, const void* k, const void* v,
+                   const void* text_k, const void* text_v, const vda::GateWeights* gate, void* out,
+                   void* stream) {
   if (plan == nullptr) return VDA_ERROR_INVALID_VALUE;
   if (stages == 0 || (stages & ~unsigned(VDA_STAGE_ALL)) != 0) return VDA_ERROR_INVALID_VALUE;
   const vda::Problem& p = plan->p;
@@ -208,9 +213,13 @@ vda_status vda_forward_stages(vda_plan_t plan, unsigned stages, const void* q, c
     const void* ptr;
     size_t bytes;
     bool used;
-  } args[6] = {{q, qk_bytes, do_read},         {k, qk_bytes, do_stats},
+  } args[9] = {{q, qk_bytes, do_read},         {k, qk_bytes, do_stats},
                {v, v_bytes, do_stats},         {text_k, tk_bytes, do_stats},
-               {text_v, tv_bytes, do_stats},   {out, o_bytes, do_read}};
+               {text_v, tv_bytes, do_stats},
+               {gate ? gate->w_gate : nullptr, size_t(p.H) * size_t(p.dv) * size_t(p.dv) * 2, gate != nullptr},
+               {gate ? gate->b_gate : nullptr, size_t(p.H) * size_t(p.dv) * 4, gate != nullptr},
+               {gate ? gate->w_out : nullptr, size_t(p.H) * size_t(p.dv) * size_t(p.dv) * 2, gate != nullptr},
+               {out, o_bytes, do_read}};
   for (const Arg& a : args) {
     if (!a.used || a.bytes == 0) continue;
     if (a.ptr == nullptr) return VDA_ERROR_INVALID_VALUE;
@@ -218,7 +227,7 @@ vda_status vda_forward_stages(vda_plan_t plan, unsigned stages, const void* q, c
   }
   if (do_read && o_bytes > 0) {
     Range o{reinterpret_cast<uintptr_t>(out), reinterpret_cast<uintptr_t>(out) + o_bytes};
-    for (int i = 0; i < 5; ++i) {
+    for (int i = 0; i < 8; ++i) {
       if (args[i].ptr == nullptr || args[i].bytes == 0) continue;
       Range r{reinterpret_cast<uintptr_t>(args[i].ptr),
               reinterpret_cast<uintptr_t>(args[i].ptr) + args[i].bytes};
@@ -248,7 +257,8 @@ vda_status vda_forward_stages(vda_plan_t plan, unsigned stages, const void* q, c
   if (e == hipSuccess && do_scan) e = vda::launch_scan(p, s);
   mark(kEvScanEnd);
   mark(kEvReadBegin);
-  if (e == hipSuccess && do_read) e = vda::launch_readout(p, q, out, s);
+  if (e == hipSuccess && do_read)
+    e = gate ? vda::launch_readout_gated(p, q, *gate, out, s) : vda::launch_readout(p, q, out, s);
   mark(kEvReadEnd);
   if (tev != nullptr && e == hipSuccess) ++plan->timed_calls;
   if (e != hipSuccess) {
@@ -256,6 +266,25 @@ vda_status vda_forward_stages(vda_plan_t plan, unsigned stages, const void* q, c
     return VDA_ERROR_DEVICE;
   }
   return VDA_SUCCESS;
+}
+
+}  // namespace
+
+extern "C" {
+
+vda_status vda_forward_stages(vda_plan_t plan, unsigned stages, const void* q, const void* k,
+                              const void* v, const void* text_k, const void* text_v, void* out,
+                              void* stream) {
+  return enqueue(plan, stages, q, k, v, text_k, text_v, nullptr, out, stream);
+}
+
+vda_status vda_forward_gated(vda_plan_t plan, const void* q, const void* k, const void* v,
+                             const void* text_k, const void* text_v, const void* w_gate,
+                             const void* b_gate, const void* w_out, void* out, void* stream) {
+  if (plan == nullptr) return VDA_ERROR_INVALID_VALUE;
+  if (!plan->p.bf16) return VDA_ERROR_NOT_SUPPORTED;
+  const vda::GateWeights gw{w_gate, b_gate, w_out};
+  return enqueue(plan, VDA_STAGE_ALL, q, k, v, text_k, text_v, &gw, out, stream);
 }
 
 vda_status vda_plan_enable_timing(vda_plan_t plan, int capacity) {

@@ -30,6 +30,15 @@ hipError_t launch_stats(const Problem& p, const void* k, const void* v, const vo
                         const void* tv, hipStream_t stream);
 hipError_t launch_scan(const Problem& p, hipStream_t stream);
 hipError_t launch_readout(const Problem& p, const void* q, void* out, hipStream_t stream);
+// Weights of the gated fusion epilogue (bfloat16 [H][dv][dv] matrices, float32 [H][dv] bias).
+struct GateWeights {
+  const void* w_gate;
+  const void* b_gate;
+  const void* w_out;
+};
+// The readout followed by the gated epilogue (bfloat16 and FP8 plans).
+hipError_t launch_readout_gated(const Problem& p, const void* q, const GateWeights& gw, void* out,
+                                hipStream_t stream);
 // Per-function attributes (dynamic LDS above 64 KB) of the kernels a plan launches, set
 // once at plan creation on the plan's device, so that launches make no other runtime
 // call (they can then be captured in a graph).

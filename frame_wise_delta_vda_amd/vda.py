@@ -52,6 +52,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.vda_plan_create.restype = c_int
     lib.vda_forward.argtypes = [c_vp] * 8
     lib.vda_forward.restype = c_int
+    lib.vda_forward_gated.argtypes = [c_vp] * 11
+    lib.vda_forward_gated.restype = c_int
     lib.vda_forward_stages.argtypes = [c_vp, ctypes.c_uint] + [c_vp] * 7
     lib.vda_forward_stages.restype = c_int
     lib.vda_plan_destroy.argtypes = [c_vp]
@@ -119,6 +121,12 @@ def vda_plan_create(B, H, F, n, d, dv, T, lam, dtype) -> int:
 def vda_forward(plan, q, k, v, text_k, text_v, out, stream=None):
     _check(load_library().vda_forward(plan, _ptr(q), _ptr(k), _ptr(v), _ptr(text_k), _ptr(text_v),
                                       _ptr(out), _stream(stream)), "vda_forward")
+
+
+def vda_forward_gated(plan, q, k, v, text_k, text_v, w_gate, b_gate, w_out, out, stream=None):
+    _check(load_library().vda_forward_gated(plan, _ptr(q), _ptr(k), _ptr(v), _ptr(text_k), _ptr(text_v),
+                                            _ptr(w_gate), _ptr(b_gate), _ptr(w_out), _ptr(out),
+                                            _stream(stream)), "vda_forward_gated")
 
 
 def vda_forward_stages(plan, stages, q, k, v, text_k, text_v, out, stream=None):
@@ -197,6 +205,13 @@ class Plan:
         if out is None:
             out = self.out_like(q)
         vda_forward(self.handle, q, k, v, text_k, text_v, out, stream)
+        return out
+
+    def forward_gated(self, q, k, v, text_k, text_v, w_gate, b_gate, w_out, out=None, stream=None):
+        """The forward pass followed by the gated epilogue (include/vda.h, vda_forward_gated)."""
+        if out is None:
+            out = self.out_like(q)
+        vda_forward_gated(self.handle, q, k, v, text_k, text_v, w_gate, b_gate, w_out, out, stream)
         return out
 
     def stages(self, stages, q=None, k=None, v=None, text_k=None, text_v=None, out=None, stream=None):

@@ -115,6 +115,25 @@ vda_status vda_forward_stages(vda_plan_t plan, unsigned stages, const void* q, c
                               const void* v, const void* text_k, const void* text_v, void* out,
                               void* stream);
 
+/* The forward pass followed by the linear branch's gated fusion epilogue, per head h
+ * and output row O (1 x dv) of the pass:
+ *   Y = sigmoid(O W_g^T + b_g) * (O W_o^T)          (elementwise product)
+ * The pages give each attention branch a content-dependent sigmoid gate and an output
+ * projection of its own before the branches merge (the aiezz page, section 03, and the
+ * laicaila page, section "technical principles": bullet "gated fusion"); this is that
+ * step for the linear branch, with the branch output as the gate's content and a
+ * per-head dv x dv projection.  Merging with the other branch is not part of it.
+ *   w_gate, w_out  [H][dv][dv] bfloat16, [output feature][input feature] (the layout of a
+ *                  torch Linear weight), shared by every batch entry;
+ *   b_gate         [H][dv] float32;
+ *   out            [B][H][F][n][dv] bfloat16: Y in place of the plain output.
+ * Other arguments, pointer rules, stream and capture behaviour as for vda_forward; the
+ * weights may not overlap out.  Timing, when enabled, records these passes too.
+ * Errors: as vda_forward, and NOT_SUPPORTED for float32 plans. */
+vda_status vda_forward_gated(vda_plan_t plan, const void* q, const void* k, const void* v,
+                             const void* text_k, const void* text_v, const void* w_gate,
+                             const void* b_gate, const void* w_out, void* out, void* stream);
+
 /* Per-stage timing of whole forward passes, for benchmarks.  After
  * vda_plan_enable_timing(plan, capacity) with capacity > 0, each of the next `capacity`
  * vda_forward calls brackets each stage's launch with HIP events on the stream it runs

@@ -28,7 +28,9 @@ introduction, bullet "hybrid architecture"):
 * Each frame reads the state out with its queries.  Reading: inclusive states
   (after frame f's own update) and the mean of the two directions,
   O_f = Q_f (X_fwd_f + X_bwd_f) / 2.
-* No feature map, no 1/sqrt(d) scaling, no decay and no gate inside the op.
+* No feature map, no 1/sqrt(d) scaling, no decay and no gate inside the op.  The
+  branch's gated fusion epilogue, applied to the op's output, is at the end of this
+  module.
 
 Every function works on float64 arrays and uses library linear algebra
 (``numpy.linalg.solve``) for the solves, with no blocking or reordering beyond
@@ -41,6 +43,7 @@ import numpy as np
 __all__ = [
     "frame_statistics", "normal_equation_update", "text_state", "scan_from",
     "head_states", "readout", "vda_forward_head", "vda_forward",
+    "gated_output", "vda_forward_gated_head", "vda_forward_gated",
 ]
 
 
@@ -119,4 +122,45 @@ def vda_forward(q, k, v, text_k, text_v, lam):
     for b in range(Bsz):
         for h in range(H):
             out[b, h] = vda_forward_head(q[b, h], k[b, h], v[b, h], text_k[b, h], text_v[b, h], lam)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Gated fusion epilogue of the linear branch
+# ---------------------------------------------------------------------------
+# The pages (aiezz page, section 03, bullet "gated fusion"; laicaila page, section
+# "technical principles", the same bullet) say the two attention branches have
+# different output scales, so each branch gets a content-dependent sigmoid gate and
+# an output projection of its own before the branches are merged.  For the linear
+# branch alone this reads, per head and per token, with the branch output O (1 x dv)
+# as the content the gate depends on:
+#     Y = sigmoid(O W_g^T + b_g) * (O W_o^T)            (elementwise product)
+# with W_g, W_o (dv x dv) stored as [output feature][input feature] and b_g (dv).
+# Merging with the softmax branch is not part of this op.
+
+def gated_output(O_rows, w_gate, b_gate, w_out):
+    """Y = sigmoid(O W_g^T + b_g) * (O W_o^T) for rows O [..., dv]; w_gate, w_out [dv, dv]
+    ([output][input]), b_gate [dv]."""
+    O_rows = np.asarray(O_rows, dtype=np.float64)
+    w_gate = np.asarray(w_gate, dtype=np.float64)
+    w_out = np.asarray(w_out, dtype=np.float64)
+    b_gate = np.asarray(b_gate, dtype=np.float64)
+    g = O_rows @ w_gate.T + b_gate
+    with np.errstate(over="ignore"):
+        gate = 1.0 / (1.0 + np.exp(-g))
+    return gate * (O_rows @ w_out.T)
+
+
+def vda_forward_gated_head(q, k, v, text_k, text_v, lam, w_gate, b_gate, w_out):
+    """The VDA output of one (batch, head) followed by the gated epilogue with that head's
+    weights: w_gate, w_out [dv, dv], b_gate [dv]."""
+    return gated_output(vda_forward_head(q, k, v, text_k, text_v, lam), w_gate, b_gate, w_out)
+
+
+def vda_forward_gated(q, k, v, text_k, text_v, lam, w_gate, b_gate, w_out):
+    """Gated VDA forward over [B,H,...] arrays with per-head weights w_gate, w_out [H, dv, dv]
+    and b_gate [H, dv], shared by every batch entry."""
+    out = vda_forward(q, k, v, text_k, text_v, lam)
+    for h in range(out.shape[1]):
+        out[:, h] = gated_output(out[:, h], w_gate[h], b_gate[h], w_out[h])
     return out

@@ -124,8 +124,46 @@ def pin_fixed_point(seed=3, lam=0.3, F=4, n=6, d=3, dv=2):
     return bool(np.allclose(xs, np.broadcast_to(M.T, xs.shape), rtol=1e-11, atol=1e-12))
 
 
+LN3, LN7 = np.log(3.0), np.log(7.0)
+
+
+def pin_gate_worked_examples():
+    """Gated epilogue, worked by hand with gate arguments whose sigmoid is rational
+    (sigmoid(0) = 1/2, sigmoid(ln 3) = 3/4, sigmoid(-ln 3) = 1/4, sigmoid(ln 7) = 7/8).
+    Weights are [output feature][input feature]."""
+    ok = True
+    # 1. zero gate weights, bias (ln 3, -ln 3): gates 3/4 and 1/4 on output features 0 and 1;
+    #    W_o = [[0, 1], [2, 0]] maps (o0, o1) to (o1, 2 o0): tokens (1, 2) -> (2, 2), (3, -1) -> (-1, 6)
+    y = oracle.gated_output(np.array([[1.0, 2.0], [3.0, -1.0]]), np.zeros((2, 2)),
+                            np.array([LN3, -LN3]), np.array([[0.0, 1.0], [2.0, 0.0]]))
+    ok &= np.allclose(y, [[1.5, 0.5], [-0.75, 1.5]], rtol=1e-14, atol=0)
+    # 2. W_g = [[0, ln 3], [0, 0]]: gate argument of output 0 is o1 ln 3; bias (0, ln 7); W_o = I.
+    #    token (1, 1): gates (3/4, 7/8) -> (0.75, 0.875); token (2, 1): gates (3/4, 7/8) -> (1.5, 0.875);
+    #    token (1, 0): gates (1/2, 7/8) -> (0.5, 0)
+    y = oracle.gated_output(np.array([[1.0, 1.0], [2.0, 1.0], [1.0, 0.0]]), np.array([[0.0, LN3], [0.0, 0.0]]),
+                            np.array([0.0, LN7]), np.eye(2))
+    ok &= np.allclose(y, [[0.75, 0.875], [1.5, 0.875], [0.5, 0.0]], rtol=1e-14, atol=1e-15)
+    return bool(ok)
+
+
+def pin_gate_limits(seed=11, dv=5):
+    """Gate saturation and the logistic function itself: a bias of +60 passes O W_o^T
+    through, -60 closes the gate; with W_g = 0, b = 0 the output is half the projection;
+    the gate agrees with scipy's expit."""
+    from scipy.special import expit
+    rng = np.random.default_rng(seed)
+    Orow = rng.standard_normal((7, dv))
+    Wg, Wo, b = rng.standard_normal((dv, dv)), rng.standard_normal((dv, dv)), rng.standard_normal(dv)
+    P = Orow @ Wo.T
+    ok = np.allclose(oracle.gated_output(Orow, np.zeros((dv, dv)), np.full(dv, 60.0), Wo), P, rtol=1e-14, atol=0)
+    ok &= np.all(np.abs(oracle.gated_output(Orow, np.zeros((dv, dv)), np.full(dv, -60.0), Wo)) <= 1e-25 * np.abs(P).max())
+    ok &= np.allclose(oracle.gated_output(Orow, np.zeros((dv, dv)), np.zeros(dv), Wo), 0.5 * P, rtol=1e-15, atol=0)
+    ok &= np.allclose(oracle.gated_output(Orow, Wg, b, np.eye(dv)), expit(Orow @ Wg.T + b) * Orow, rtol=1e-13, atol=0)
+    return bool(ok)
+
+
 PINS = [pin_golden, pin_lstsq, lambda: pin_lstsq(seed=4, n=6, d=3, dv=3), pin_delta_rule,
-        pin_fixed_point]
+        pin_fixed_point, pin_gate_worked_examples, pin_gate_limits]
 
 
 # ---------------------------------------------------------------------------
@@ -257,6 +295,30 @@ def test_heads_and_batch_are_independent():
     assert np.array_equal(out2[0], out[0]) and np.array_equal(out2[1, :2], out[1, :2])
 
 
+def test_gate_worked_examples():
+    assert pin_gate_worked_examples()
+
+
+def test_gate_limits_and_logistic():
+    assert pin_gate_limits()
+
+
+def test_gated_forward_applies_each_heads_weights():
+    rng = np.random.default_rng(21)
+    B, H, F, n, d, dv, T = 2, 3, 3, 4, 3, 2, 2
+    q, k, v = rng.standard_normal((B, H, F, n, d)), _rownorm(rng.standard_normal((B, H, F, n, d))), \
+        rng.standard_normal((B, H, F, n, dv))
+    tk, tv = _rownorm(rng.standard_normal((B, H, T, d))), rng.standard_normal((B, H, T, dv))
+    Wg, Wo, bg = rng.standard_normal((H, dv, dv)), rng.standard_normal((H, dv, dv)), rng.standard_normal((H, dv))
+    y = oracle.vda_forward_gated(q, k, v, tk, tv, 0.5, Wg, bg, Wo)
+    for b in range(B):
+        for h in range(H):
+            o = oracle.vda_forward_head(q[b, h], k[b, h], v[b, h], tk[b, h], tv[b, h], 0.5)
+            assert np.array_equal(y[b, h], oracle.gated_output(o, Wg[h], bg[h], Wo[h]))
+            assert np.array_equal(y[b, h], oracle.vda_forward_gated_head(q[b, h], k[b, h], v[b, h], tk[b, h],
+                                                                         tv[b, h], 0.5, Wg[h], bg[h], Wo[h]))
+
+
 def test_rejects_nonpositive_lambda():
     h = _tiny_head(13)
     with pytest.raises(ValueError):
@@ -322,7 +384,32 @@ def _states_exclusive(k, v, text_k, text_v, lam):
     return X_text, fx, bx
 
 
+def _gate_tanh(O_rows, w_gate, b_gate, w_out):
+    return np.tanh(O_rows @ w_gate.T + b_gate) * (O_rows @ w_out.T)
+
+
+def _gate_bias_sign(O_rows, w_gate, b_gate, w_out):
+    return 1.0 / (1.0 + np.exp(-(O_rows @ w_gate.T - b_gate))) * (O_rows @ w_out.T)
+
+
+def _gate_w_out_transposed(O_rows, w_gate, b_gate, w_out):
+    return 1.0 / (1.0 + np.exp(-(O_rows @ w_gate.T + b_gate))) * (O_rows @ w_out)
+
+
+def _gate_w_gate_transposed(O_rows, w_gate, b_gate, w_out):
+    return 1.0 / (1.0 + np.exp(-(O_rows @ w_gate + b_gate))) * (O_rows @ w_out.T)
+
+
+def _gate_additive(O_rows, w_gate, b_gate, w_out):
+    return 1.0 / (1.0 + np.exp(-(O_rows @ w_gate.T + b_gate))) + (O_rows @ w_out.T)
+
+
 MUTANTS = {
+    "gate_tanh": ("gated_output", _gate_tanh),
+    "gate_bias_sign": ("gated_output", _gate_bias_sign),
+    "gate_w_out_transposed": ("gated_output", _gate_w_out_transposed),
+    "gate_w_gate_transposed": ("gated_output", _gate_w_gate_transposed),
+    "gate_additive": ("gated_output", _gate_additive),
     "no_lam_on_prev": ("normal_equation_update", _update_no_lam_on_prev),
     "no_lam_on_identity": ("normal_equation_update", _update_no_lam_on_identity),
     "sign_of_cross_term": ("normal_equation_update", _update_sign),
