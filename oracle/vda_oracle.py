@@ -44,6 +44,7 @@ __all__ = [
     "frame_statistics", "normal_equation_update", "text_state", "scan_from",
     "head_states", "readout", "vda_forward_head", "vda_forward",
     "gated_output", "vda_forward_gated_head", "vda_forward_gated",
+    "vda_backward_head", "vda_backward",
 ]
 
 
@@ -164,3 +165,75 @@ def vda_forward_gated(q, k, v, text_k, text_v, lam, w_gate, b_gate, w_out):
     for h in range(out.shape[1]):
         out[:, h] = gated_output(out[:, h], w_gate[h], b_gate[h], w_out[h])
     return out
+
+
+# ---------------------------------------------------------------------------
+# Backward pass (gradients) of the forward op
+# ---------------------------------------------------------------------------
+# The pages train the branch (aiezz page, section 03, bullet "three-stage training
+# adaptation"; laicaila page, the same bullet): layer-wise alignment of the linear
+# branch, then end-to-end optimisation, then LoRA with the branch.  Training needs the
+# gradient of the op.  Given dO = dL/dO for every frame, the chain rule through the
+# definition above gives (A_f = lam I + K_f^T K_f, B_f = K_f^T V_f, W_f the readout
+# state, all A_f symmetric):
+#   readout:       dQ_f = dO_f W_f^T,   dW_f = Q_f^T dO_f,  each direction gets dW_f / 2
+#   forward chain: U_f = A_f^{-1} (dW_f / 2 + lam U_{f+1}),  f = F..1,  U_{F+1} = 0
+#   backward chain: V_f = A_f^{-1} (dW_f / 2 + lam V_{f-1}), f = 1..F,  V_0 = 0
+#   frames:        dB_f = U_f + V_f,   dA_f = -(U_f X_fwd_f^T + V_f X_bwd_f^T)
+#   text:          U_0 = A_0^{-1} lam (U_1 + V_F),  dB_0 = U_0,  dA_0 = -U_0 X_text^T
+#   statistics:    dK += V dB^T + K (dA + dA^T),   dV += K dB
+# (X_f = A_f^{-1} R_f gives dR_f = A_f^{-1} Gamma_f and dA_f = -A_f^{-1} Gamma_f X_f^T.)
+# Each step is written out below in that order with library solves.
+
+def vda_backward_head(q, k, v, text_k, text_v, lam, d_out):
+    """Gradients of sum(d_out * O) for one (batch, head).  q,k [F,n,d], v [F,n,dv],
+    text_k [T,d], text_v [T,dv], d_out [F,n,dv].  Returns (dq, dk, dv, d_text_k, d_text_v)."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    d_out = np.asarray(d_out, dtype=np.float64)
+    d, dv = k.shape[-1], v.shape[-1]
+    text_k = np.asarray(text_k, dtype=np.float64).reshape(-1, d)
+    text_v = np.asarray(text_v, dtype=np.float64).reshape(-1, dv)
+    F = k.shape[0]
+    X_text, X_fwd, X_bwd = head_states(k, v, text_k, text_v, lam)
+    A = [lam * np.eye(d) + frame_statistics(k[f], v[f])[0] for f in range(F)]
+    W = 0.5 * (X_fwd + X_bwd)
+    dq = np.stack([d_out[f] @ W[f].T for f in range(F)]) if F else np.zeros_like(q)
+    half_dW = [0.5 * (q[f].T @ d_out[f]) for f in range(F)]
+    U = [None] * (F + 2)
+    U[F + 1] = np.zeros((d, dv))
+    for f in range(F, 0, -1):                      # frames are 1-based in the chains
+        U[f] = np.linalg.solve(A[f - 1], half_dW[f - 1] + lam * U[f + 1])
+    V = [None] * (F + 1)
+    V[0] = np.zeros((d, dv))
+    for f in range(1, F + 1):
+        V[f] = np.linalg.solve(A[f - 1], half_dW[f - 1] + lam * V[f - 1])
+    dk = np.empty_like(k)
+    dvv = np.empty_like(v)
+    for f in range(1, F + 1):
+        dB = U[f] + V[f]
+        dA = -(U[f] @ X_fwd[f - 1].T + V[f] @ X_bwd[f - 1].T)
+        dk[f - 1] = v[f - 1] @ dB.T + k[f - 1] @ (dA + dA.T)
+        dvv[f - 1] = k[f - 1] @ dB
+    A0 = lam * np.eye(d) + text_k.T @ text_k
+    gamma_text = lam * (U[1] + V[F]) if F else np.zeros((d, dv))
+    U0 = np.linalg.solve(A0, gamma_text)
+    dA0 = -(U0 @ X_text.T)
+    d_text_k = text_v @ U0.T + text_k @ (dA0 + dA0.T)
+    d_text_v = text_k @ U0
+    return dq, dk, dvv, d_text_k, d_text_v
+
+
+def vda_backward(q, k, v, text_k, text_v, lam, d_out):
+    """Gradients over [B,H,...] arrays (heads and batch entries are independent)."""
+    q = np.asarray(q, dtype=np.float64)
+    Bsz, H = q.shape[:2]
+    grads = [np.empty(np.shape(a), dtype=np.float64) for a in (q, k, v, text_k, text_v)]
+    for b in range(Bsz):
+        for h in range(H):
+            res = vda_backward_head(q[b, h], k[b, h], v[b, h], text_k[b, h], text_v[b, h], lam,
+                                    d_out[b, h])
+            for g, r in zip(grads, res):
+                g[b, h] = r
+    return tuple(grads)

@@ -162,8 +162,71 @@ def pin_gate_limits(seed=11, dv=5):
     return bool(ok)
 
 
+def _loss_grads_fd(h, lam, d_out, rng, eps=1e-6):
+    """Central differences of L = sum(d_out * O) along one random direction per input."""
+    names = ("q", "k", "v", "text_k", "text_v")
+    out = []
+    for name in names:
+        dirn = rng.standard_normal(np.shape(h[name]))
+        hp = dict(h); hp[name] = h[name] + eps * dirn
+        hm = dict(h); hm[name] = h[name] - eps * dirn
+        lp = np.sum(d_out * oracle.vda_forward_head(**hp, lam=lam))
+        lm = np.sum(d_out * oracle.vda_forward_head(**hm, lam=lam))
+        out.append((dirn, (lp - lm) / (2 * eps)))
+    return out
+
+
+def pin_backward_finite_differences(seed=31, lam=0.7, F=3, n=4, d=3, dv=2, T=2):
+    """Directional derivatives of sum(d_out * O) by central differences (a route that never
+    uses the adjoint equations) against the oracle's gradients."""
+    rng = np.random.default_rng(seed)
+    h = _tiny_head(seed, F=F, n=n, d=d, dv=dv, T=T)
+    d_out = rng.standard_normal((F, n, dv))
+    g = oracle.vda_backward_head(**h, lam=lam, d_out=d_out)
+    ok = True
+    for gi, (dirn, fd) in zip(g, _loss_grads_fd(h, lam, d_out, rng)):
+        ok &= abs(np.sum(gi * dirn) - fd) <= 1e-6 * max(1.0, abs(fd))
+    return bool(ok)
+
+
+def _torch_forward_head(q, k, v, tk, tv, lam):
+    """The forward op written again with torch float64 ops (solves by torch.linalg.solve)."""
+    import torch
+    d = k.shape[-1]
+    eye = torch.eye(d, dtype=torch.float64)
+
+    def upd(x, kk, vv):
+        return torch.linalg.solve(lam * eye + kk.T @ kk, lam * x + kk.T @ vv)
+
+    xt = upd(torch.zeros(d, v.shape[-1], dtype=torch.float64), tk, tv)
+    fwd, x = [], xt
+    for f in range(k.shape[0]):
+        x = upd(x, k[f], v[f])
+        fwd.append(x)
+    bwd, x = [None] * k.shape[0], xt
+    for f in reversed(range(k.shape[0])):
+        x = upd(x, k[f], v[f])
+        bwd[f] = x
+    return torch.stack([q[f] @ (0.5 * (fwd[f] + bwd[f])) for f in range(k.shape[0])])
+
+
+def pin_backward_torch_autograd(seed=32, lam=0.4, F=4, n=5, d=4, dv=3, T=3):
+    """Every gradient element against torch's reverse-mode autograd of the same op written
+    independently in torch (float64, CPU)."""
+    import torch
+    rng = np.random.default_rng(seed)
+    h = _tiny_head(seed, F=F, n=n, d=d, dv=dv, T=T)
+    d_out = rng.standard_normal((F, n, dv))
+    g = oracle.vda_backward_head(**h, lam=lam, d_out=d_out)
+    ts = [torch.tensor(h[name], dtype=torch.float64, requires_grad=True)
+          for name in ("q", "k", "v", "text_k", "text_v")]
+    (torch.sum(torch.tensor(d_out) * _torch_forward_head(*ts, lam))).backward()
+    return bool(all(np.allclose(gi, t.grad.numpy(), rtol=1e-9, atol=1e-12) for gi, t in zip(g, ts)))
+
+
 PINS = [pin_golden, pin_lstsq, lambda: pin_lstsq(seed=4, n=6, d=3, dv=3), pin_delta_rule,
-        pin_fixed_point, pin_gate_worked_examples, pin_gate_limits]
+        pin_fixed_point, pin_gate_worked_examples, pin_gate_limits,
+        pin_backward_finite_differences, pin_backward_torch_autograd]
 
 
 # ---------------------------------------------------------------------------
@@ -319,6 +382,29 @@ def test_gated_forward_applies_each_heads_weights():
                                                                          tv[b, h], 0.5, Wg[h], bg[h], Wo[h]))
 
 
+def test_backward_matches_finite_differences():
+    assert pin_backward_finite_differences()
+    assert pin_backward_finite_differences(seed=33, lam=0.2, F=1, n=6, d=2, dv=3, T=1)
+
+
+def test_backward_matches_torch_autograd():
+    assert pin_backward_torch_autograd()
+    assert pin_backward_torch_autograd(seed=34, lam=1.0, F=2, n=1, d=3, dv=3, T=1)
+
+
+def test_backward_with_no_text_and_linearity_in_d_out():
+    rng = np.random.default_rng(35)
+    h = _tiny_head(35, F=3, n=4, d=3, dv=2, T=0)
+    h["text_k"], h["text_v"] = np.zeros((0, 3)), np.zeros((0, 2))
+    d1, d2 = rng.standard_normal((3, 4, 2)), rng.standard_normal((3, 4, 2))
+    g1 = oracle.vda_backward_head(**h, lam=0.5, d_out=d1)
+    g2 = oracle.vda_backward_head(**h, lam=0.5, d_out=d2)
+    g12 = oracle.vda_backward_head(**h, lam=0.5, d_out=2 * d1 - d2)
+    for a, b, c in zip(g1, g2, g12):
+        assert np.allclose(c, 2 * a - b, rtol=1e-10, atol=1e-12)
+    assert g1[3].shape == (0, 3) and g1[4].shape == (0, 2)
+
+
 def test_rejects_nonpositive_lambda():
     h = _tiny_head(13)
     with pytest.raises(ValueError):
@@ -421,6 +507,43 @@ MUTANTS = {
     "backward_not_reordered": ("head_states", _states_bwd_not_reversed),
     "exclusive_states": ("head_states", _states_exclusive),
 }
+
+
+# mistakes planted in the backward pass: one-line edits of the oracle's own source
+BACKWARD_MUTANTS = {
+    "adjoint_no_lam": ("half_dW[f - 1] + lam * U[f + 1]", "half_dW[f - 1] + U[f + 1]"),
+    "adjoint_wrong_direction": ("half_dW[f - 1] + lam * V[f - 1]", "half_dW[f - 1] + lam * V[f - 1] * 0"),
+    "dA_states_swapped": ("U[f] @ X_fwd[f - 1].T + V[f] @ X_bwd[f - 1].T",
+                          "U[f] @ X_bwd[f - 1].T + V[f] @ X_fwd[f - 1].T"),
+    "dA_not_symmetrised": ("k[f - 1] @ (dA + dA.T)", "k[f - 1] @ (2 * dA)"),
+    "dW_not_halved": ("half_dW = [0.5 * (q[f].T", "half_dW = [(q[f].T"),
+    "text_adjoint_dropped": ("gamma_text = lam * (U[1] + V[F])", "gamma_text = lam * U[1]"),
+    "dq_forward_state_only": ("d_out[f] @ W[f].T", "d_out[f] @ X_fwd[f].T"),
+}
+
+
+def _backward_mutant(name):
+    import inspect
+    src = inspect.getsource(O.vda_backward_head)
+    old, new = BACKWARD_MUTANTS[name]
+    assert old in src, name
+    ns = dict(vars(O))
+    exec(src.replace(old, new), ns)
+    return ns["vda_backward_head"]
+
+
+@pytest.mark.parametrize("name", sorted(BACKWARD_MUTANTS))
+def test_backward_mutants_are_caught(name, monkeypatch):
+    fn = _backward_mutant(name)
+    monkeypatch.setattr(O, "vda_backward_head", fn)
+    monkeypatch.setattr(oracle, "vda_backward_head", fn, raising=False)
+    results = []
+    for pin in (pin_backward_finite_differences, pin_backward_torch_autograd):
+        try:
+            results.append(pin())
+        except Exception:
+            results.append(False)
+    assert not all(results), f"mutant {name} passes every pin"
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
