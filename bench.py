@@ -251,6 +251,100 @@ def _rows(path):
         return list(csv.DictReader(f))
 
 
+def run_backward(args):
+    """Time vda_backward (gradients of q, k, v and the text) after one forward pass on the same
+    plan; one JSON line like the forward's, with the backward's own spans."""
+    import numpy as np
+    import torch
+    import oracle
+    import workloads as W
+    from frame_wise_delta_vda_amd import vda as binding
+
+    w = W.by_name(args.workload)
+    if w.dtype != "bf16":
+        raise SystemExit("the backward pass runs on bfloat16 workloads")
+    print(f"[bench] backward {w.name}: generating inputs", file=sys.stderr, flush=True)
+    arrays = W.full_storage(w)
+    dev = to_device(w, arrays)
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence((w.seed, 0xD0))))
+    d_out_bits = W.float32_to_bf16_bits(rng.standard_normal(w.shapes()["out"], dtype=np.float32))
+    d_out = torch.from_numpy(d_out_bits.view(np.int16)).view(torch.bfloat16).cuda()
+    q, k, v, tk, tv = (dev[x] for x in W.TENSORS)
+    plan = binding.Plan(w.B, w.H, w.F, w.n, w.d, w.dv, w.T, w.lam, w.dtype)
+    out = torch.empty(w.shapes()["out"], device="cuda", dtype=torch.bfloat16)
+    plan.forward(q, k, v, tk, tv, out)  # the statistics and states the backward pass reads
+    grads = tuple(torch.empty_like(t) for t in (q, k, v, tk, tv))
+
+    def step():
+        plan.backward(q, k, v, tk, tv, d_out, grads=grads)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    plan.enable_timing(args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    calls, st_ms, sc_ms, rd_ms = plan.timings()
+    if calls != args.steps:
+        raise RuntimeError(f"timed {calls} of {args.steps} passes")
+    BH = w.B * w.H
+    tok = BH * w.F * w.n
+    ttok = BH * w.T
+    e = 2  # bf16
+    # bytes each span must move: Q^T dO reads Q and dO; the products read dO, K, V and write
+    # dQ, dK, dV (and the text's K, V in, gradients out)
+    alg = {"stats": tok * (w.d + w.dv) * e,
+           "products": tok * (w.dv + w.d + w.dv + w.d + w.d + w.dv) * e + ttok * 2 * (w.d + w.dv) * e}
+    spans = {"stats": st_ms, "adjoint": sc_ms, "products": rd_ms}
+    kernels = {n: {"ms": round(ms, 4)} for n, ms in spans.items()}
+    for n in alg:
+        gbs = alg[n] / (spans[n] * 1e-3) / 1e9
+        kernels[n].update({"alg_bytes": alg[n], "GB/s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)})
+    dom = max(alg, key=lambda n: spans[n])
+    ach = kernels[dom]["GB/s"]
+    # the whole backward must read Q, K, V, dO and write dQ, dK, dV (and the text's two pairs)
+    whole = tok * (4 * w.d + 3 * w.dv) * e + ttok * 2 * (w.d + w.dv) * e
+    result = {
+        "metric": "VDA backward (gradients of q, k, v and text) video tokens/s at 768p shape; % of HBM roofline",
+        "value": round(w.video_tokens / (ms_step * 1e-3), 1), "unit": "video tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "pass": "backward", "B": w.B, "H": w.H, "F": w.F, "n": w.n,
+                   "d": w.d, "dv": w.dv, "T": w.T, "lambda": w.lam, "alg_bytes_per_step": whole,
+                   "whole_step_GB/s": round(whole / (ms_step * 1e-3) / 1e9, 1)},
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None},
+        "kernels": kernels,
+    }
+    plan.close()
+    if not args.no_cpu_baseline:
+        print(f"[bench] backward {w.name}: timing the oracle on host cores", file=sys.stderr, flush=True)
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        threads = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
+        spent, done = 0.0, 0
+        for h in range(w.H):
+            x = {kk: W.storage_to_float64(w, arrays[kk][0, h]) for kk in W.TENSORS}
+            dO = W.bf16_bits_to_float32(d_out_bits[0, h]).astype(np.float64)
+            t1 = time.perf_counter()
+            oracle.vda_backward_head(x["q"], x["k"], x["v"], x["text_k"], x["text_v"], w.lam, dO)
+            spent += time.perf_counter() - t1
+            done += 1
+            if spent >= args.cpu_budget:
+                break
+        result["cpu_baseline"] = {"value": done * w.F * w.n / spent, "unit": "video tokens/s", "cores": threads,
+                                  "kind": "oracle", "sample": f"{done} of {w.B * w.H} (b,h) slices of {w.name}, "
+                                                              f"numpy float64 backward, {spent:.1f} s"}
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
 def summarize_stats(args):
     rows = _rows(args.summarize_stats)
     print(f"# rocprofv3 --kernel-trace --stats summary")
@@ -315,6 +409,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="768p_bf16")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward pass (gradients) after one forward pass")
     ap.add_argument("--gated", action="store_true",
                     help="run the pass with the gated fusion epilogue (seeded synthetic weights)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -336,6 +432,8 @@ def main():
         return summarize_pmc(args)
     if args.copy_probe:
         return copy_probe(args)
+    if args.backward:
+        return run_backward(args)
     run(args)
 
 

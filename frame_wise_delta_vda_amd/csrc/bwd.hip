@@ -1,0 +1,350 @@
+// Backward pass of the VDA forward: the per-frame adjoint terms.
+//
+// Training the branch (aiezz page, section 03, and laicaila page, "technical principles":
+// bullet "three-stage training adaptation") needs the op's gradient.  With dO the
+// gradient of the output, the statistics stage run on (Q, dO) gives dW_f = Q_f^T dO_f,
+// and the scan run on (A^{-1}, dW) gives the two adjoint chains scaled by two:
+//   S_fwd_f = A_f^{-1} (dW_f + lam S_fwd_{f-1})  = 2 V_f,
+//   S_bwd_f = A_f^{-1} (dW_f + lam S_bwd_{f+1})  = 2 U_f,
+// both from a zero start, stored in float32 (as are the forward states, recomputed by the
+// scan for this pass).  Per frame this file forms, in the layouts the readout kernels take
+// as their state (state_index), with dB and M as bf16 hi + lo pairs:
+//   WT_f = W_f^T,            W_f = (X_fwd_f + X_bwd_f) / 2          (dQ_f = dO_f W_f^T)
+//   DB2_f = [dB hi ; dB lo], dB_f = (S_fwd_f + S_bwd_f) / 2          (dV_f = [K K] DB2_f)
+//   Z_f  = [M hi ; M lo ; dB^T hi ; dB^T lo],  M_f = dA_f + dA_f^T,
+//          dA_f = -(S_bwd_f X_fwd_f^T + S_fwd_f X_bwd_f^T) / 2       (dK_f = [K K V V] Z_f)
+// and for the text (frame 0 of a head), with Gamma = lam (S_bwd_1 + S_fwd_F) / 2:
+//   U_0 = A_0^{-1} Gamma,  dB_0 = U_0,  dA_0 = -U_0 X_text^T,  X_text = A_0^{-1} Bm_0.
+// The arithmetic is fp32 on the vector units: it is O(d^3) per frame, against the
+// O(n d^2) token work of the readouts that consume these matrices.
+#include "vda_device.h"
+#include "vda_internal.h"
+
+namespace vda {
+namespace {
+
+// position of the 8-element run (rows 8 (e / 8) .. +7 of one column) that state-order
+// chunk q holds, for a D-row state: returns (row0, col)
+template <int D>
+__device__ __forceinline__ void chunk_rc(int q, int& row0, int& col) {
+  const int c15 = q & 15, t = q >> 4, g = t & 3, u = t >> 2;
+  const int rb = u % (D / 32), cb = u / (D / 32);
+  row0 = rb * 32 + g * 8;
+  col = cb * 16 + c15;
+}
+
+// bf16 hi / lo of x: hi = rne(x), lo = rne(x - hi)
+__device__ __forceinline__ float lo_part(float x) { return x - bf16_bits_to_f32(f32_to_bf16_bits(x)); }
+
+template <int D, int DV>
+struct BwdFrame {
+  static constexpr int LROW = D + 4;              // floats per LDS row: row c holds column c of a D x DV matrix
+  static constexpr int MAT = DV * LROW;
+  static constexpr int PROW = D + 4;              // floats per LDS row of P (D x D)
+  static constexpr int LDS_BYTES = cmax(2 * MAT * 4, D * PROW * 4);
+  static constexpr int PB = D / 16;               // P block side per thread (16 x 16 threads)
+  static constexpr int ZR = 2 * D + 2 * DV;       // rows of Z: M hi, M lo, dB^T hi, dB^T lo
+};
+
+// One workgroup per video frame.  Inputs are float32 and blocked (blk_index): the forward
+// states X_fwd, X_bwd recomputed for the backward pass, and the adjoint chains S_fwd, S_bwd.
+// Outputs, in the readout's state order (bf16): WT = W^T; DB2 = [dB hi ; dB lo]; Z = [M hi ;
+// M lo ; dB^T hi ; dB^T lo] -- the gradient products take each factor as hi + lo, since
+// for ill-conditioned frames dB and M are large along directions that K maps to small
+// values, and one bf16 rounding there shows in K dB.
+template <int D, int DV>
+__global__ void __launch_bounds__(kThreads)
+bwd_frame_kernel(const float* __restrict__ xf, const float* __restrict__ xb,
+                 const float* __restrict__ sf, const float* __restrict__ sb,
+                 uint16_t* __restrict__ wt, uint16_t* __restrict__ db2, uint16_t* __restrict__ z) {
+  using C = BwdFrame<D, DV>;
+  extern __shared__ __align__(16) unsigned char smem[];
+  float* L1 = reinterpret_cast<float*>(smem);
+  float* L2 = L1 + C::MAT;
+  const int64_t fr = blockIdx.x;
+  const int64_t base = fr * int64_t(D) * DV;
+  const float* XF = xf + base;
+  const float* XB = xb + base;
+  const float* SF = sf + base;
+  const float* SB = sb + base;
+  const int tid = threadIdx.x;
+  auto dB = [&](int i, int c) -> float {
+    const int e = blk_index(i, c, D);
+    return 0.5f * (SB[e] + SF[e]);
+  };
+
+  // 1. element-wise outputs straight from the (cached) inputs
+  for (int qc = tid; qc < D * DV / 8; qc += kThreads) {
+    int r0, c;
+    uint32_t w[4];
+    chunk_rc<DV>(qc, r0, c);  // WT: rows r0.. are value features, column c an input feature
+#pragma unroll
+    for (int m = 0; m < 8; m += 2) {
+      const int e0 = blk_index(c, r0 + m, D), e1 = blk_index(c, r0 + m + 1, D);
+      w[m / 2] = pack_bf16x2(0.5f * (XF[e0] + XB[e0]), 0.5f * (XF[e1] + XB[e1]));
+    }
+    reinterpret_cast<uint4*>(wt + base)[qc] = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+  uint16_t* dbf = db2 + fr * int64_t(2 * D) * DV;
+  for (int qc = tid; qc < 2 * D * DV / 8; qc += kThreads) {
+    int r0, c;
+    chunk_rc<2 * D>(qc, r0, c);  // rows 0..D-1: dB hi, D..2D-1: dB lo
+    const bool lo = r0 >= D;
+    const int i0 = lo ? r0 - D : r0;
+    uint32_t w[4];
+#pragma unroll
+    for (int m = 0; m < 8; m += 2) {
+      const float a = dB(i0 + m, c), b = dB(i0 + m + 1, c);
+      w[m / 2] = lo ? pack_bf16x2(lo_part(a), lo_part(b)) : pack_bf16x2(a, b);
+    }
+    reinterpret_cast<uint4*>(dbf)[qc] = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+  uint16_t* zf = z + fr * int64_t(C::ZR) * D;
+  for (int qc = tid; qc < C::ZR * D / 8; qc += kThreads) {
+    int r0, i;
+    chunk_rc<C::ZR>(qc, r0, i);  // rows 2D + c (hi) and 2D + DV + c (lo): dB^T[c][i] = dB[i][c]
+    if (r0 < 2 * D) continue;
+    const bool lo = r0 >= 2 * D + DV;
+    const int c0 = r0 - 2 * D - (lo ? DV : 0);
+    uint32_t w[4];
+#pragma unroll
+    for (int m = 0; m < 8; m += 2) {
+      const float a = dB(i, c0 + m), b = dB(i, c0 + m + 1);
+      w[m / 2] = lo ? pack_bf16x2(lo_part(a), lo_part(b)) : pack_bf16x2(a, b);
+    }
+    reinterpret_cast<uint4*>(zf)[qc] = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+
+  // 2. P = S_bwd X_fwd^T + S_fwd X_bwd^T (D x D), a PB x PB block per thread, in two passes
+  //    through LDS (each pass holds two float32 matrices, transposed: row c = column c)
+  auto load_t = [&](const float* M, float* L) {
+    for (int g = tid; g < D * DV / 4; g += kThreads) {
+      const int c15 = g & 15, t = g >> 4, q4 = t & 3, u = t >> 2;
+      const int i = (u % (D / 16)) * 16 + q4 * 4, c = (u / (D / 16)) * 16 + c15;
+      *reinterpret_cast<float4*>(L + c * C::LROW + i) = reinterpret_cast<const float4*>(M)[g];
+    }
+  };
+  const int bi = (tid >> 4) * C::PB, bj = (tid & 15) * C::PB;
+  float p[C::PB][C::PB];
+#pragma unroll
+  for (int a = 0; a < C::PB; ++a)
+#pragma unroll
+    for (int b = 0; b < C::PB; ++b) p[a][b] = 0.0f;
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    load_t(pass == 0 ? SB : SF, L1);
+    load_t(pass == 0 ? XF : XB, L2);
+    __syncthreads();
+    for (int c = 0; c < DV; ++c) {
+      float u[C::PB], xv[C::PB];
+#pragma unroll
+      for (int a = 0; a < C::PB; ++a) {
+        u[a] = L1[c * C::LROW + bi + a];
+        xv[a] = L2[c * C::LROW + bj + a];
+      }
+#pragma unroll
+      for (int a = 0; a < C::PB; ++a)
+#pragma unroll
+        for (int b = 0; b < C::PB; ++b) p[a][b] = __builtin_fmaf(u[a], xv[b], p[a][b]);
+    }
+    __syncthreads();
+  }
+  float* LP = reinterpret_cast<float*>(smem);
+#pragma unroll
+  for (int a = 0; a < C::PB; ++a)
+#pragma unroll
+    for (int b = 0; b < C::PB; ++b) LP[(bi + a) * C::PROW + bj + b] = p[a][b];
+  __syncthreads();
+
+  // 3. Z rows 0..2D-1: M = dA + dA^T = -(P + P^T) / 2, hi then lo
+  for (int qc = tid; qc < C::ZR * D / 8; qc += kThreads) {
+    int r0, c;
+    chunk_rc<C::ZR>(qc, r0, c);
+    if (r0 >= 2 * D) continue;
+    const bool lo = r0 >= D;
+    const int i0 = lo ? r0 - D : r0;
+    uint32_t w[4];
+#pragma unroll
+    for (int m = 0; m < 8; m += 2) {
+      const int r = i0 + m;
+      const float a = -0.5f * (LP[r * C::PROW + c] + LP[c * C::PROW + r]);
+      const float b = -0.5f * (LP[(r + 1) * C::PROW + c] + LP[c * C::PROW + r + 1]);
+      w[m / 2] = lo ? pack_bf16x2(lo_part(a), lo_part(b)) : pack_bf16x2(a, b);
+    }
+    reinterpret_cast<uint4*>(zf)[qc] = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+// The text frame of each head: one workgroup per (b, h), fp32 through LDS.
+//   Gamma = lam (S_bwd_1 + S_fwd_F) / 2,  X_text = A_0^{-1} Bm_0,  U_0 = A_0^{-1} Gamma,
+//   DB2_text = [U_0 hi ; lo],  Z_text = [M hi ; M lo ; U_0^T hi ; lo] with M = -(P + P^T),
+//   P = U_0 X_text^T.  A_0^{-1} arrives as the packed bf16 hi / lo planes of the statistics.
+template <int D, int DV>
+struct BwdText {
+  static constexpr int AROW = D + 1;
+  static constexpr int RROW = DV + 1;
+  static constexpr int ASZ = D * cmax(AROW, RROW);  // A_0^{-1}, later U_0
+  static constexpr int LDS_BYTES = (ASZ + D * RROW) * 4;
+};
+
+template <int D, int DV>
+__global__ void __launch_bounds__(kThreads)
+bwd_text_kernel(const uint16_t* __restrict__ ainv, const float* __restrict__ bm,
+                const float* __restrict__ sf, const float* __restrict__ sb,
+                uint16_t* __restrict__ db2_text, uint16_t* __restrict__ z_text, int64_t F, float lam) {
+  using C = BwdText<D, DV>;
+  extern __shared__ __align__(16) unsigned char smem[];
+  float* LA = reinterpret_cast<float*>(smem);   // A_0^{-1} [D][AROW]
+  float* LR = LA + C::ASZ;                       // right-hand sides / results [D][RROW]
+  float* LU = LA;                                // U_0 [D][RROW], over A once it is used
+  const int64_t bh = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int64_t F1 = F + 1;
+  const uint16_t* hi = ainv + bh * F1 * int64_t(2 * D * D);
+  const uint16_t* lo = hi + sym_blocks(D) * 256;
+  for (int e = tid; e < D * D; e += kThreads) {
+    const int r = e / D, c = e % D;
+    const int rr = (r >> 4) <= (c >> 4) ? r : c, cc = (r >> 4) <= (c >> 4) ? c : r;
+    const int idx = sym_index(rr, cc, D);
+    LA[r * C::AROW + c] = bf16_bits_to_f32(hi[idx]) + bf16_bits_to_f32(lo[idx]);
+  }
+  const float* bm0 = bm + bh * F1 * int64_t(D) * DV;
+  for (int e = tid; e < D * DV; e += kThreads) {
+    const int r = e / DV, c = e % DV;
+    LR[r * C::RROW + c] = bm0[blk_index(r, c, D)];
+  }
+  __syncthreads();
+  constexpr int RI = D / 16, RJ = DV / 16;
+  const int ti = tid >> 4, tj = tid & 15;
+  auto solve_product = [&](float (&y)[RI][RJ]) {
+#pragma unroll
+    for (int a = 0; a < RI; ++a)
+#pragma unroll
+      for (int b = 0; b < RJ; ++b) y[a][b] = 0.0f;
+    for (int k = 0; k < D; ++k) {
+#pragma unroll
+      for (int a = 0; a < RI; ++a) {
+        const float av = LA[(ti * RI + a) * C::AROW + k];
+#pragma unroll
+        for (int b = 0; b < RJ; ++b) y[a][b] = __builtin_fmaf(av, LR[k * C::RROW + tj * RJ + b], y[a][b]);
+      }
+    }
+  };
+  float xt[RI][RJ], u0[RI][RJ];
+  solve_product(xt);                       // X_text
+  __syncthreads();
+  // Gamma = lam (S_bwd_1 + S_fwd_F) / 2 (frame f of a chain at index f - 1)
+  const float* s1 = sb + (bh * F + 0) * int64_t(D) * DV;
+  const float* sF = sf + (bh * F + (F - 1)) * int64_t(D) * DV;
+  for (int e = tid; e < D * DV; e += kThreads) {
+    const int r = e / DV, c = e % DV;
+    const int idx = blk_index(r, c, D);
+    LR[r * C::RROW + c] = 0.5f * lam * (s1[idx] + sF[idx]);
+  }
+  __syncthreads();
+  solve_product(u0);                       // U_0
+  __syncthreads();
+#pragma unroll
+  for (int a = 0; a < RI; ++a)
+#pragma unroll
+    for (int b = 0; b < RJ; ++b) {
+      LU[(ti * RI + a) * C::RROW + tj * RJ + b] = u0[a][b];
+      LR[(ti * RI + a) * C::RROW + tj * RJ + b] = xt[a][b];
+    }
+  __syncthreads();
+  auto put = [&](uint16_t* dst, int r, int c, int R, float x) {  // hi at row r, lo at row r + R
+    dst[state_index(r, c, 2 * R)] = uint16_t(f32_to_bf16_bits(x));
+    dst[state_index(r + R, c, 2 * R)] = uint16_t(f32_to_bf16_bits(lo_part(x)));
+  };
+  uint16_t* dbt = db2_text + bh * int64_t(2 * D) * DV;
+  for (int e = tid; e < D * DV; e += kThreads) {
+    const int r = e / DV, c = e % DV;
+    put(dbt, r, c, D, LU[r * C::RROW + c]);
+  }
+  constexpr int ZR = 2 * D + 2 * DV;
+  uint16_t* zt = z_text + bh * int64_t(ZR) * D;
+  for (int e = tid; e < DV * D; e += kThreads) {  // rows 2D + c (hi), 2D + DV + c (lo): U_0^T
+    const int c = e / D, i = e % D;
+    const float x = LU[i * C::RROW + c];
+    zt[state_index(2 * D + c, i, ZR)] = uint16_t(f32_to_bf16_bits(x));
+    zt[state_index(2 * D + DV + c, i, ZR)] = uint16_t(f32_to_bf16_bits(lo_part(x)));
+  }
+  for (int e = tid; e < D * D; e += kThreads) {  // rows i (hi), D + i (lo): M = -(P + P^T)
+    const int i = e / D, j = e % D;
+    float pij = 0.0f, pji = 0.0f;
+    for (int c = 0; c < DV; ++c) {
+      pij = __builtin_fmaf(LU[i * C::RROW + c], LR[j * C::RROW + c], pij);
+      pji = __builtin_fmaf(LU[j * C::RROW + c], LR[i * C::RROW + c], pji);
+    }
+    const float x = -(pij + pji);
+    zt[state_index(i, j, ZR)] = uint16_t(f32_to_bf16_bits(x));
+    zt[state_index(D + i, j, ZR)] = uint16_t(f32_to_bf16_bits(lo_part(x)));
+  }
+}
+
+template <int D, int DV>
+hipError_t launch_bwd_frames_t(const BwdProblem& b, hipStream_t s, bool prepare) {
+  using C = BwdFrame<D, DV>;
+  using T = BwdText<D, DV>;
+  auto kf = bwd_frame_kernel<D, DV>;
+  auto kt = bwd_text_kernel<D, DV>;
+  if (prepare) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kf),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
+    if (e != hipSuccess) return e;
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(kt),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, T::LDS_BYTES);
+  }
+  const int64_t BH = b.p.B * b.p.H;
+  if (BH * b.p.F > 0)
+    hipLaunchKernelGGL(kf, dim3(unsigned(BH * b.p.F)), dim3(kThreads), C::LDS_BYTES, s, b.xf32, b.xb32,
+                       b.sf, b.sb, b.wt, b.db2, b.z);
+  if (BH > 0 && b.p.T > 0 && b.p.F > 0)
+    hipLaunchKernelGGL(kt, dim3(unsigned(BH)), dim3(kThreads), T::LDS_BYTES, s,
+                       reinterpret_cast<const uint16_t*>(b.p.ainv), b.p.bm, b.sf, b.sb, b.db2_text,
+                       b.z_text, b.p.F, b.p.lam);
+  return hipGetLastError();
+}
+
+__global__ void zero_kernel(uint4* __restrict__ p, int64_t n16, uint8_t* __restrict__ tail, int64_t ntail) {
+  for (int64_t i = blockIdx.x * int64_t(kThreads) + threadIdx.x; i < n16; i += int64_t(gridDim.x) * kThreads)
+    p[i] = make_uint4(0, 0, 0, 0);
+  if (blockIdx.x == 0 && threadIdx.x < ntail) tail[threadIdx.x] = 0;
+}
+
+}  // namespace
+
+// Zero a device buffer with a kernel (so the call may sit in a captured graph).
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t s) {
+  const int64_t n16 = int64_t(bytes / 16), ntail = int64_t(bytes % 16);
+  int64_t blocks = (n16 + kThreads - 1) / kThreads;
+  if (blocks < 1) blocks = 1;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(zero_kernel, dim3(unsigned(blocks)), dim3(kThreads), 0, s, static_cast<uint4*>(p), n16,
+                     static_cast<uint8_t*>(p) + n16 * 16, ntail);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_frames(const BwdProblem& b, hipStream_t s) {
+#define VDA_CASE(DD, VV) \
+  if (b.p.d == DD && b.p.dv == VV) return launch_bwd_frames_t<DD, VV>(b, s, false);
+  VDA_CASE(32, 32) VDA_CASE(32, 64) VDA_CASE(32, 128)
+  VDA_CASE(64, 32) VDA_CASE(64, 64) VDA_CASE(64, 128)
+  VDA_CASE(128, 32) VDA_CASE(128, 64) VDA_CASE(128, 128)
+#undef VDA_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t prepare_bwd_frames(const Problem& p) {
+  BwdProblem b{};
+  b.p = p;
+#define VDA_CASE(DD, VV) \
+  if (p.d == DD && p.dv == VV) return launch_bwd_frames_t<DD, VV>(b, nullptr, true);
+  VDA_CASE(32, 32) VDA_CASE(32, 64) VDA_CASE(32, 128)
+  VDA_CASE(64, 32) VDA_CASE(64, 64) VDA_CASE(64, 128)
+  VDA_CASE(128, 32) VDA_CASE(128, 64) VDA_CASE(128, 128)
+#undef VDA_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace vda

@@ -385,6 +385,128 @@ readout_gated_kernel(const In* __restrict__ q, const uint16_t* __restrict__ xf,
   }
 }
 
+// Gradient products of the backward pass: out_f = [Q1 (R1 times) Q2 (R2 times)] S_f, with
+// the state S_f (R1 D1 + R2 D2 rows x DV) in state order.  Each factor of a product
+// arrives as bf16 hi + lo rows (R = 2), so each input's operand fragments feed two MFMAs
+// (dV = [K K] [dB hi ; lo], dK = [K K V V] [M hi ; M lo ; dB^T hi ; dB^T lo]).  The state
+// is up to four times as deep as a forward state, so the waves split the output features
+// WF ways (and the tokens of a 16 (4 / WF)-token tile the rest), to keep each wave's
+// fragments within 32 x 16 bytes per lane.
+template <int D1, int R1, int D2, int R2, int DV, int WF>
+struct ReadParts {
+  static constexpr int KS1 = D1 / 32, KS2 = D2 / 32;
+  static constexpr int KS = R1 * KS1 + R2 * KS2;  // k-steps over the state's rows
+  static constexpr int DS = 32 * KS;              // state rows
+  static constexpr int WT = 4 / WF;               // waves across the tokens of a tile
+  static constexpr int TT = 16 * WT;
+  static constexpr int FH = DV / WF;              // output features per wave
+  static constexpr int NBW = FH / 16;
+  static constexpr int NQ = KS1 + KS2;            // operand loads per lane and tile
+  static constexpr int OWROW = FH + 8;
+  static constexpr int OCH = FH / 8;
+  static constexpr int ORPI = 64 / OCH < 16 ? 64 / OCH : 16;
+  static constexpr int OST = 16 / ORPI;
+  static constexpr int OW_BYTES = 16 * OWROW * 2;
+  static constexpr int LDS_BYTES = 4 * OW_BYTES;
+  static_assert(NBW >= 1 && NBW * KS <= 32, "fragments exceed the register budget");
+};
+
+template <int D1, int R1, int D2, int R2, int DV, int WF>
+__global__ void __launch_bounds__(kThreads, 2)
+readout_parts_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ q2,
+                     const uint16_t* __restrict__ st, uint16_t* __restrict__ out, int64_t n,
+                     int64_t tiles_per_frame, int64_t splits, int64_t tiles_per_split,
+                     int64_t head_blocks, int64_t tail_splits, int64_t tail_tiles_per_split) {
+  using C = ReadParts<D1, R1, D2, R2, DV, WF>;
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int th = wave % C::WT, fh = wave / C::WT;
+  uint16_t* ow = reinterpret_cast<uint16_t*>(smem + wave * C::OW_BYTES);
+  const int c16 = lane & 15, g4 = lane >> 4;
+  int64_t frame, t_first, tps;
+  if (blockIdx.x < head_blocks) {
+    frame = blockIdx.x / splits;
+    t_first = (blockIdx.x % splits) * tiles_per_split;
+    tps = tiles_per_split;
+  } else {
+    const int64_t i = blockIdx.x - head_blocks;
+    frame = head_blocks / splits + i / tail_splits;
+    t_first = (i % tail_splits) * tail_tiles_per_split;
+    tps = tail_tiles_per_split;
+  }
+  const int64_t t_last = (t_first + tps < tiles_per_frame) ? t_first + tps : tiles_per_frame;
+  if (t_first >= t_last) return;
+
+  uint4 wfr[C::NBW][C::KS];
+  {
+    const uint4* sp = reinterpret_cast<const uint4*>(st + frame * int64_t(C::DS) * DV) + lane;
+#pragma unroll
+    for (int jb = 0; jb < C::NBW; ++jb)
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) wfr[jb][ks] = sp[((fh * C::NBW + jb) * C::KS + ks) * 64];
+  }
+  auto wave_rows = [&](int64_t tok0) -> uint32_t {
+    const int64_t r = n - tok0;
+    return uint32_t(r < 0 ? 0 : (r < 16 ? r : 16));
+  };
+  auto load_q = [&](int64_t tile, uint4 (&dst)[C::NQ]) {
+    const int64_t tok0 = tile * C::TT + 16 * th;
+    const auto r1 = make_rsrc(q1 + (frame * n + tok0) * D1, wave_rows(tok0) * D1 * 2);
+#pragma unroll
+    for (int ks = 0; ks < C::KS1; ++ks) dst[ks] = buffer_load16(r1, uint32_t((c16 * D1 + 32 * ks + 8 * g4) * 2));
+    if constexpr (C::KS2 > 0) {
+      const auto r2 = make_rsrc(q2 + (frame * n + tok0) * D2, wave_rows(tok0) * D2 * 2);
+#pragma unroll
+      for (int ks = 0; ks < C::KS2; ++ks)
+        dst[C::KS1 + ks] = buffer_load16(r2, uint32_t((c16 * D2 + 32 * ks + 8 * g4) * 2));
+    }
+  };
+  uint4 pfa[C::NQ], pfb[C::NQ];
+  load_q(t_first, pfa);
+  load_q(t_first + 1 < t_last ? t_first + 1 : t_first, pfb);
+
+  auto step = [&](int64_t tile, uint4 (&pf)[C::NQ]) {
+    const int64_t tok0 = tile * C::TT + 16 * th;
+    uint4 qf[C::NQ];
+#pragma unroll
+    for (int i = 0; i < C::NQ; ++i) qf[i] = pf[i];
+    load_q(tile + 2 < t_last ? tile + 2 : t_last - 1, pf);
+#pragma unroll
+    for (int jb = 0; jb < C::NBW; ++jb) {
+      f32x4 acc = f32x4{};
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        // k-step ks of the state: copy r of input 1 (ks < R1 KS1) or of input 2
+        const int qi = ks < R1 * C::KS1 ? ks % C::KS1 : C::KS1 + (ks - R1 * C::KS1) % (C::KS2 > 0 ? C::KS2 : 1);
+        acc = mfma16_bf16(wfr[jb][ks], qf[qi], acc);
+      }
+      *reinterpret_cast<uint2*>(ow + c16 * C::OWROW + 16 * jb + 4 * g4) =
+          make_uint2(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]));
+    }
+    const auto rs = make_rsrc(out + (frame * n + tok0) * DV, wave_rows(tok0) * DV * 2);
+    const int orow = lane / C::OCH, och = lane % C::OCH;
+    if (orow < C::ORPI) {
+#pragma unroll
+      for (int j = 0; j < C::OST; ++j) {
+        const int r = orow + j * C::ORPI;
+        buffer_store16<kCacheStreamOut>(rs, uint32_t(r * DV * 2 + fh * C::FH * 2 + och * 16),
+                                        *reinterpret_cast<const uint4*>(ow + r * C::OWROW + och * 8));
+      }
+    }
+  };
+  for (int64_t tile = t_first; tile < t_last; tile += 2) {
+    step(tile, pfa);
+    if (tile + 1 < t_last) step(tile + 1, pfb);
+  }
+}
+
+// smallest output-feature split whose fragments fit 32 x 16 bytes per lane
+template <int KS, int DV>
+constexpr int parts_wf() {
+  return (DV / 16) * KS <= 32 ? 1 : (DV / 32) * KS <= 32 ? 2 : 4;
+}
+
 template <int D, int DV>
 struct ReadF32 {
   static constexpr int WROW = DV + 4;
@@ -536,6 +658,21 @@ hipError_t launch_readout_gated_t(const Problem& p, const void* q, const GateWei
   else launch(readout_gated_kernel<D, DV, uint16_t>, uint16_t{});
   return hipGetLastError();
 }
+
+template <int D1, int R1, int D2, int R2, int DV>
+hipError_t launch_parts_t(const Problem& p, const void* q1, const void* q2, const void* state, void* out,
+                          hipStream_t s) {
+  constexpr int KS = R1 * (D1 / 32) + R2 * (D2 / 32);
+  constexpr int WF = parts_wf<KS, DV>();
+  using C = ReadParts<D1, R1, D2, R2, DV, WF>;
+  const ReadGrid gr = readout_grid(p.B * p.H * p.F, (p.n + C::TT - 1) / C::TT, p.num_cus);
+  hipLaunchKernelGGL((readout_parts_kernel<D1, R1, D2, R2, DV, WF>), dim3(unsigned(gr.grid)), dim3(kThreads),
+                     C::LDS_BYTES, s, static_cast<const uint16_t*>(q1), static_cast<const uint16_t*>(q2),
+                     static_cast<const uint16_t*>(state), static_cast<uint16_t*>(out), p.n, gr.tpf,
+                     gr.splits, gr.tps, gr.head_blocks, gr.tail_splits, gr.tail_tps);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_readout(const Problem& p, const void* q, void* out, hipStream_t s) {
@@ -566,6 +703,31 @@ hipError_t launch_readout_gated(const Problem& p, const void* q, const GateWeigh
                                 hipStream_t s) {
 #define VDA_CASE(DD, VV) \
   if (p.d == DD && p.dv == VV) return launch_readout_gated_t<DD, VV>(p, q, gw, out, s, false);
+  VDA_CASE(32, 32) VDA_CASE(32, 64) VDA_CASE(32, 128)
+  VDA_CASE(64, 32) VDA_CASE(64, 64) VDA_CASE(64, 128)
+  VDA_CASE(128, 32) VDA_CASE(128, 64) VDA_CASE(128, 128)
+#undef VDA_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace vda
+
+namespace vda {
+
+hipError_t launch_grad_dv(const Problem& p, const void* k, const void* state, void* out, hipStream_t s) {
+#define VDA_CASE(DD, VV) \
+  if (p.d == DD && p.dv == VV) return launch_parts_t<DD, 2, 0, 0, VV>(p, k, nullptr, state, out, s);
+  VDA_CASE(32, 32) VDA_CASE(32, 64) VDA_CASE(32, 128)
+  VDA_CASE(64, 32) VDA_CASE(64, 64) VDA_CASE(64, 128)
+  VDA_CASE(128, 32) VDA_CASE(128, 64) VDA_CASE(128, 128)
+#undef VDA_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_grad_dk(const Problem& p, const void* k, const void* v, const void* state, void* out,
+                          hipStream_t s) {
+#define VDA_CASE(DD, VV) \
+  if (p.d == DD && p.dv == VV) return launch_parts_t<DD, 2, VV, 2, DD>(p, k, v, state, out, s);
   VDA_CASE(32, 32) VDA_CASE(32, 64) VDA_CASE(32, 128)
   VDA_CASE(64, 32) VDA_CASE(64, 64) VDA_CASE(64, 128)
   VDA_CASE(128, 32) VDA_CASE(128, 64) VDA_CASE(128, 128)

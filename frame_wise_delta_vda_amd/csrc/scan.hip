@@ -163,6 +163,10 @@ scan_kernel(const float* __restrict__ ainv, const float* __restrict__ bm,
 // bfloat16 plans.  One wave per 16-row block of X (D/16 waves), 32 columns of X per
 // workgroup (DV/32 workgroups per chain).  Each wave loads only its own 16 rows of
 // Ainv_f, as 1 KB fragment-ordered runs (frag_index), and the 32-column slice of Bm.
+// How the bfloat16 scan stores its states: bf16 in the readout's operand order, the same
+// with the FP8 plans' paired row order, or float32 blocked (for the backward pass).
+constexpr int kStoreBf16 = 0, kStorePairedBf16 = 1, kStoreF32 = 2;
+
 template <int D, int DV>
 struct ScanBf16Cfg {
   static constexpr int NW = D / 16;               // waves; wave w owns rows 16w..16w+15
@@ -186,7 +190,7 @@ template <int D, int DV>
 __global__ void __launch_bounds__(4 * D)
 scan_bf16_kernel(const uint16_t* __restrict__ ainv_planes, const float* __restrict__ bm,
                  float* __restrict__ xf, float* __restrict__ xb, int64_t nchains, int64_t F,
-                 float lam, int64_t grid, bool paired) {
+                 float lam, int64_t grid, int store_mode) {
   using C = ScanBf16Cfg<D, DV>;
   extern __shared__ __align__(16) unsigned char smem[];
   uint16_t* abuf = reinterpret_cast<uint16_t*>(smem);  // [2][ABUF]: packed Ainv planes of two steps
@@ -206,7 +210,7 @@ scan_bf16_kernel(const uint16_t* __restrict__ ainv_planes, const float* __restri
   const int c0 = cb * 16 * C::CW;
   const int row0 = wave * 16 + 4 * g;  // first of the 4 output rows of this lane
   // where those rows go in the stored state (FP8 plans: the paired row order)
-  const int srow0 = paired ? paired_row(row0) : row0;
+  const int srow0 = store_mode == kStorePairedBf16 ? paired_row(row0) : row0;
 
   const uint16_t* ainv_h = ainv_planes + bh * F1 * int64_t(2 * D * D);
   const float* bm_h = bm + bh * F1 * int64_t(D) * DV;
@@ -340,12 +344,21 @@ scan_bf16_kernel(const uint16_t* __restrict__ ainv_planes, const float* __restri
       // The states leave the chain only for the readout, which rounds their mean to bf16
       // for its MFMA: they are stored as bf16 in the readout's operand order (state_index),
       // a lane's 4 rows as 8 bytes, and kept out of the caches.
-      uint16_t* dst = xo_h + (frame_at(s) - 1) * int64_t(D) * DV;
+      if (store_mode == kStoreF32) {
+        // float32 and blocked (the backward pass, where the states meet cancellation)
+        float* dst = reinterpret_cast<float*>(backward ? xb : xf) + (bh * F + frame_at(s) - 1) * int64_t(D) * DV;
 #pragma unroll
-      for (int cw = 0; cw < C::CW; ++cw)
-        __builtin_nontemporal_store(
-            u32x2{pack_bf16x2(x[cw][0], x[cw][1]), pack_bf16x2(x[cw][2], x[cw][3])},
-            reinterpret_cast<u32x2*>(dst + state_index(srow0, c0 + 16 * cw + n, D)));
+        for (int cw = 0; cw < C::CW; ++cw)
+          *reinterpret_cast<float4*>(dst + blk_index(row0, c0 + 16 * cw + n, D)) =
+              make_float4(x[cw][0], x[cw][1], x[cw][2], x[cw][3]);
+      } else {
+        uint16_t* dst = xo_h + (frame_at(s) - 1) * int64_t(D) * DV;
+#pragma unroll
+        for (int cw = 0; cw < C::CW; ++cw)
+          __builtin_nontemporal_store(
+              u32x2{pack_bf16x2(x[cw][0], x[cw][1]), pack_bf16x2(x[cw][2], x[cw][3])},
+              reinterpret_cast<u32x2*>(dst + state_index(srow0, c0 + 16 * cw + n, D)));
+      }
     }
     if (s < F) {
 #pragma unroll
@@ -383,7 +396,8 @@ hipError_t launch_scan_t(const Problem& p, hipStream_t s, bool prepare) {
     const int64_t grid = ((nchains + kXcds - 1) / kXcds) * kXcds * C::NCB;
     hipLaunchKernelGGL(kern, dim3(unsigned(grid)), dim3(C::THREADS), C::LDS_BYTES, s,
                        reinterpret_cast<const uint16_t*>(p.ainv), p.bm, p.xf, p.xb, nchains, p.F,
-                       p.lam, grid, p.fp8 && D >= 64);
+                       p.lam, grid,
+                       p.states_f32 ? kStoreF32 : (p.fp8 && D >= 64) ? kStorePairedBf16 : kStoreBf16);
   } else {
     using C = ScanCfg<D, DV>;
     if (prepare) return hipSuccess;  // static LDS only

@@ -19,6 +19,9 @@ struct vda_plan_s {
   int timing_capacity;
   int timed_calls;
   hipEvent_t* timing_events;
+  // backward-pass workspace, allocated by the first vda_backward call
+  void* bwd_workspace;
+  size_t bwd_workspace_bytes;
 };
 
 namespace {
@@ -114,6 +117,7 @@ vda_status vda_plan_create(int64_t B, int64_t H, int64_t F, int64_t n, int64_t d
   p.lam = lambda;
   p.bf16 = (dtype != VDA_DTYPE_F32);  // FP8 inputs run the bfloat16 path after conversion
   p.fp8 = (dtype == VDA_DTYPE_FP8_E4M3);
+  p.states_f32 = false;
   p.ainv = p.bm = p.xf = p.xb = nullptr;
   plan->workspace = nullptr;
   plan->workspace_bytes = 0;
@@ -141,9 +145,12 @@ vda_status vda_plan_create(int64_t B, int64_t H, int64_t F, int64_t n, int64_t d
   plan->timing_capacity = 0;
   plan->timed_calls = 0;
   plan->timing_events = nullptr;
+  plan->bwd_workspace = nullptr;
+  plan->bwd_workspace_bytes = 0;
   // kernel attributes once, here, so that a forward pass makes no runtime call but launches
   if (vda::prepare_stats(p) != hipSuccess || vda::prepare_scan(p) != hipSuccess ||
-      vda::prepare_readout(p) != hipSuccess) {
+      vda::prepare_readout(p) != hipSuccess ||
+      (p.bf16 && !p.fp8 && vda::prepare_bwd_frames(p) != hipSuccess)) {
     (void)hipGetLastError();
     if (plan->workspace != nullptr) (void)hipFree(plan->workspace);
     delete plan;
@@ -164,6 +171,7 @@ vda_status vda_plan_destroy(vda_plan_t plan) {
   };
   free_timing(plan);
   if (plan->workspace != nullptr) check(hipFree(plan->workspace));
+  if (plan->bwd_workspace != nullptr) check(hipFree(plan->bwd_workspace));
   delete plan;
   return st;
 }
@@ -268,6 +276,172 @@ vda_status enqueue(vda_plan_t plan, unsigned stages, const void* q, const void* 
   return VDA_SUCCESS;
 }
 
+
+// Layout of the backward workspace (byte offsets, each 256-aligned).
+struct BwdLayout {
+  size_t ainv, dw, xf, xb, sf, sb, wt, db2, z, db2_text, z_text, total;
+};
+BwdLayout bwd_layout(const vda::Problem& p) {
+  const size_t BH = size_t(p.B) * size_t(p.H), F = size_t(p.F), d = size_t(p.d), dv = size_t(p.dv);
+  BwdLayout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += (bytes + 255) & ~size_t(255);
+    return at;
+  };
+  L.ainv = take(BH * (F + 1) * d * d * 4);
+  L.dw = take(BH * (F + 1) * d * dv * 4);
+  L.xf = take(BH * F * d * dv * 4);
+  L.xb = take(BH * F * d * dv * 4);
+  L.sf = take(BH * F * d * dv * 4);
+  L.sb = take(BH * F * d * dv * 4);
+  L.wt = take(BH * F * dv * d * 2);
+  L.db2 = take(BH * F * 2 * d * dv * 2);
+  L.z = take(BH * F * (2 * d + 2 * dv) * d * 2);
+  L.db2_text = take(BH * 2 * d * dv * 2);
+  L.z_text = take(BH * (2 * d + 2 * dv) * d * 2);
+  L.total = off;
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+vda_status vda_backward(vda_plan_t plan, const void* q, const void* k, const void* v,
+                        const void* text_k, const void* text_v, const void* d_out, void* d_q,
+                        void* d_k, void* d_v, void* d_text_k, void* d_text_v, void* stream) {
+  if (plan == nullptr) return VDA_ERROR_INVALID_VALUE;
+  const vda::Problem& p = plan->p;
+  if (!p.bf16 || p.fp8) return VDA_ERROR_NOT_SUPPORTED;
+  const size_t BH = size_t(p.B) * size_t(p.H);
+  const size_t tok = BH * size_t(p.F) * size_t(p.n), ttok = BH * size_t(p.T);
+  const size_t qk = tok * size_t(p.d) * 2, vo = tok * size_t(p.dv) * 2;
+  const size_t tkb = ttok * size_t(p.d) * 2, tvb = ttok * size_t(p.dv) * 2;
+  struct Arg {
+    const void* ptr;
+    size_t bytes;
+  } in[6] = {{q, qk}, {k, qk}, {v, vo}, {text_k, tkb}, {text_v, tvb}, {d_out, vo}},
+    outs[5] = {{d_q, qk}, {d_k, qk}, {d_v, vo}, {d_text_k, tkb}, {d_text_v, tvb}};
+  for (const Arg& a : in) {
+    if (a.bytes == 0) continue;
+    if (a.ptr == nullptr) return VDA_ERROR_INVALID_VALUE;
+    if (!aligned16(a.ptr)) return VDA_ERROR_MISALIGNED;
+  }
+  for (const Arg& a : outs) {
+    if (a.bytes == 0) continue;
+    if (a.ptr == nullptr) return VDA_ERROR_INVALID_VALUE;
+    if (!aligned16(a.ptr)) return VDA_ERROR_MISALIGNED;
+  }
+  // no output may overlap an input or another output
+  for (int i = 0; i < 5; ++i) {
+    if (outs[i].bytes == 0) continue;
+    const Range o{reinterpret_cast<uintptr_t>(outs[i].ptr), reinterpret_cast<uintptr_t>(outs[i].ptr) + outs[i].bytes};
+    for (const Arg& a : in)
+      if (a.bytes > 0 && overlaps(o, Range{reinterpret_cast<uintptr_t>(a.ptr), reinterpret_cast<uintptr_t>(a.ptr) + a.bytes}))
+        return VDA_ERROR_INVALID_VALUE;
+    for (int j = 0; j < i; ++j)
+      if (outs[j].bytes > 0 &&
+          overlaps(o, Range{reinterpret_cast<uintptr_t>(outs[j].ptr), reinterpret_cast<uintptr_t>(outs[j].ptr) + outs[j].bytes}))
+        return VDA_ERROR_INVALID_VALUE;
+  }
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return VDA_ERROR_DEVICE;
+  }
+  if (dev != plan->device) return VDA_ERROR_INVALID_VALUE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (BH == 0) return VDA_SUCCESS;
+  if (p.F == 0 || p.n == 0) {
+    // no output element: every gradient is zero (the text's included)
+    hipError_t e = hipSuccess;
+    if (tkb > 0) e = vda::launch_zero(d_text_k, tkb, s);
+    if (e == hipSuccess && tvb > 0) e = vda::launch_zero(d_text_v, tvb, s);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      return VDA_ERROR_DEVICE;
+    }
+    return VDA_SUCCESS;
+  }
+  const BwdLayout L = bwd_layout(p);
+  if (plan->bwd_workspace == nullptr) {
+    void* ws = nullptr;
+    if (hipMalloc(&ws, L.total) != hipSuccess || ws == nullptr) {
+      (void)hipGetLastError();
+      return VDA_ERROR_OUT_OF_MEMORY;
+    }
+    plan->bwd_workspace = ws;
+    plan->bwd_workspace_bytes = L.total;
+  }
+  unsigned char* w = static_cast<unsigned char*>(plan->bwd_workspace);
+  auto u16 = [&](size_t off) { return reinterpret_cast<uint16_t*>(w + off); };
+  auto f32 = [&](size_t off) { return reinterpret_cast<float*>(w + off); };
+
+  hipError_t e = hipSuccess;
+  hipEvent_t* tev = nullptr;
+  if (plan->timing_capacity > 0 && plan->timed_calls < plan->timing_capacity)
+    tev = plan->timing_events + size_t(plan->timed_calls) * kTimingEvents;
+  auto mark = [&](int slot) {
+    if (tev != nullptr && e == hipSuccess) e = hipEventRecord(tev[slot], s);
+  };
+  // 1. dW_f = Q_f^T dO_f: the statistics stage on (Q, dO) with no text (frame 0 is zero)
+  mark(kEvStatsBegin);
+  vda::Problem pw = p;
+  pw.T = 0;
+  pw.ainv = f32(L.ainv);
+  pw.bm = f32(L.dw);
+  e = vda::launch_stats(pw, q, d_out, nullptr, nullptr, s);
+  mark(kEvStatsEnd);
+  // 2. the forward states again, in float32 (the forward pass keeps them in bf16), and the
+  //    adjoint chains (twice the adjoints): the scan on (A^{-1} of the forward, dW), float32
+  //    states; then the per-frame terms
+  mark(kEvScanBegin);
+  vda::Problem px = p;
+  px.states_f32 = true;
+  px.xf = f32(L.xf);
+  px.xb = f32(L.xb);
+  if (e == hipSuccess) e = vda::launch_scan(px, s);
+  vda::Problem ps = p;
+  ps.states_f32 = true;
+  ps.bm = f32(L.dw);
+  ps.xf = f32(L.sf);
+  ps.xb = f32(L.sb);
+  if (e == hipSuccess) e = vda::launch_scan(ps, s);
+  vda::BwdProblem b{p, f32(L.xf), f32(L.xb), f32(L.sf), f32(L.sb), u16(L.wt), u16(L.db2), u16(L.z),
+                    u16(L.db2_text), u16(L.z_text)};
+  if (e == hipSuccess) e = vda::launch_bwd_frames(b, s);
+  mark(kEvScanEnd);
+  // 3. the gradient products: dQ = dO W^T, dV = [K K] [dB hi ; lo],
+  //    dK = [K K V V] [M hi ; M lo ; dB^T hi ; dB^T lo]
+  mark(kEvReadBegin);
+  vda::Problem pq = p;
+  pq.d = p.dv;
+  pq.dv = p.d;
+  pq.xf = pq.xb = f32(L.wt);
+  if (e == hipSuccess) e = vda::launch_readout(pq, d_out, d_q, s);
+  if (e == hipSuccess) e = vda::launch_grad_dv(p, k, u16(L.db2), d_v, s);
+  if (e == hipSuccess) e = vda::launch_grad_dk(p, k, v, u16(L.z), d_k, s);
+  if (p.T > 0) {
+    vda::Problem pt = p;
+    pt.F = 1;
+    pt.n = p.T;
+    if (e == hipSuccess) e = vda::launch_grad_dv(pt, text_k, u16(L.db2_text), d_text_v, s);
+    if (e == hipSuccess) e = vda::launch_grad_dk(pt, text_k, text_v, u16(L.z_text), d_text_k, s);
+  }
+  mark(kEvReadEnd);
+  if (tev != nullptr && e == hipSuccess) ++plan->timed_calls;
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return VDA_ERROR_DEVICE;
+  }
+  return VDA_SUCCESS;
+}
+
+}  // extern "C"
+
+namespace {
 }  // namespace
 
 extern "C" {

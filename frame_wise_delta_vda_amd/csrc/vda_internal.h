@@ -17,6 +17,7 @@ struct Problem {
   float lam;
   bool bf16;        // bfloat16 path: bfloat16 out and states (set for FP8 inputs as well)
   bool fp8;         // q, k, v and text are OCP FP8 e4m3 codes (bfloat16 path otherwise)
+  bool states_f32;  // bf16 path: the scan stores float32 blocked states (backward pass)
   int num_cus;      // compute units of the plan's device (sizes persistent grids)
   // workspace (float32), frame index 0 = text, 1..F = frames
   float* ainv;      // [BH][F+1][d][d]
@@ -36,6 +37,34 @@ struct GateWeights {
   const void* b_gate;
   const void* w_out;
 };
+// Backward pass: the forward problem (its workspace holds the saved statistics), the
+// forward states recomputed in float32 (xf32, xb32, blocked), the adjoint chains of the
+// scan run on (A^{-1}, Q^T dO) (sf: forward chain, sb: backward chain, float32 blocked,
+// both twice the adjoints), and the per-frame outputs in the readouts' state order (bf16):
+// wt = W^T [BH][F][dv*d], db2 = [dB hi ; lo] [BH][F][2d*dv],
+// z = [M hi ; M lo ; dB^T hi ; dB^T lo] [BH][F][(2d+2dv)*d], and the text's db2_text,
+// z_text [BH][...].
+struct BwdProblem {
+  Problem p;
+  const float* xf32;
+  const float* xb32;
+  const float* sf;
+  const float* sb;
+  uint16_t* wt;
+  uint16_t* db2;
+  uint16_t* z;
+  uint16_t* db2_text;
+  uint16_t* z_text;
+};
+hipError_t launch_bwd_frames(const BwdProblem& b, hipStream_t stream);
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream);
+hipError_t prepare_bwd_frames(const Problem& p);
+// The backward pass's gradient products, bf16 in and out, per frame:
+//   split_dv:  out (n x dv) = [K K] DB2,           DB2 a 2d x dv state (dB hi ; lo)
+//   split_dk:  out (n x d)  = [K K V V] Z,         Z a (2d + 2dv) x d state
+hipError_t launch_grad_dv(const Problem& p, const void* k, const void* state, void* out, hipStream_t stream);
+hipError_t launch_grad_dk(const Problem& p, const void* k, const void* v, const void* state, void* out,
+                          hipStream_t stream);
 // The readout followed by the gated epilogue (bfloat16 and FP8 plans).
 hipError_t launch_readout_gated(const Problem& p, const void* q, const GateWeights& gw, void* out,
                                 hipStream_t stream);

@@ -54,6 +54,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.vda_forward.restype = c_int
     lib.vda_forward_gated.argtypes = [c_vp] * 11
     lib.vda_forward_gated.restype = c_int
+    lib.vda_backward.argtypes = [c_vp] * 13
+    lib.vda_backward.restype = c_int
     lib.vda_forward_stages.argtypes = [c_vp, ctypes.c_uint] + [c_vp] * 7
     lib.vda_forward_stages.restype = c_int
     lib.vda_plan_destroy.argtypes = [c_vp]
@@ -127,6 +129,12 @@ def vda_forward_gated(plan, q, k, v, text_k, text_v, w_gate, b_gate, w_out, out,
     _check(load_library().vda_forward_gated(plan, _ptr(q), _ptr(k), _ptr(v), _ptr(text_k), _ptr(text_v),
                                             _ptr(w_gate), _ptr(b_gate), _ptr(w_out), _ptr(out),
                                             _stream(stream)), "vda_forward_gated")
+
+
+def vda_backward(plan, q, k, v, text_k, text_v, d_out, d_q, d_k, d_v, d_text_k, d_text_v, stream=None):
+    _check(load_library().vda_backward(plan, _ptr(q), _ptr(k), _ptr(v), _ptr(text_k), _ptr(text_v),
+                                       _ptr(d_out), _ptr(d_q), _ptr(d_k), _ptr(d_v), _ptr(d_text_k),
+                                       _ptr(d_text_v), _stream(stream)), "vda_backward")
 
 
 def vda_forward_stages(plan, stages, q, k, v, text_k, text_v, out, stream=None):
@@ -213,6 +221,15 @@ class Plan:
             out = self.out_like(q)
         vda_forward_gated(self.handle, q, k, v, text_k, text_v, w_gate, b_gate, w_out, out, stream)
         return out
+
+    def backward(self, q, k, v, text_k, text_v, d_out, grads=None, stream=None):
+        """Gradients (dq, dk, dv, d_text_k, d_text_v) of sum(d_out * O) after a forward call on
+        the same inputs (include/vda.h, vda_backward).  grads: optional output tensors."""
+        import torch
+        if grads is None:
+            grads = tuple(torch.empty_like(t) if t is not None else None for t in (q, k, v, text_k, text_v))
+        vda_backward(self.handle, q, k, v, text_k, text_v, d_out, *grads, stream=stream)
+        return grads
 
     def stages(self, stages, q=None, k=None, v=None, text_k=None, text_v=None, out=None, stream=None):
         vda_forward_stages(self.handle, stages, q, k, v, text_k, text_v, out, stream)

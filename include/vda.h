@@ -134,6 +134,33 @@ vda_status vda_forward_gated(vda_plan_t plan, const void* q, const void* k, cons
                              const void* text_k, const void* text_v, const void* w_gate,
                              const void* b_gate, const void* w_out, void* out, void* stream);
 
+/* Backward pass: the gradients of L = sum(d_out * O) with respect to q, k, v, text_k
+ * and text_v, where O is the output of vda_forward.  The pages train the branch (the
+ * aiezz page, section 03, and the laicaila page, "technical principles": bullet "three-
+ * stage training adaptation"), which needs them.  With A_f = lam I + K_f^T K_f and
+ * dW_f = Q_f^T dO_f, the two chains' adjoints run in the opposite directions with the same
+ * solves, U_f = A_f^{-1}(dW_f/2 + lam U_{f+1}) and V_f = A_f^{-1}(dW_f/2 + lam V_{f-1});
+ * then dB_f = U_f + V_f, dA_f = -(U_f X_fwd_f^T + V_f X_bwd_f^T),
+ * dK_f = V_f dB_f^T + K_f (dA_f + dA_f^T), dV_f = K_f dB_f, dQ_f = dO_f W_f^T, and the text
+ * gets the same terms from U_0 = A_0^{-1} lam (U_1 + V_F).
+ * The call reads the statistics and states that the last vda_forward (or
+ * vda_forward_gated) on this plan left in its workspace: run the forward pass first,
+ * with the same k, v, text_k, text_v, and keep the plan's workspace untouched in between.
+ *   d_out          [B][H][F][n][dv], the gradient of the output;
+ *   d_q, d_k, d_v, d_text_k, d_text_v: written, same layouts as q, k, v, text_k, text_v.
+ * All tensors are bfloat16.  Only bfloat16 plans are supported.  The first call on a plan
+ * allocates its backward workspace (hipMalloc, kept until vda_plan_destroy); later calls
+ * make no runtime call but kernel launches and may be captured.  Outputs may not overlap
+ * inputs or each other.  With no output element (F or n = 0) every gradient is zero.
+ * When timing is enabled (vda_plan_enable_timing) a backward call is recorded as one
+ * timed pass whose three spans are the Q^T dO statistics, the adjoint chains with the
+ * per-frame terms, and the gradient products.
+ * Errors: INVALID_VALUE, MISALIGNED, OUT_OF_MEMORY, DEVICE; NOT_SUPPORTED for float32 and
+ * FP8 plans. */
+vda_status vda_backward(vda_plan_t plan, const void* q, const void* k, const void* v,
+                        const void* text_k, const void* text_v, const void* d_out, void* d_q,
+                        void* d_k, void* d_v, void* d_text_k, void* d_text_v, void* stream);
+
 /* Per-stage timing of whole forward passes, for benchmarks.  After
  * vda_plan_enable_timing(plan, capacity) with capacity > 0, each of the next `capacity`
  * vda_forward calls brackets each stage's launch with HIP events on the stream it runs

@@ -17,6 +17,7 @@ def lib():
 def test_every_declared_symbol_is_exported(lib):
     names = vda.declared_functions()
     assert set(names) == {"vda_plan_create", "vda_forward", "vda_forward_stages", "vda_forward_gated",
+                          "vda_backward",
                           "vda_plan_destroy",
                           "vda_plan_workspace_bytes", "vda_status_string", "vda_debug_workspace",
                           "vda_plan_enable_timing", "vda_plan_timings"}
@@ -65,6 +66,7 @@ def test_null_handles(lib):
     assert lib.vda_forward(None, *([None] * 7)) == binding.VDA_ERROR_INVALID_VALUE
     assert lib.vda_forward_stages(None, 7, *([None] * 7)) == binding.VDA_ERROR_INVALID_VALUE
     assert lib.vda_forward_gated(None, *([None] * 10)) == binding.VDA_ERROR_INVALID_VALUE
+    assert lib.vda_backward(None, *([None] * 12)) == binding.VDA_ERROR_INVALID_VALUE
     p = ctypes.c_void_p()
     assert lib.vda_debug_workspace(None, ctypes.byref(p), None, None, None) == \
         binding.VDA_ERROR_INVALID_VALUE
