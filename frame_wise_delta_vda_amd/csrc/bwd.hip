@@ -68,51 +68,62 @@ bwd_frame_kernel(const float* __restrict__ xf, const float* __restrict__ xb,
   const float* SF = sf + base;
   const float* SB = sb + base;
   const int tid = threadIdx.x;
-  auto dB = [&](int i, int c) -> float {
-    const int e = blk_index(i, c, D);
-    return 0.5f * (SB[e] + SF[e]);
-  };
 
-  // 1. element-wise outputs straight from the (cached) inputs
-  for (int qc = tid; qc < D * DV / 8; qc += kThreads) {
-    int r0, c;
-    uint32_t w[4];
-    chunk_rc<DV>(qc, r0, c);  // WT: rows r0.. are value features, column c an input feature
-#pragma unroll
-    for (int m = 0; m < 8; m += 2) {
-      const int e0 = blk_index(c, r0 + m, D), e1 = blk_index(c, r0 + m + 1, D);
-      w[m / 2] = pack_bf16x2(0.5f * (XF[e0] + XB[e0]), 0.5f * (XF[e1] + XB[e1]));
-    }
-    reinterpret_cast<uint4*>(wt + base)[qc] = make_uint4(w[0], w[1], w[2], w[3]);
-  }
+  // 1. element-wise outputs straight from the (cached) inputs.  In the blocked layout four
+  //    consecutive rows of a column are one float4, so outputs that run along a row (WT and
+  //    the dB^T rows of Z: 8 consecutive value features of one input feature) are made for
+  //    4 rows x 8 columns at a time, and those that run down a column (DB2) 8 rows at a time.
+  auto chunk_of = [](int row0, int col, int R) -> int {  // inverse of chunk_rc for an R-row state
+    return (((col >> 4) * (R / 32) + (row0 >> 5)) * 4 + ((row0 & 31) >> 3)) * 16 + (col & 15);
+  };
   uint16_t* dbf = db2 + fr * int64_t(2 * D) * DV;
-  for (int qc = tid; qc < 2 * D * DV / 8; qc += kThreads) {
-    int r0, c;
-    chunk_rc<2 * D>(qc, r0, c);  // rows 0..D-1: dB hi, D..2D-1: dB lo
-    const bool lo = r0 >= D;
-    const int i0 = lo ? r0 - D : r0;
-    uint32_t w[4];
-#pragma unroll
-    for (int m = 0; m < 8; m += 2) {
-      const float a = dB(i0 + m, c), b = dB(i0 + m + 1, c);
-      w[m / 2] = lo ? pack_bf16x2(lo_part(a), lo_part(b)) : pack_bf16x2(a, b);
-    }
-    reinterpret_cast<uint4*>(dbf)[qc] = make_uint4(w[0], w[1], w[2], w[3]);
-  }
   uint16_t* zf = z + fr * int64_t(C::ZR) * D;
-  for (int qc = tid; qc < C::ZR * D / 8; qc += kThreads) {
-    int r0, i;
-    chunk_rc<C::ZR>(qc, r0, i);  // rows 2D + c (hi) and 2D + DV + c (lo): dB^T[c][i] = dB[i][c]
-    if (r0 < 2 * D) continue;
-    const bool lo = r0 >= 2 * D + DV;
-    const int c0 = r0 - 2 * D - (lo ? DV : 0);
-    uint32_t w[4];
+  for (int u = tid; u < (D / 4) * (DV / 8); u += kThreads) {
+    const int i0 = 4 * (u % (D / 4)), c0 = 8 * (u / (D / 4));
+    float4 xf4[8], xb4[8], sf4[8], sb4[8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const int e = blk_index(i0, c0 + m, D) / 4;
+      xf4[m] = reinterpret_cast<const float4*>(XF)[e];
+      xb4[m] = reinterpret_cast<const float4*>(XB)[e];
+      sf4[m] = reinterpret_cast<const float4*>(SF)[e];
+      sb4[m] = reinterpret_cast<const float4*>(SB)[e];
+    }
+    auto comp = [](const float4& a, int r) { return r == 0 ? a.x : r == 1 ? a.y : r == 2 ? a.z : a.w; };
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      uint32_t w[4], h[4], l[4];
+#pragma unroll
+      for (int m = 0; m < 8; m += 2) {
+        w[m / 2] = pack_bf16x2(0.5f * (comp(xf4[m], r) + comp(xb4[m], r)),
+                               0.5f * (comp(xf4[m + 1], r) + comp(xb4[m + 1], r)));
+        const float a = 0.5f * (comp(sb4[m], r) + comp(sf4[m], r));
+        const float b = 0.5f * (comp(sb4[m + 1], r) + comp(sf4[m + 1], r));
+        h[m / 2] = pack_bf16x2(a, b);
+        l[m / 2] = pack_bf16x2(lo_part(a), lo_part(b));
+      }
+      // WT: rows c0.. (value features) of column i0 + r; Z rows 2D + c0.. (dB^T hi) and
+      // 2D + DV + c0.. (lo) of column i0 + r
+      reinterpret_cast<uint4*>(wt + base)[chunk_of(c0, i0 + r, DV)] = make_uint4(w[0], w[1], w[2], w[3]);
+      reinterpret_cast<uint4*>(zf)[chunk_of(2 * D + c0, i0 + r, C::ZR)] = make_uint4(h[0], h[1], h[2], h[3]);
+      reinterpret_cast<uint4*>(zf)[chunk_of(2 * D + DV + c0, i0 + r, C::ZR)] = make_uint4(l[0], l[1], l[2], l[3]);
+    }
+  }
+  for (int u = tid; u < (D / 8) * DV; u += kThreads) {  // DB2: rows i0..i0+7 of column c, hi and lo
+    const int i0 = 8 * (u % (D / 8)), c = u / (D / 8);
+    const int e0 = blk_index(i0, c, D) / 4, e1 = blk_index(i0 + 4, c, D) / 4;
+    const float4 s0 = reinterpret_cast<const float4*>(SB)[e0], t0 = reinterpret_cast<const float4*>(SF)[e0];
+    const float4 s1 = reinterpret_cast<const float4*>(SB)[e1], t1 = reinterpret_cast<const float4*>(SF)[e1];
+    const float v[8] = {0.5f * (s0.x + t0.x), 0.5f * (s0.y + t0.y), 0.5f * (s0.z + t0.z), 0.5f * (s0.w + t0.w),
+                        0.5f * (s1.x + t1.x), 0.5f * (s1.y + t1.y), 0.5f * (s1.z + t1.z), 0.5f * (s1.w + t1.w)};
+    uint32_t h[4], l[4];
 #pragma unroll
     for (int m = 0; m < 8; m += 2) {
-      const float a = dB(i, c0 + m), b = dB(i, c0 + m + 1);
-      w[m / 2] = lo ? pack_bf16x2(lo_part(a), lo_part(b)) : pack_bf16x2(a, b);
+      h[m / 2] = pack_bf16x2(v[m], v[m + 1]);
+      l[m / 2] = pack_bf16x2(lo_part(v[m]), lo_part(v[m + 1]));
     }
-    reinterpret_cast<uint4*>(zf)[qc] = make_uint4(w[0], w[1], w[2], w[3]);
+    reinterpret_cast<uint4*>(dbf)[chunk_of(i0, c, 2 * D)] = make_uint4(h[0], h[1], h[2], h[3]);
+    reinterpret_cast<uint4*>(dbf)[chunk_of(D + i0, c, 2 * D)] = make_uint4(l[0], l[1], l[2], l[3]);
   }
 
   // 2. P = S_bwd X_fwd^T + S_fwd X_bwd^T (D x D), a PB x PB block per thread, in two passes

@@ -501,6 +501,140 @@ readout_parts_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict
   }
 }
 
+// dK product, staged: out_f = [K K V V] Z_f with Z_f the (2 D1 + 2 D2) x DV state (M hi ; M lo ;
+// dB^T hi ; dB^T lo).  The state is four times as deep as a forward state, so each wave
+// keeps the fragments of a quarter of the output features; the workgroup loads each
+// 64-token tile of K and V once (whole 16-byte pieces, coalesced) into LDS, and every
+// wave reads its operands from there (double-buffered, one barrier per tile).
+template <int D1, int D2, int DV>
+struct ReadStaged {
+  static constexpr int KS1 = D1 / 32, KS2 = D2 / 32;
+  static constexpr int KS = 2 * KS1 + 2 * KS2;
+  static constexpr int DS = 32 * KS;
+  static constexpr int TT = 64;                   // tokens per tile
+  static constexpr int FH = DV / 4;               // output features per wave
+  static constexpr int NBW = FH / 16;
+  static constexpr int RW = D1 + D2 + 8;          // bf16 per LDS token row (K then V, padded)
+  static constexpr int BUF = TT * RW;             // bf16 per tile buffer
+  static constexpr int PIECES = TT * (D1 + D2) / 8;  // 16-byte pieces per tile
+  static constexpr int PPT = PIECES / kThreads;   // per thread
+  static constexpr int OWROW = FH + 8;
+  static constexpr int OCH = FH / 8;
+  static constexpr int ORPI = 64 / OCH < 16 ? 64 / OCH : 16;
+  static constexpr int OST = 16 / ORPI;
+  static constexpr int OW_BYTES = 16 * OWROW * 2;
+  static constexpr int LDS_BYTES = 2 * BUF * 2 + 4 * OW_BYTES;
+  static_assert(NBW >= 1 && PIECES % kThreads == 0, "shape outside the staged product");
+};
+
+template <int D1, int D2, int DV>
+__global__ void __launch_bounds__(kThreads, 2)
+readout_staged_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ q2,
+                      const uint16_t* __restrict__ st, uint16_t* __restrict__ out, int64_t n,
+                      int64_t tiles_per_frame, int64_t splits, int64_t tiles_per_split,
+                      int64_t head_blocks, int64_t tail_splits, int64_t tail_tiles_per_split) {
+  using C = ReadStaged<D1, D2, DV>;
+  extern __shared__ __align__(16) unsigned char smem[];
+  uint16_t* buf = reinterpret_cast<uint16_t*>(smem);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  uint16_t* ow = reinterpret_cast<uint16_t*>(smem + 2 * C::BUF * 2 + wave * C::OW_BYTES);
+  const int c16 = lane & 15, g4 = lane >> 4;
+  int64_t frame, t_first, tps;
+  if (blockIdx.x < head_blocks) {
+    frame = blockIdx.x / splits;
+    t_first = (blockIdx.x % splits) * tiles_per_split;
+    tps = tiles_per_split;
+  } else {
+    const int64_t i = blockIdx.x - head_blocks;
+    frame = head_blocks / splits + i / tail_splits;
+    t_first = (i % tail_splits) * tail_tiles_per_split;
+    tps = tail_tiles_per_split;
+  }
+  const int64_t t_last = (t_first + tps < tiles_per_frame) ? t_first + tps : tiles_per_frame;
+  if (t_first >= t_last) return;
+
+  uint4 wfr[C::NBW][C::KS];
+  {
+    const uint4* sp = reinterpret_cast<const uint4*>(st + frame * int64_t(C::DS) * DV) + lane;
+#pragma unroll
+    for (int jb = 0; jb < C::NBW; ++jb)
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) wfr[jb][ks] = sp[((wave * C::NBW + jb) * C::KS + ks) * 64];
+  }
+  // tile loads: piece p of a tile is token p / (PR) and 16 bytes (p % PR) of its K (first
+  // D1 / 8 pieces) or V row; loads past the frame's last token return zeros
+  constexpr int PR = (D1 + D2) / 8;  // pieces per token
+  auto load_tile = [&](int64_t tile, uint4 (&r)[C::PPT]) {
+    const int64_t tok0 = tile * C::TT;
+    const int64_t left = n - tok0;
+    const uint32_t rows = uint32_t(left < 0 ? 0 : (left < C::TT ? left : C::TT));
+    const auto r1 = make_rsrc(q1 + (frame * n + tok0) * D1, rows * D1 * 2);
+    const auto r2 = make_rsrc(q2 + (frame * n + tok0) * D2, rows * D2 * 2);
+#pragma unroll
+    for (int i = 0; i < C::PPT; ++i) {
+      const int p = i * kThreads + tid, t = p / PR, c = p % PR;
+      r[i] = c < D1 / 8 ? buffer_load16(r1, uint32_t((t * D1 + 8 * c) * 2))
+                        : buffer_load16(r2, uint32_t((t * D2 + 8 * (c - D1 / 8)) * 2));
+    }
+  };
+  auto store_tile = [&](int b, const uint4 (&r)[C::PPT]) {
+#pragma unroll
+    for (int i = 0; i < C::PPT; ++i) {
+      const int p = i * kThreads + tid, t = p / PR, c = p % PR;
+      *reinterpret_cast<uint4*>(buf + b * C::BUF + t * C::RW + 8 * c) = r[i];
+    }
+  };
+  uint4 ra[C::PPT];
+  load_tile(t_first, ra);
+  store_tile(0, ra);
+  if (t_first + 1 < t_last) load_tile(t_first + 1, ra);
+  __syncthreads();
+
+  for (int64_t tile = t_first; tile < t_last; ++tile) {
+    const int b = int((tile - t_first) & 1);
+    const uint16_t* tb = buf + b * C::BUF;
+#pragma unroll
+    for (int tg = 0; tg < 4; ++tg) {  // 16-token groups of the tile
+      uint4 qf[C::KS1 + C::KS2];
+#pragma unroll
+      for (int ks = 0; ks < C::KS1 + C::KS2; ++ks)
+        qf[ks] = *reinterpret_cast<const uint4*>(tb + (16 * tg + c16) * C::RW + 32 * ks + 8 * g4);
+#pragma unroll
+      for (int jb = 0; jb < C::NBW; ++jb) {
+        f32x4 acc = f32x4{};
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) {
+          // state k-steps: K (hi rows), K (lo rows), V (hi), V (lo)
+          const int qi = ks < 2 * C::KS1 ? ks % C::KS1 : C::KS1 + (ks - 2 * C::KS1) % C::KS2;
+          acc = mfma16_bf16(wfr[jb][ks], qf[qi], acc);
+        }
+        *reinterpret_cast<uint2*>(ow + c16 * C::OWROW + 16 * jb + 4 * g4) =
+            make_uint2(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]));
+      }
+      const int64_t tok0 = tile * C::TT + 16 * tg;
+      const int64_t left = n - tok0;
+      const uint32_t rows = uint32_t(left < 0 ? 0 : (left < 16 ? left : 16));
+      const auto rs = make_rsrc(out + (frame * n + tok0) * DV, rows * DV * 2);
+      const int orow = lane / C::OCH, och = lane % C::OCH;
+      if (orow < C::ORPI) {
+#pragma unroll
+        for (int j = 0; j < C::OST; ++j) {
+          const int r = orow + j * C::ORPI;
+          buffer_store16<kCacheStreamOut>(rs, uint32_t(r * DV * 2 + wave * C::FH * 2 + och * 16),
+                                          *reinterpret_cast<const uint4*>(ow + r * C::OWROW + och * 8));
+        }
+      }
+    }
+    // the next tile (already in registers) into the other buffer, the one after into registers
+    if (tile + 1 < t_last) {
+      store_tile(b ^ 1, ra);
+      if (tile + 2 < t_last) load_tile(tile + 2, ra);
+    }
+    __syncthreads();
+  }
+}
+
 // smallest output-feature split whose fragments fit 32 x 16 bytes per lane
 template <int KS, int DV>
 constexpr int parts_wf() {
@@ -659,6 +793,23 @@ hipError_t launch_readout_gated_t(const Problem& p, const void* q, const GateWei
   return hipGetLastError();
 }
 
+template <int D1, int D2, int DV>
+hipError_t launch_staged_t(const Problem& p, const void* q1, const void* q2, const void* state, void* out,
+                           hipStream_t s, bool prepare) {
+  using C = ReadStaged<D1, D2, DV>;
+  auto kern = readout_staged_kernel<D1, D2, DV>;
+  if (prepare)
+    return C::LDS_BYTES > 65536 ? hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                      hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES)
+                                : hipSuccess;
+  const ReadGrid gr = readout_grid(p.B * p.H * p.F, (p.n + C::TT - 1) / C::TT, p.num_cus);
+  hipLaunchKernelGGL(kern, dim3(unsigned(gr.grid)), dim3(kThreads), C::LDS_BYTES, s,
+                     static_cast<const uint16_t*>(q1), static_cast<const uint16_t*>(q2),
+                     static_cast<const uint16_t*>(state), static_cast<uint16_t*>(out), p.n, gr.tpf,
+                     gr.splits, gr.tps, gr.head_blocks, gr.tail_splits, gr.tail_tps);
+  return hipGetLastError();
+}
+
 template <int D1, int R1, int D2, int R2, int DV>
 hipError_t launch_parts_t(const Problem& p, const void* q1, const void* q2, const void* state, void* out,
                           hipStream_t s) {
@@ -726,6 +877,11 @@ hipError_t launch_grad_dv(const Problem& p, const void* k, const void* state, vo
 
 hipError_t launch_grad_dk(const Problem& p, const void* k, const void* v, const void* state, void* out,
                           hipStream_t s) {
+  // d = 128: the staged product (a quarter of the output features per wave); narrower
+  // outputs keep every operand in the waves' own registers
+  if (p.d == 128 && p.dv == 128) return launch_staged_t<128, 128, 128>(p, k, v, state, out, s, false);
+  if (p.d == 128 && p.dv == 64) return launch_staged_t<128, 64, 128>(p, k, v, state, out, s, false);
+  if (p.d == 128 && p.dv == 32) return launch_staged_t<128, 32, 128>(p, k, v, state, out, s, false);
 #define VDA_CASE(DD, VV) \
   if (p.d == DD && p.dv == VV) return launch_parts_t<DD, 2, VV, 2, DD>(p, k, v, state, out, s);
   VDA_CASE(32, 32) VDA_CASE(32, 64) VDA_CASE(32, 128)
@@ -733,6 +889,17 @@ hipError_t launch_grad_dk(const Problem& p, const void* k, const void* v, const 
   VDA_CASE(128, 32) VDA_CASE(128, 64) VDA_CASE(128, 128)
 #undef VDA_CASE
   return hipErrorInvalidValue;
+}
+
+}  // namespace vda
+
+namespace vda {
+
+hipError_t prepare_grad(const Problem& p) {
+  if (p.d == 128 && p.dv == 128) return launch_staged_t<128, 128, 128>(p, nullptr, nullptr, nullptr, nullptr, nullptr, true);
+  if (p.d == 128 && p.dv == 64) return launch_staged_t<128, 64, 128>(p, nullptr, nullptr, nullptr, nullptr, nullptr, true);
+  if (p.d == 128 && p.dv == 32) return launch_staged_t<128, 32, 128>(p, nullptr, nullptr, nullptr, nullptr, nullptr, true);
+  return hipSuccess;
 }
 
 }  // namespace vda

@@ -150,7 +150,7 @@ vda_status vda_plan_create(int64_t B, int64_t H, int64_t F, int64_t n, int64_t d
   // kernel attributes once, here, so that a forward pass makes no runtime call but launches
   if (vda::prepare_stats(p) != hipSuccess || vda::prepare_scan(p) != hipSuccess ||
       vda::prepare_readout(p) != hipSuccess ||
-      (p.bf16 && !p.fp8 && vda::prepare_bwd_frames(p) != hipSuccess)) {
+      (p.bf16 && !p.fp8 && (vda::prepare_bwd_frames(p) != hipSuccess || vda::prepare_grad(p) != hipSuccess))) {
     (void)hipGetLastError();
     if (plan->workspace != nullptr) (void)hipFree(plan->workspace);
     delete plan;

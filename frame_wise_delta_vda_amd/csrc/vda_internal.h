@@ -63,6 +63,7 @@ hipError_t prepare_bwd_frames(const Problem& p);
 //   split_dv:  out (n x dv) = [K K] DB2,           DB2 a 2d x dv state (dB hi ; lo)
 //   split_dk:  out (n x d)  = [K K V V] Z,         Z a (2d + 2dv) x d state
 hipError_t launch_grad_dv(const Problem& p, const void* k, const void* state, void* out, hipStream_t stream);
+hipError_t prepare_grad(const Problem& p);
 hipError_t launch_grad_dk(const Problem& p, const void* k, const void* v, const void* state, void* out,
                           hipStream_t stream);
 // The readout followed by the gated epilogue (bfloat16 and FP8 plans).
