@@ -38,12 +38,11 @@ __device__ __forceinline__ float lo_part(float x) { return x - bf16_bits_to_f32(
 
 template <int D, int DV>
 struct BwdFrame {
-  static constexpr int LROW = D + 4;              // floats per LDS row: row c holds column c of a D x DV matrix
-  static constexpr int MAT = DV * LROW;
+  static constexpr int TR = D + 8;                // bf16 per LDS plane row (row c: value feature c)
   static constexpr int PROW = D + 4;              // floats per LDS row of P (D x D)
-  static constexpr int LDS_BYTES = cmax(2 * MAT * 4, D * PROW * 4);
-  static constexpr int PB = D / 16;               // P block side per thread (16 x 16 threads)
+  static constexpr int LDS_BYTES = cmax(4 * DV * TR * 2, D * PROW * 4);
   static constexpr int ZR = 2 * D + 2 * DV;       // rows of Z: M hi, M lo, dB^T hi, dB^T lo
+  static_assert(D % 32 == 0 && DV % 16 == 0, "P tiles of 32 x 32, k-steps of 16");
 };
 
 // One workgroup per video frame.  Inputs are float32 and blocked (blk_index): the forward
@@ -59,8 +58,6 @@ bwd_frame_kernel(const float* __restrict__ xf, const float* __restrict__ xb,
                  uint16_t* __restrict__ wt, uint16_t* __restrict__ db2, uint16_t* __restrict__ z) {
   using C = BwdFrame<D, DV>;
   extern __shared__ __align__(16) unsigned char smem[];
-  float* L1 = reinterpret_cast<float*>(smem);
-  float* L2 = L1 + C::MAT;
   const int64_t fr = blockIdx.x;
   const int64_t base = fr * int64_t(D) * DV;
   const float* XF = xf + base;
@@ -126,45 +123,81 @@ bwd_frame_kernel(const float* __restrict__ xf, const float* __restrict__ xb,
     reinterpret_cast<uint4*>(dbf)[chunk_of(D + i0, c, 2 * D)] = make_uint4(l[0], l[1], l[2], l[3]);
   }
 
-  // 2. P = S_bwd X_fwd^T + S_fwd X_bwd^T (D x D), a PB x PB block per thread, in two passes
-  //    through LDS (each pass holds two float32 matrices, transposed: row c = column c)
-  auto load_t = [&](const float* M, float* L) {
+  // 2. P = S_bwd X_fwd^T + S_fwd X_bwd^T (D x D) on the 32x32x16 bf16 MFMA with split
+  //    operands (S = S_hi + S_lo, X likewise; S_hi X_hi + S_hi X_lo + S_lo X_hi leaves an
+  //    error of order 2^-16 of the products, as in the scan), in two passes, each with the
+  //    hi / lo planes of one S and one X in LDS laid out value-feature-major ([c][i]): the
+  //    operands (8 consecutive value features of one row of S or X) are then two
+  //    transposing reads, as in the statistics kernel.  Wave w owns the 32-row block w of
+  //    P when D = 128 (the 32-column tiles of all rows otherwise, split over the waves).
+  constexpr int TR = C::TR;
+  constexpr int PL = DV * TR;  // bf16 per plane
+  uint16_t* pl = reinterpret_cast<uint16_t*>(smem);  // [S hi, S lo, X hi, X lo]
+  auto load_planes = [&](const float* M, uint16_t* hi, uint16_t* lo) {
     for (int g = tid; g < D * DV / 4; g += kThreads) {
       const int c15 = g & 15, t = g >> 4, q4 = t & 3, u = t >> 2;
       const int i = (u % (D / 16)) * 16 + q4 * 4, c = (u / (D / 16)) * 16 + c15;
-      *reinterpret_cast<float4*>(L + c * C::LROW + i) = reinterpret_cast<const float4*>(M)[g];
+      const float4 x = reinterpret_cast<const float4*>(M)[g];  // rows i..i+3 of column c
+      uint32_t h0, l0, h1, l1;
+      split_bf16x2(x.x, x.y, h0, l0);
+      split_bf16x2(x.z, x.w, h1, l1);
+      *reinterpret_cast<uint2*>(hi + c * TR + i) = make_uint2(h0, h1);
+      *reinterpret_cast<uint2*>(lo + c * TR + i) = make_uint2(l0, l1);
     }
   };
-  const int bi = (tid >> 4) * C::PB, bj = (tid & 15) * C::PB;
-  float p[C::PB][C::PB];
+  const int lane = tid & 63, wave = tid >> 6;
+  const int fr_off = (8 * (lane >> 5) + ((lane & 15) >> 2)) * TR + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  auto frag = [&](const uint16_t* plane, int k0, int f0) -> uint4 {
+    typedef short v4s __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) v4s* lds_v4s;
+    const uint16_t* q = plane + k0 * TR + fr_off + f0;
+    const v4s x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(q));
+    const v4s y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(q + 4 * TR));
+    const uint2 xl = __builtin_bit_cast(uint2, x), yl = __builtin_bit_cast(uint2, y);
+    return make_uint4(xl.x, xl.y, yl.x, yl.y);
+  };
+  constexpr int NT = D / 32;              // 32 x 32 tiles per side of P
+  constexpr int TPW = NT * NT / 4 > 0 ? NT * NT / 4 : 1;  // tiles per wave
+  f32x16 acc[TPW];
 #pragma unroll
-  for (int a = 0; a < C::PB; ++a)
-#pragma unroll
-    for (int b = 0; b < C::PB; ++b) p[a][b] = 0.0f;
+  for (int t = 0; t < TPW; ++t) acc[t] = f32x16{};
+  auto tile_of = [&](int t, int& ti, int& tj) {  // tile t of this wave
+    const int idx = wave * TPW + t;
+    ti = idx / NT;
+    tj = idx % NT;
+  };
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
-    load_t(pass == 0 ? SB : SF, L1);
-    load_t(pass == 0 ? XF : XB, L2);
+    load_planes(pass == 0 ? SB : SF, pl, pl + PL);
+    load_planes(pass == 0 ? XF : XB, pl + 2 * PL, pl + 3 * PL);
     __syncthreads();
-    for (int c = 0; c < DV; ++c) {
-      float u[C::PB], xv[C::PB];
+    if (wave * TPW < NT * NT) {
+      for (int k0 = 0; k0 < DV; k0 += 16) {
 #pragma unroll
-      for (int a = 0; a < C::PB; ++a) {
-        u[a] = L1[c * C::LROW + bi + a];
-        xv[a] = L2[c * C::LROW + bj + a];
+        for (int t = 0; t < TPW; ++t) {
+          int ti, tj;
+          tile_of(t, ti, tj);
+          const uint4 sh = frag(pl, k0, 32 * ti), sl = frag(pl + PL, k0, 32 * ti);
+          const uint4 xh = frag(pl + 2 * PL, k0, 32 * tj), xl = frag(pl + 3 * PL, k0, 32 * tj);
+          acc[t] = mfma32_bf16(sh, xh, acc[t]);
+          acc[t] = mfma32_bf16(sh, xl, acc[t]);
+          acc[t] = mfma32_bf16(sl, xh, acc[t]);
+        }
       }
-#pragma unroll
-      for (int a = 0; a < C::PB; ++a)
-#pragma unroll
-        for (int b = 0; b < C::PB; ++b) p[a][b] = __builtin_fmaf(u[a], xv[b], p[a][b]);
     }
     __syncthreads();
   }
   float* LP = reinterpret_cast<float*>(smem);
+  if (wave * TPW < NT * NT) {
 #pragma unroll
-  for (int a = 0; a < C::PB; ++a)
+    for (int t = 0; t < TPW; ++t) {
+      int ti, tj;
+      tile_of(t, ti, tj);
 #pragma unroll
-    for (int b = 0; b < C::PB; ++b) LP[(bi + a) * C::PROW + bj + b] = p[a][b];
+      for (int e = 0; e < 16; ++e)
+        LP[(32 * ti + mfma32_row(e, lane)) * C::PROW + 32 * tj + (lane & 31)] = acc[t][e];
+    }
+  }
   __syncthreads();
 
   // 3. Z rows 0..2D-1: M = dA + dA^T = -(P + P^T) / 2, hi then lo
