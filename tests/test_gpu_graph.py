@@ -60,3 +60,50 @@ def test_forward_replays_in_a_graph(idx, over):
     assert not torch.equal(ref2.view(ints), eager.view(ints))
     del g
     plan.close()
+
+
+def test_gated_forward_and_backward_replay_in_graphs():
+    """vda_forward_gated and vda_backward (after its first call, which allocates the backward
+    workspace) launch kernels only, so each can be captured and replayed."""
+    import numpy as np
+    w = W.WORKLOADS[3].replace(name="graph_gated_bwd", H=2, F=4, n=200, T=20)
+    say("[gpu] graph replay gated + backward")
+    dev = to_device(w, W.full_storage(w, threads=1))
+    plan = binding.Plan(w.B, w.H, w.F, w.n, w.d, w.dv, w.T, w.lam, w.dtype)
+    g = W.gate_weights(w)
+    bits = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    wg, wo = bits(g["w_gate"]), bits(g["w_out"])
+    bg = torch.from_numpy(np.ascontiguousarray(g["b_gate"])).cuda()
+    args = (dev["q"], dev["k"], dev["v"], dev["text_k"], dev["text_v"])
+    y_eager = plan.forward_gated(*args, wg, bg, wo)
+    d_out = torch.randn(w.shapes()["out"], generator=torch.Generator().manual_seed(3)).to(torch.bfloat16).cuda()
+    plan.forward(*args, torch.empty_like(y_eager))
+    grads_eager = [t.clone() for t in plan.backward(*args, d_out)]  # first call allocates
+    torch.cuda.synchronize()
+
+    y = torch.empty_like(y_eager)
+    grads = tuple(torch.empty_like(t) for t in grads_eager)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        plan.forward_gated(*args, wg, bg, wo, out=y)
+        plan.backward(*args, d_out, grads=grads)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        # the gated pass writes the same statistics and states the backward pass reads
+        plan.forward_gated(*args, wg, bg, wo, out=y)
+        plan.backward(*args, d_out, grads=grads)
+    for i in range(3):
+        y.zero_()
+        for t in grads:
+            t.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), y_eager.view(torch.int16)), f"replay {i}"
+        for a, b in zip(grads, grads_eager):
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"replay {i}"
+    del graph
+    plan.close()
