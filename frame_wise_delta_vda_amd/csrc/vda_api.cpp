@@ -22,6 +22,9 @@ struct vda_plan_s {
   // backward-pass workspace, allocated by the first vda_backward call
   void* bwd_workspace;
   size_t bwd_workspace_bytes;
+  // set once a forward pass (whole, or its statistics stage) has been enqueued: the backward
+  // pass reads the statistics it leaves in the workspace
+  bool has_statistics;
 };
 
 namespace {
@@ -147,6 +150,7 @@ vda_status vda_plan_create(int64_t B, int64_t H, int64_t F, int64_t n, int64_t d
   plan->timing_events = nullptr;
   plan->bwd_workspace = nullptr;
   plan->bwd_workspace_bytes = 0;
+  plan->has_statistics = false;
   // kernel attributes once, here, so that a forward pass makes no runtime call but launches
   if (vda::prepare_stats(p) != hipSuccess || vda::prepare_scan(p) != hipSuccess ||
       vda::prepare_readout(p) != hipSuccess ||
@@ -177,7 +181,7 @@ vda_status vda_plan_destroy(vda_plan_t plan) {
 }
 
 size_t vda_plan_workspace_bytes(vda_plan_t plan) {
-  return plan == nullptr ? 0 : plan->workspace_bytes;
+  return plan == nullptr ? 0 : plan->workspace_bytes + plan->bwd_workspace_bytes;
 }
 
 vda_status vda_debug_workspace(vda_plan_t plan, const float** ainv, const float** bm,
@@ -273,6 +277,7 @@ vda_status enqueue(vda_plan_t plan, unsigned stages, const void* q, const void* 
     (void)hipGetLastError();
     return VDA_ERROR_DEVICE;
   }
+  if (do_stats) plan->has_statistics = true;
   return VDA_SUCCESS;
 }
 
@@ -317,6 +322,9 @@ vda_status vda_backward(vda_plan_t plan, const void* q, const void* k, const voi
   if (!p.bf16 || p.fp8) return VDA_ERROR_NOT_SUPPORTED;
   const size_t BH = size_t(p.B) * size_t(p.H);
   const size_t tok = BH * size_t(p.F) * size_t(p.n), ttok = BH * size_t(p.T);
+  // the statistics of a forward pass must be in the workspace (problems with no output
+  // element need none)
+  if (tok > 0 && !plan->has_statistics) return VDA_ERROR_INVALID_VALUE;
   const size_t qk = tok * size_t(p.d) * 2, vo = tok * size_t(p.dv) * 2;
   const size_t tkb = ttok * size_t(p.d) * 2, tvb = ttok * size_t(p.dv) * 2;
   struct Arg {

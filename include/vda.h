@@ -146,6 +146,8 @@ vda_status vda_forward_gated(vda_plan_t plan, const void* q, const void* k, cons
  * The call reads the statistics and states that the last vda_forward (or
  * vda_forward_gated) on this plan left in its workspace: run the forward pass first,
  * with the same k, v, text_k, text_v, and keep the plan's workspace untouched in between.
+ * On a plan whose workspace holds no statistics yet (no forward pass enqueued) the call
+ * returns INVALID_VALUE.
  *   d_out          [B][H][F][n][dv], the gradient of the output;
  *   d_q, d_k, d_v, d_text_k, d_text_v: written, same layouts as q, k, v, text_k, text_v.
  * All tensors are bfloat16.  Only bfloat16 plans are supported.  The first call on a plan
@@ -180,7 +182,8 @@ vda_status vda_plan_timings(vda_plan_t plan, int* calls, float* stats_ms, float*
  * the plan is still running (synchronise its stream first).  NULL is accepted. */
 vda_status vda_plan_destroy(vda_plan_t plan);
 
-/* Bytes of device workspace the plan holds (0 for NULL). */
+/* Bytes of device workspace the plan holds (0 for NULL): the forward workspace, plus the
+ * backward workspace once vda_backward has allocated it. */
 size_t vda_plan_workspace_bytes(vda_plan_t plan);
 
 /* Static, human-readable name of a status code. */

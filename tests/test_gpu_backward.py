@@ -133,7 +133,15 @@ def test_backward_argument_errors():
         binding.VDA_ERROR_INVALID_VALUE
     torch.cuda.synchronize()
     assert not any(t.any() for t in g)
+    ws_fwd = plan.workspace_bytes
+    assert f(plan.handle, *ins, P(dO), *[P(t) for t in g], s) == binding.VDA_SUCCESS
+    torch.cuda.synchronize()
+    assert plan.workspace_bytes > ws_fwd  # the backward workspace is counted once allocated
     plan.close()
+    # no forward pass on this plan yet: nothing to differentiate
+    fresh = binding.Plan(w.B, w.H, w.F, w.n, w.d, w.dv, w.T, w.lam, w.dtype)
+    assert f(fresh.handle, *ins, P(dO), *[P(t) for t in g], s) == binding.VDA_ERROR_INVALID_VALUE
+    fresh.close()
     for dtype, idx in (("fp8", 6), ("f32", 1)):
         wx = W.WORKLOADS[idx].replace(H=1, F=2, n=64, T=4)
         px = binding.Plan(wx.B, wx.H, wx.F, wx.n, wx.d, wx.dv, wx.T, wx.lam, wx.dtype)
