@@ -635,6 +635,133 @@ readout_staged_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restric
   }
 }
 
+// dK and dV together at d = dv = 128: both products read K, so one workgroup of 8 waves
+// stages each 64-token tile of K and V once; waves 0-3 compute quarters of dK = [K K V V] Z
+// (as in the staged product above) and waves 4-7 quarters of dV = [K K] DB2 from the same
+// staged K, each keeping its own state fragments.
+struct ReadKV {
+  static constexpr int D = 128;
+  static constexpr int THREADS = 512;
+  static constexpr int KSK = 16, KSV = 8;           // state k-steps of dK (K hi, K lo, V hi, V lo) and dV
+  static constexpr int NBW = 2;                     // 16-feature output blocks per wave (32 features)
+  static constexpr int TT = 64;
+  static constexpr int RW = 2 * D + 8;              // bf16 per LDS token row (K then V, padded)
+  static constexpr int BUF = TT * RW;
+  static constexpr int PIECES = TT * 2 * D / 8;
+  static constexpr int PPT = PIECES / THREADS;
+  static constexpr int OWROW = 32 + 8;
+  static constexpr int OW_BYTES = 16 * OWROW * 2;
+  static constexpr int LDS_BYTES = 2 * BUF * 2 + 8 * OW_BYTES;
+};
+
+__global__ void __launch_bounds__(ReadKV::THREADS)
+readout_kv_kernel(const uint16_t* __restrict__ kq, const uint16_t* __restrict__ vq,
+                  const uint16_t* __restrict__ zk, const uint16_t* __restrict__ zv,
+                  uint16_t* __restrict__ dk, uint16_t* __restrict__ dvo, int64_t n,
+                  int64_t tiles_per_frame, int64_t splits, int64_t tiles_per_split,
+                  int64_t head_blocks, int64_t tail_splits, int64_t tail_tiles_per_split) {
+  using C = ReadKV;
+  constexpr int D = C::D;
+  extern __shared__ __align__(16) unsigned char smem[];
+  uint16_t* buf = reinterpret_cast<uint16_t*>(smem);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool is_k = wave < 4;                       // dK waves 0-3, dV waves 4-7
+  const int q4 = wave & 3;                          // quarter of the output features
+  uint16_t* ow = reinterpret_cast<uint16_t*>(smem + 2 * C::BUF * 2 + wave * C::OW_BYTES);
+  const int c16 = lane & 15, g4 = lane >> 4;
+  int64_t frame, t_first, tps;
+  if (blockIdx.x < head_blocks) {
+    frame = blockIdx.x / splits;
+    t_first = (blockIdx.x % splits) * tiles_per_split;
+    tps = tiles_per_split;
+  } else {
+    const int64_t i = blockIdx.x - head_blocks;
+    frame = head_blocks / splits + i / tail_splits;
+    t_first = (i % tail_splits) * tail_tiles_per_split;
+    tps = tail_tiles_per_split;
+  }
+  const int64_t t_last = (t_first + tps < tiles_per_frame) ? t_first + tps : tiles_per_frame;
+  if (t_first >= t_last) return;
+
+  // state fragments: dK waves 2 x 16, dV waves 2 x 8 (the first half of the array)
+  uint4 wfr[C::NBW][C::KSK];
+  {
+    const int ks_n = is_k ? C::KSK : C::KSV;
+    const int64_t rows = is_k ? 4 * D : 2 * D;
+    const uint4* sp = reinterpret_cast<const uint4*>((is_k ? zk : zv) + frame * rows * D) + lane;
+#pragma unroll
+    for (int jb = 0; jb < C::NBW; ++jb)
+#pragma unroll
+      for (int ks = 0; ks < C::KSK; ++ks)
+        if (ks < ks_n) wfr[jb][ks] = sp[((q4 * C::NBW + jb) * ks_n + ks) * 64];
+  }
+  constexpr int PR = 2 * D / 8;  // 16-byte pieces per token (K then V)
+  uint4 ra[C::PPT];
+  auto load_tile = [&](int64_t tile) {
+    const int64_t tok0 = tile * C::TT;
+    const int64_t left = n - tok0;
+    const uint32_t rows = uint32_t(left < 0 ? 0 : (left < C::TT ? left : C::TT));
+    const auto r1 = make_rsrc(kq + (frame * n + tok0) * D, rows * D * 2);
+    const auto r2 = make_rsrc(vq + (frame * n + tok0) * D, rows * D * 2);
+#pragma unroll
+    for (int i = 0; i < C::PPT; ++i) {
+      const int p = i * C::THREADS + tid, t = p / PR, c = p % PR;
+      ra[i] = c < D / 8 ? buffer_load16(r1, uint32_t((t * D + 8 * c) * 2))
+                        : buffer_load16(r2, uint32_t((t * D + 8 * (c - D / 8)) * 2));
+    }
+  };
+  auto store_tile = [&](int b) {
+#pragma unroll
+    for (int i = 0; i < C::PPT; ++i) {
+      const int p = i * C::THREADS + tid, t = p / PR, c = p % PR;
+      *reinterpret_cast<uint4*>(buf + b * C::BUF + t * C::RW + 8 * c) = ra[i];
+    }
+  };
+  load_tile(t_first);
+  store_tile(0);
+  if (t_first + 1 < t_last) load_tile(t_first + 1);
+  __syncthreads();
+
+  uint16_t* outp = is_k ? dk : dvo;
+  for (int64_t tile = t_first; tile < t_last; ++tile) {
+    const int b = int((tile - t_first) & 1);
+    const uint16_t* tb = buf + b * C::BUF;
+#pragma unroll
+    for (int tg = 0; tg < 4; ++tg) {
+      uint4 qf[8];  // K features 0..127 (4 k-steps), then V (4)
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+        if (is_k || ks < 4) qf[ks] = *reinterpret_cast<const uint4*>(tb + (16 * tg + c16) * C::RW + 32 * ks + 8 * g4);
+#pragma unroll
+      for (int jb = 0; jb < C::NBW; ++jb) {
+        f32x4 acc = f32x4{};
+        if (is_k) {
+#pragma unroll
+          for (int ks = 0; ks < C::KSK; ++ks) acc = mfma16_bf16(wfr[jb][ks], qf[ks < 8 ? ks % 4 : 4 + ks % 4], acc);
+        } else {
+#pragma unroll
+          for (int ks = 0; ks < C::KSV; ++ks) acc = mfma16_bf16(wfr[jb][ks], qf[ks % 4], acc);
+        }
+        *reinterpret_cast<uint2*>(ow + c16 * C::OWROW + 16 * jb + 4 * g4) =
+            make_uint2(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]));
+      }
+      const int64_t tok0 = tile * C::TT + 16 * tg;
+      const int64_t left = n - tok0;
+      const uint32_t rows = uint32_t(left < 0 ? 0 : (left < 16 ? left : 16));
+      const auto rs = make_rsrc(outp + (frame * n + tok0) * D, rows * D * 2);
+      const int orow = lane >> 2, och = lane & 3;  // 16 rows x 4 chunks of 16 bytes
+      buffer_store16<kCacheStreamOut>(rs, uint32_t(orow * D * 2 + q4 * 64 + och * 16),
+                                      *reinterpret_cast<const uint4*>(ow + orow * C::OWROW + och * 8));
+    }
+    if (tile + 1 < t_last) {
+      store_tile(b ^ 1);
+      if (tile + 2 < t_last) load_tile(tile + 2);
+    }
+    __syncthreads();
+  }
+}
+
 // smallest output-feature split whose fragments fit 32 x 16 bytes per lane
 template <int KS, int DV>
 constexpr int parts_wf() {
@@ -810,6 +937,21 @@ hipError_t launch_staged_t(const Problem& p, const void* q1, const void* q2, con
   return hipGetLastError();
 }
 
+hipError_t launch_kv_t(const Problem& p, const void* k, const void* v, const void* zk, const void* zv,
+                       void* dk, void* dv, hipStream_t s, bool prepare) {
+  using C = ReadKV;
+  if (prepare)
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(readout_kv_kernel),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
+  const ReadGrid gr = readout_grid(p.B * p.H * p.F, (p.n + C::TT - 1) / C::TT, p.num_cus);
+  hipLaunchKernelGGL(readout_kv_kernel, dim3(unsigned(gr.grid)), dim3(C::THREADS), C::LDS_BYTES, s,
+                     static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+                     static_cast<const uint16_t*>(zk), static_cast<const uint16_t*>(zv), static_cast<uint16_t*>(dk),
+                     static_cast<uint16_t*>(dv), p.n, gr.tpf, gr.splits, gr.tps, gr.head_blocks, gr.tail_splits,
+                     gr.tail_tps);
+  return hipGetLastError();
+}
+
 template <int D1, int R1, int D2, int R2, int DV>
 hipError_t launch_parts_t(const Problem& p, const void* q1, const void* q2, const void* state, void* out,
                           hipStream_t s) {
@@ -865,6 +1007,13 @@ hipError_t launch_readout_gated(const Problem& p, const void* q, const GateWeigh
 
 namespace vda {
 
+hipError_t launch_grad_kv(const Problem& p, const void* k, const void* v, const void* zk, const void* zv,
+                          void* dk, void* dv, hipStream_t s) {
+  if (p.d == 128 && p.dv == 128) return launch_kv_t(p, k, v, zk, zv, dk, dv, s, false);
+  const hipError_t e = launch_grad_dv(p, k, zv, dv, s);
+  return e != hipSuccess ? e : launch_grad_dk(p, k, v, zk, dk, s);
+}
+
 hipError_t launch_grad_dv(const Problem& p, const void* k, const void* state, void* out, hipStream_t s) {
 #define VDA_CASE(DD, VV) \
   if (p.d == DD && p.dv == VV) return launch_parts_t<DD, 2, 0, 0, VV>(p, k, nullptr, state, out, s);
@@ -896,7 +1045,10 @@ hipError_t launch_grad_dk(const Problem& p, const void* k, const void* v, const 
 namespace vda {
 
 hipError_t prepare_grad(const Problem& p) {
-  if (p.d == 128 && p.dv == 128) return launch_staged_t<128, 128, 128>(p, nullptr, nullptr, nullptr, nullptr, nullptr, true);
+  if (p.d == 128 && p.dv == 128) {
+    const hipError_t e = launch_staged_t<128, 128, 128>(p, nullptr, nullptr, nullptr, nullptr, nullptr, true);
+    return e != hipSuccess ? e : launch_kv_t(p, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, true);
+  }
   if (p.d == 128 && p.dv == 64) return launch_staged_t<128, 64, 128>(p, nullptr, nullptr, nullptr, nullptr, nullptr, true);
   if (p.d == 128 && p.dv == 32) return launch_staged_t<128, 32, 128>(p, nullptr, nullptr, nullptr, nullptr, nullptr, true);
   return hipSuccess;

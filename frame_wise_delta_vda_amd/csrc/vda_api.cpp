@@ -429,14 +429,13 @@ vda_status vda_backward(vda_plan_t plan, const void* q, const void* k, const voi
   pq.dv = p.d;
   pq.xf = pq.xb = f32(L.wt);
   if (e == hipSuccess) e = vda::launch_readout(pq, d_out, d_q, s);
-  if (e == hipSuccess) e = vda::launch_grad_dv(p, k, u16(L.db2), d_v, s);
-  if (e == hipSuccess) e = vda::launch_grad_dk(p, k, v, u16(L.z), d_k, s);
+  if (e == hipSuccess) e = vda::launch_grad_kv(p, k, v, u16(L.z), u16(L.db2), d_k, d_v, s);
   if (p.T > 0) {
     vda::Problem pt = p;
     pt.F = 1;
     pt.n = p.T;
-    if (e == hipSuccess) e = vda::launch_grad_dv(pt, text_k, u16(L.db2_text), d_text_v, s);
-    if (e == hipSuccess) e = vda::launch_grad_dk(pt, text_k, text_v, u16(L.z_text), d_text_k, s);
+    if (e == hipSuccess)
+      e = vda::launch_grad_kv(pt, text_k, text_v, u16(L.z_text), u16(L.db2_text), d_text_k, d_text_v, s);
   }
   mark(kEvReadEnd);
   if (tev != nullptr && e == hipSuccess) ++plan->timed_calls;

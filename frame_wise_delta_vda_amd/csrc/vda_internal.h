@@ -64,6 +64,9 @@ hipError_t prepare_bwd_frames(const Problem& p);
 //   split_dk:  out (n x d)  = [K K V V] Z,         Z a (2d + 2dv) x d state
 hipError_t launch_grad_dv(const Problem& p, const void* k, const void* state, void* out, hipStream_t stream);
 hipError_t prepare_grad(const Problem& p);
+// dK and dV of the backward pass together (one pass over K and V at d = dv = 128)
+hipError_t launch_grad_kv(const Problem& p, const void* k, const void* v, const void* zk, const void* zv,
+                          void* dk, void* dv, hipStream_t stream);
 hipError_t launch_grad_dk(const Problem& p, const void* k, const void* v, const void* state, void* out,
                           hipStream_t stream);
 // The readout followed by the gated epilogue (bfloat16 and FP8 plans).
