@@ -52,13 +52,11 @@ struct BwdFrame {
 // for ill-conditioned frames dB and M are large along directions that K maps to small
 // values, and one bf16 rounding there shows in K dB.
 template <int D, int DV>
-__global__ void __launch_bounds__(kThreads)
-bwd_frame_kernel(const float* __restrict__ xf, const float* __restrict__ xb,
-                 const float* __restrict__ sf, const float* __restrict__ sb,
-                 uint16_t* __restrict__ wt, uint16_t* __restrict__ db2, uint16_t* __restrict__ z) {
+__device__ __forceinline__ void frame_terms(const float* __restrict__ xf, const float* __restrict__ xb,
+                                            const float* __restrict__ sf, const float* __restrict__ sb,
+                                            uint16_t* __restrict__ wt, uint16_t* __restrict__ db2,
+                                            uint16_t* __restrict__ z, int64_t fr, unsigned char* smem) {
   using C = BwdFrame<D, DV>;
-  extern __shared__ __align__(16) unsigned char smem[];
-  const int64_t fr = blockIdx.x;
   const int64_t base = fr * int64_t(D) * DV;
   const float* XF = xf + base;
   const float* XB = xb + base;
@@ -232,16 +230,14 @@ struct BwdText {
 };
 
 template <int D, int DV>
-__global__ void __launch_bounds__(kThreads)
-bwd_text_kernel(const uint16_t* __restrict__ ainv, const float* __restrict__ bm,
-                const float* __restrict__ sf, const float* __restrict__ sb,
-                uint16_t* __restrict__ db2_text, uint16_t* __restrict__ z_text, int64_t F, float lam) {
+__device__ __forceinline__ void text_terms(const uint16_t* __restrict__ ainv, const float* __restrict__ bm,
+                                           const float* __restrict__ sf, const float* __restrict__ sb,
+                                           uint16_t* __restrict__ db2_text, uint16_t* __restrict__ z_text,
+                                           int64_t F, float lam, int64_t bh, unsigned char* smem) {
   using C = BwdText<D, DV>;
-  extern __shared__ __align__(16) unsigned char smem[];
   float* LA = reinterpret_cast<float*>(smem);   // A_0^{-1} [D][AROW]
   float* LR = LA + C::ASZ;                       // right-hand sides / results [D][RROW]
   float* LU = LA;                                // U_0 [D][RROW], over A once it is used
-  const int64_t bh = blockIdx.x;
   const int tid = threadIdx.x;
   const int64_t F1 = F + 1;
   const uint16_t* hi = ainv + bh * F1 * int64_t(2 * D * D);
@@ -326,27 +322,36 @@ bwd_text_kernel(const uint16_t* __restrict__ ainv, const float* __restrict__ bm,
   }
 }
 
+// One launch for both: the text workgroups (one per head) come first in the grid, so they
+// run beside the frame workgroups instead of after them.
+template <int D, int DV>
+__global__ void __launch_bounds__(kThreads)
+bwd_frames_kernel(const float* __restrict__ xf, const float* __restrict__ xb,
+                  const float* __restrict__ sf, const float* __restrict__ sb,
+                  uint16_t* __restrict__ wt, uint16_t* __restrict__ db2, uint16_t* __restrict__ z,
+                  const uint16_t* __restrict__ ainv, const float* __restrict__ bm,
+                  uint16_t* __restrict__ db2_text, uint16_t* __restrict__ z_text, int64_t F, float lam,
+                  int64_t text_blocks) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  if (int64_t(blockIdx.x) < text_blocks)
+    text_terms<D, DV>(ainv, bm, sf, sb, db2_text, z_text, F, lam, blockIdx.x, smem);
+  else
+    frame_terms<D, DV>(xf, xb, sf, sb, wt, db2, z, blockIdx.x - text_blocks, smem);
+}
+
 template <int D, int DV>
 hipError_t launch_bwd_frames_t(const BwdProblem& b, hipStream_t s, bool prepare) {
-  using C = BwdFrame<D, DV>;
-  using T = BwdText<D, DV>;
-  auto kf = bwd_frame_kernel<D, DV>;
-  auto kt = bwd_text_kernel<D, DV>;
-  if (prepare) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kf),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
-    if (e != hipSuccess) return e;
-    return hipFuncSetAttribute(reinterpret_cast<const void*>(kt),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, T::LDS_BYTES);
-  }
+  constexpr int lds = cmax(BwdFrame<D, DV>::LDS_BYTES, BwdText<D, DV>::LDS_BYTES);
+  auto kern = bwd_frames_kernel<D, DV>;
+  if (prepare)
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                               lds);
   const int64_t BH = b.p.B * b.p.H;
-  if (BH * b.p.F > 0)
-    hipLaunchKernelGGL(kf, dim3(unsigned(BH * b.p.F)), dim3(kThreads), C::LDS_BYTES, s, b.xf32, b.xb32,
-                       b.sf, b.sb, b.wt, b.db2, b.z);
-  if (BH > 0 && b.p.T > 0 && b.p.F > 0)
-    hipLaunchKernelGGL(kt, dim3(unsigned(BH)), dim3(kThreads), T::LDS_BYTES, s,
-                       reinterpret_cast<const uint16_t*>(b.p.ainv), b.p.bm, b.sf, b.sb, b.db2_text,
-                       b.z_text, b.p.F, b.p.lam);
+  if (BH == 0 || b.p.F == 0) return hipSuccess;
+  const int64_t text_blocks = b.p.T > 0 ? BH : 0;
+  hipLaunchKernelGGL(kern, dim3(unsigned(text_blocks + BH * b.p.F)), dim3(kThreads), lds, s, b.xf32, b.xb32,
+                     b.sf, b.sb, b.wt, b.db2, b.z, reinterpret_cast<const uint16_t*>(b.p.ainv), b.p.bm,
+                     b.db2_text, b.z_text, b.p.F, b.p.lam, text_blocks);
   return hipGetLastError();
 }
 
