@@ -154,6 +154,15 @@ __device__ __forceinline__ void sweep_neg_inverse_128(f32x16 (&t)[4], float* lds
 }
 
 // ---------------------------------------------------------------- bfloat16 inputs
+// sym_tiles, the d = 128 split of the 32x32 output tiles over the four waves.  Wave w
+// holds the K operand fragments of all four 32-feature blocks, rotated so that a[i] is
+// block (w + i) % 4 (a[0], its own block, is also the column operand of its G tiles), and
+// accumulates
+//   acc[0] = G(w, w),  acc[1] = G(w, w + 1),  acc[2] = G(w, w + 2) (waves 0 and 1 only),
+//   acc[3 + i] = Bm((w + i) % 4, w),
+// block indices mod 4.  That is each of the ten G tiles on and above the block diagonal
+// once (G is symmetric; the epilogue writes the mirror of each off-diagonal tile) and all
+// sixteen Bm tiles: 7, 7, 6 and 6 MFMAs and 5 operand fragments per wave and k-step.
 template <int D, int DV>
 struct StatsBf16 {
   static constexpr int TC = 64;                  // tokens per chunk
@@ -161,12 +170,13 @@ struct StatsBf16 {
   static constexpr int NK = D / 32, NV = DV / 32, NC = NK + NV;
   static constexpr int RPW = 4 / NK;             // waves sharing one 32-row block of G
   static constexpr int CPW = (NC + RPW - 1) / RPW;  // 32x32 output tiles per wave
-  // d = 128: wave j accumulates column tile j of G and of Bm over all four row blocks
-  // (6 fragment reads per k-step instead of 9); other widths: wave row blocks as above
+  // d = 128: wave j accumulates column tile j of Bm over all four row blocks and its share
+  // of the ten tiles on and above the diagonal of G (sym_tiles); other widths: wave row
+  // blocks as above
   static constexpr bool COLW = D == 128;
   // d = dv = 128: every thread loads, and waves split evenly between K and V
   static constexpr bool DEEP = D == 128 && DV == 128;
-  static constexpr int ACC = COLW ? 8 : CPW;
+  static constexpr int ACC = COLW ? 7 : CPW;
   static constexpr int NSEG = (D + DV) / 8;      // 8-feature segments per token (K then V)
   // d = dv = 128 stage token-major instead: a row per token (K then V, padded to 576 B so
   // the transposing LDS reads of four consecutive rows hit distinct banks)
@@ -264,16 +274,19 @@ stats_bf16_kernel(const In* __restrict__ k, const In* __restrict__ v,
     const uint16_t* vt = kt + D * C::ROW;
     const int col = ks * 16 + (lane >> 5) * 8;
     if constexpr (C::COLW) {
-      // acc[rb] = G(rb, wave), acc[4 + rb] = Bm(rb, wave)
-      const uint4 bk = *reinterpret_cast<const uint4*>(kt + (wave * 32 + (lane & 31)) * C::ROW + col);
-      uint4 bv = make_uint4(0, 0, 0, 0);
-      if (C::NV >= 4 || wave < C::NV) bv = *reinterpret_cast<const uint4*>(vt + (wave * 32 + (lane & 31)) * C::ROW + col);
+      // the tiles of sym_tiles
+      uint4 a[4];
 #pragma unroll
-      for (int rbi = 0; rbi < 4; ++rbi) {
-        const uint4 a = *reinterpret_cast<const uint4*>(kt + (rbi * 32 + (lane & 31)) * C::ROW + col);
-        acc[rbi] = mfma32_bf16(a, bk, acc[rbi]);
-        if (C::NV >= 4 || wave < C::NV) acc[4 + rbi] = mfma32_bf16(a, bv, acc[4 + rbi]);
+      for (int i = 0; i < 4; ++i)
+        a[i] = *reinterpret_cast<const uint4*>(kt + (32 * ((wave + i) & 3) + (lane & 31)) * C::ROW + col);
+      if (C::NV >= 4 || wave < C::NV) {
+        const uint4 bv = *reinterpret_cast<const uint4*>(vt + (wave * 32 + (lane & 31)) * C::ROW + col);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[3 + i] = mfma32_bf16(a[i], bv, acc[3 + i]);
       }
+      acc[0] = mfma32_bf16(a[0], a[0], acc[0]);
+      acc[1] = mfma32_bf16(a[0], a[1], acc[1]);
+      if (wave < 2) acc[2] = mfma32_bf16(a[0], a[2], acc[2]);
     } else {
       const uint4 a = *reinterpret_cast<const uint4*>(kt + (rb * 32 + (lane & 31)) * C::ROW + col);
 #pragma unroll
@@ -342,17 +355,18 @@ stats_bf16_kernel(const In* __restrict__ k, const In* __restrict__ v,
       }
       return r;
     };
-    // acc[rb] = G(rb, wave), acc[4 + rb] = Bm(rb, wave) over one 64-token k-step
+    // the tiles of sym_tiles over one 64-token k-step
     auto kstep8 = [&](int buf, int ks) {
       const uint8_t* rows = stage8 + buf * C::BUF8 + ks * 64 * C::TROW8;
-      const i32x8 bk = frag8(rows, wave * 32);
+      i32x8 a[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = frag8(rows, 32 * ((wave + i) & 3));
       const i32x8 bv = frag8(rows, 128 + wave * 32);
 #pragma unroll
-      for (int rbi = 0; rbi < 4; ++rbi) {
-        const i32x8 a = frag8(rows, rbi * 32);
-        acc[rbi] = mfma32_fp8(a, bk, acc[rbi]);
-        acc[4 + rbi] = mfma32_fp8(a, bv, acc[4 + rbi]);
-      }
+      for (int i = 0; i < 4; ++i) acc[3 + i] = mfma32_fp8(a[i], bv, acc[3 + i]);
+      acc[0] = mfma32_fp8(a[0], a[0], acc[0]);
+      acc[1] = mfma32_fp8(a[0], a[1], acc[1]);
+      if (wave < 2) acc[2] = mfma32_fp8(a[0], a[2], acc[2]);
     };
     // multiply the chunk in buffer buf while loading chunk ch (4 loads before each k-step)
     auto mult_load8 = [&](int buf, int64_t ch, uint4 (&r)[8]) {
@@ -416,17 +430,18 @@ stats_bf16_kernel(const In* __restrict__ k, const In* __restrict__ v,
       const uint2 xl = __builtin_bit_cast(uint2, x), yl = __builtin_bit_cast(uint2, y);
       return make_uint4(xl.x, xl.y, yl.x, yl.y);
     };
-    // acc[rb] = G(rb, wave), acc[4 + rb] = Bm(rb, wave) over one 16-token k-step
+    // the tiles of sym_tiles over one 16-token k-step
     auto kstep_tm = [&](int buf, int ks) {
       const uint16_t* rows = stage + buf * C::BUF + ks * 16 * C::TROW;
-      const uint4 bk = frag(rows, wave * 32);
+      uint4 a[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = frag(rows, 32 * ((wave + i) & 3));
       const uint4 bv = frag(rows, D + wave * 32);
 #pragma unroll
-      for (int rbi = 0; rbi < 4; ++rbi) {
-        const uint4 a = frag(rows, rbi * 32);
-        acc[rbi] = mfma32_bf16(a, bk, acc[rbi]);
-        acc[4 + rbi] = mfma32_bf16(a, bv, acc[4 + rbi]);
-      }
+      for (int i = 0; i < 4; ++i) acc[3 + i] = mfma32_bf16(a[i], bv, acc[3 + i]);
+      acc[0] = mfma32_bf16(a[0], a[0], acc[0]);
+      acc[1] = mfma32_bf16(a[0], a[1], acc[1]);
+      if (wave < 2) acc[2] = mfma32_bf16(a[0], a[2], acc[2]);
     };
     // Multiply the chunk in LDS buffer buf while loading chunk ch into r.  The memory
     // queue is usually full, so a load can stall its wave at issue; two loads go out
@@ -479,17 +494,28 @@ stats_bf16_kernel(const In* __restrict__ k, const In* __restrict__ v,
     const int l32 = lane & 31;
     if (wave < C::NV) {
 #pragma unroll
-      for (int rbi = 0; rbi < 4; ++rbi)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int e = 0; e < 16; ++e)
-          bmo[blk_index(rbi * 32 + mfma32_row(e, lane), wave * 32 + l32, D)] = acc[4 + rbi][e];
+          bmo[blk_index(32 * ((wave + i) & 3) + mfma32_row(e, lane), wave * 32 + l32, D)] = acc[3 + i][e];
     }
-    // G column block -> LDS -> G row block in the accumulator layout the sweep works on
+    // G tiles (and the mirror of each off-diagonal one) -> LDS -> G row block in the
+    // accumulator layout the sweep works on
     float* gsm = reinterpret_cast<float*>(smem);
+    {
+      const int r0 = 32 * wave, r1 = 32 * ((wave + 1) & 3), r2 = 32 * ((wave + 2) & 3);
 #pragma unroll
-    for (int rbi = 0; rbi < 4; ++rbi)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) gsm[(rbi * 32 + mfma32_row(e, lane)) * C::GS + wave * 32 + l32] = acc[rbi][e];
+      for (int e = 0; e < 16; ++e) {
+        const int r = mfma32_row(e, lane);
+        gsm[(r0 + r) * C::GS + r0 + l32] = acc[0][e];
+        gsm[(r0 + r) * C::GS + r1 + l32] = acc[1][e];
+        gsm[(r1 + l32) * C::GS + r0 + r] = acc[1][e];
+        if (wave < 2) {
+          gsm[(r0 + r) * C::GS + r2 + l32] = acc[2][e];
+          gsm[(r2 + l32) * C::GS + r0 + r] = acc[2][e];
+        }
+      }
+    }
     __syncthreads();
     f32x16 t[4];
 #pragma unroll
