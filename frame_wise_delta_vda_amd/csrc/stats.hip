@@ -195,7 +195,9 @@ struct StatsBf16 {
 
 // In: uint16_t (bfloat16 inputs) or uint8_t (FP8 e4m3 inputs, converted to bfloat16 as
 // they are written to LDS, so everything after the staging is the same).
-template <int D, int DV, typename In>
+// GRAM = false computes Bm = K^T V alone (no G, no inverse, nothing written to ainv): the
+// backward pass's dW = Q^T dO.
+template <int D, int DV, typename In, bool GRAM = true>
 __global__ void __launch_bounds__(kThreads, 2)
 stats_bf16_kernel(const In* __restrict__ k, const In* __restrict__ v,
                   const In* __restrict__ tk, const In* __restrict__ tv,
@@ -284,15 +286,17 @@ stats_bf16_kernel(const In* __restrict__ k, const In* __restrict__ v,
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[3 + i] = mfma32_bf16(a[i], bv, acc[3 + i]);
       }
-      acc[0] = mfma32_bf16(a[0], a[0], acc[0]);
-      acc[1] = mfma32_bf16(a[0], a[1], acc[1]);
-      if (wave < 2) acc[2] = mfma32_bf16(a[0], a[2], acc[2]);
+      if constexpr (GRAM) {
+        acc[0] = mfma32_bf16(a[0], a[0], acc[0]);
+        acc[1] = mfma32_bf16(a[0], a[1], acc[1]);
+        if (wave < 2) acc[2] = mfma32_bf16(a[0], a[2], acc[2]);
+      }
     } else {
       const uint4 a = *reinterpret_cast<const uint4*>(kt + (rb * 32 + (lane & 31)) * C::ROW + col);
 #pragma unroll
       for (int jj = 0; jj < C::CPW; ++jj) {
         const int c = jj * C::RPW + cofs;
-        if (c < C::NC) {
+        if (c < C::NC && (GRAM || c >= C::NK)) {
           const uint16_t* bs = c < C::NK ? kt + (c * 32 + (lane & 31)) * C::ROW
                                          : vt + ((c - C::NK) * 32 + (lane & 31)) * C::ROW;
           const uint4 b = *reinterpret_cast<const uint4*>(bs + col);
@@ -364,9 +368,11 @@ stats_bf16_kernel(const In* __restrict__ k, const In* __restrict__ v,
       const i32x8 bv = frag8(rows, 128 + wave * 32);
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[3 + i] = mfma32_fp8(a[i], bv, acc[3 + i]);
-      acc[0] = mfma32_fp8(a[0], a[0], acc[0]);
-      acc[1] = mfma32_fp8(a[0], a[1], acc[1]);
-      if (wave < 2) acc[2] = mfma32_fp8(a[0], a[2], acc[2]);
+      if constexpr (GRAM) {
+        acc[0] = mfma32_fp8(a[0], a[0], acc[0]);
+        acc[1] = mfma32_fp8(a[0], a[1], acc[1]);
+        if (wave < 2) acc[2] = mfma32_fp8(a[0], a[2], acc[2]);
+      }
     };
     // multiply the chunk in buffer buf while loading chunk ch (4 loads before each k-step)
     auto mult_load8 = [&](int buf, int64_t ch, uint4 (&r)[8]) {
@@ -439,9 +445,11 @@ stats_bf16_kernel(const In* __restrict__ k, const In* __restrict__ v,
       const uint4 bv = frag(rows, D + wave * 32);
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[3 + i] = mfma32_bf16(a[i], bv, acc[3 + i]);
-      acc[0] = mfma32_bf16(a[0], a[0], acc[0]);
-      acc[1] = mfma32_bf16(a[0], a[1], acc[1]);
-      if (wave < 2) acc[2] = mfma32_bf16(a[0], a[2], acc[2]);
+      if constexpr (GRAM) {
+        acc[0] = mfma32_bf16(a[0], a[0], acc[0]);
+        acc[1] = mfma32_bf16(a[0], a[1], acc[1]);
+        if (wave < 2) acc[2] = mfma32_bf16(a[0], a[2], acc[2]);
+      }
     };
     // Multiply the chunk in LDS buffer buf while loading chunk ch into r.  The memory
     // queue is usually full, so a load can stall its wave at issue; two loads go out
@@ -486,8 +494,6 @@ stats_bf16_kernel(const In* __restrict__ k, const In* __restrict__ v,
   }
 
   float* bmo = bm + (bh * F1 + fi) * int64_t(D) * DV;
-  uint16_t* hi_plane = reinterpret_cast<uint16_t*>(ainv + (bh * F1 + fi) * int64_t(D) * D);
-  uint16_t* lo_plane = hi_plane + sym_blocks(D) * 256;
   if constexpr (D == 128) {
     // ---- epilogue (d = 128): Bm tiles to the workspace; lam I + G inverted in the
     // accumulators by the blocked sweep; A^{-1} = -(swept matrix) written out.
@@ -499,6 +505,9 @@ stats_bf16_kernel(const In* __restrict__ k, const In* __restrict__ v,
         for (int e = 0; e < 16; ++e)
           bmo[blk_index(32 * ((wave + i) & 3) + mfma32_row(e, lane), wave * 32 + l32, D)] = acc[3 + i][e];
     }
+    if constexpr (!GRAM) return;
+    uint16_t* hi_plane = reinterpret_cast<uint16_t*>(ainv + (bh * F1 + fi) * int64_t(D) * D);
+    uint16_t* lo_plane = hi_plane + sym_blocks(D) * 256;
     // G tiles (and the mirror of each off-diagonal one) -> LDS -> G row block in the
     // accumulator layout the sweep works on
     float* gsm = reinterpret_cast<float*>(smem);
@@ -556,13 +565,16 @@ stats_bf16_kernel(const In* __restrict__ k, const In* __restrict__ v,
     for (int e = 0; e < 16; ++e) {
       const int row = rb * 32 + mfma32_row(e, lane);
       if (c < C::NK) {
-        gsm[row * C::GS + c * 32 + (lane & 31)] = acc[jj][e];
+        if constexpr (GRAM) gsm[row * C::GS + c * 32 + (lane & 31)] = acc[jj][e];
       } else {
         bmo[blk_index(row, (c - C::NK) * 32 + (lane & 31), D)] = acc[jj][e];
       }
     }
   }
+  if constexpr (!GRAM) return;
   __syncthreads();
+  uint16_t* hi_plane = reinterpret_cast<uint16_t*>(ainv + (bh * F1 + fi) * int64_t(D) * D);
+  uint16_t* lo_plane = hi_plane + sym_blocks(D) * 256;
   float* rowv = reinterpret_cast<float*>(smem + C::MAIN_BYTES);
   float* colv = rowv + 2 * D;
   float a[D / 16][D / 16];
@@ -719,9 +731,18 @@ hipError_t launch_stats_t(const Problem& p, const void* k, const void* v, const 
                          p.n, p.T, p.lam);
       return hipGetLastError();
     };
+    if (prepare && !p.fp8) {
+      const hipError_t e = launch(stats_bf16_kernel<D, DV, uint16_t, false>, uint16_t{});
+      if (e != hipSuccess) return e;
+    }
+    if (p.bm_only) {
+      if (p.fp8) return hipErrorInvalidValue;
+      return launch(stats_bf16_kernel<D, DV, uint16_t, false>, uint16_t{});
+    }
     return p.fp8 ? launch(stats_bf16_kernel<D, DV, uint8_t>, uint8_t{})
                  : launch(stats_bf16_kernel<D, DV, uint16_t>, uint16_t{});
   } else {
+    if (p.bm_only) return hipErrorInvalidValue;
     constexpr int lds = StatsF32<D, DV>::LDS_BYTES;
     auto kern = stats_f32_kernel<D, DV>;
     if (prepare)

@@ -121,6 +121,7 @@ vda_status vda_plan_create(int64_t B, int64_t H, int64_t F, int64_t n, int64_t d
   p.bf16 = (dtype != VDA_DTYPE_F32);  // FP8 inputs run the bfloat16 path after conversion
   p.fp8 = (dtype == VDA_DTYPE_FP8_E4M3);
   p.states_f32 = false;
+  p.bm_only = false;
   p.ainv = p.bm = p.xf = p.xb = nullptr;
   plan->workspace = nullptr;
   plan->workspace_bytes = 0;
@@ -284,7 +285,7 @@ vda_status enqueue(vda_plan_t plan, unsigned stages, const void* q, const void* 
 
 // Layout of the backward workspace (byte offsets, each 256-aligned).
 struct BwdLayout {
-  size_t ainv, dw, xf, xb, sf, sb, wt, db2, z, db2_text, z_text, total;
+  size_t dw, xf, xb, sf, sb, wt, db2, z, db2_text, z_text, total;
 };
 BwdLayout bwd_layout(const vda::Problem& p) {
   const size_t BH = size_t(p.B) * size_t(p.H), F = size_t(p.F), d = size_t(p.d), dv = size_t(p.dv);
@@ -295,7 +296,6 @@ BwdLayout bwd_layout(const vda::Problem& p) {
     off += (bytes + 255) & ~size_t(255);
     return at;
   };
-  L.ainv = take(BH * (F + 1) * d * d * 4);
   L.dw = take(BH * (F + 1) * d * dv * 4);
   L.xf = take(BH * F * d * dv * 4);
   L.xb = take(BH * F * d * dv * 4);
@@ -394,11 +394,13 @@ vda_status vda_backward(vda_plan_t plan, const void* q, const void* k, const voi
   auto mark = [&](int slot) {
     if (tev != nullptr && e == hipSuccess) e = hipEventRecord(tev[slot], s);
   };
-  // 1. dW_f = Q_f^T dO_f: the statistics stage on (Q, dO) with no text (frame 0 is zero)
+  // 1. dW_f = Q_f^T dO_f: the statistics stage on (Q, dO), Bm only, with no text (frame 0
+  //    is zero)
   mark(kEvStatsBegin);
   vda::Problem pw = p;
   pw.T = 0;
-  pw.ainv = f32(L.ainv);
+  pw.bm_only = true;
+  pw.ainv = nullptr;
   pw.bm = f32(L.dw);
   e = vda::launch_stats(pw, q, d_out, nullptr, nullptr, s);
   mark(kEvStatsEnd);

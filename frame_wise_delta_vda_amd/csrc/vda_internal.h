@@ -18,6 +18,7 @@ struct Problem {
   bool bf16;        // bfloat16 path: bfloat16 out and states (set for FP8 inputs as well)
   bool fp8;         // q, k, v and text are OCP FP8 e4m3 codes (bfloat16 path otherwise)
   bool states_f32;  // bf16 path: the scan stores float32 blocked states (backward pass)
+  bool bm_only;     // bf16 path: the statistics stage writes Bm = K^T V only (ainv unused)
   int num_cus;      // compute units of the plan's device (sizes persistent grids)
   // workspace (float32), frame index 0 = text, 1..F = frames
   float* ainv;      // [BH][F+1][d][d]
