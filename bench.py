@@ -295,11 +295,19 @@ def run_backward(args):
     tok = BH * w.F * w.n
     ttok = BH * w.T
     e = 2  # bf16
-    # bytes each span must move: Q^T dO reads Q and dO; the products read dO, K, V and write
-    # dQ, dK, dV (and the text's K, V in, gradients out)
-    alg = {"stats": tok * (w.d + w.dv) * e,
-           "products": tok * (w.dv + w.d + w.dv + w.d + w.d + w.dv) * e + ttok * 2 * (w.d + w.dv) * e}
-    spans = {"stats": st_ms, "adjoint": sc_ms, "products": rd_ms}
+    # bytes each span must move.  At d = dv = 128 the first span is the float32 state
+    # recompute and one pass over (Q, dO) that forms dW = Q^T dO and dQ = dO W^T (reads Q, dO,
+    # writes dQ); the products read K, V and write dK, dV (and the text's K, V in, gradients
+    # out).  At other widths the first span is Q^T dO alone and dQ is one of the products.
+    text = ttok * 2 * (w.d + w.dv) * e
+    if w.d == 128 and w.dv == 128:
+        first = "recompute_dw_dq"
+        alg = {first: tok * (w.d + w.dv + w.d) * e, "products": tok * 2 * (w.d + w.dv) * e + text}
+    else:
+        first = "stats"
+        alg = {first: tok * (w.d + w.dv) * e,
+               "products": tok * (w.dv + w.d + w.dv + w.d + w.d + w.dv) * e + text}
+    spans = {first: st_ms, "adjoint": sc_ms, "products": rd_ms}
     kernels = {n: {"ms": round(ms, 4)} for n, ms in spans.items()}
     for n in alg:
         gbs = alg[n] / (spans[n] * 1e-3) / 1e9

@@ -99,7 +99,8 @@ __device__ __forceinline__ void frame_terms(const float* __restrict__ xf, const 
       }
       // WT: rows c0.. (value features) of column i0 + r; Z rows 2D + c0.. (dB^T hi) and
       // 2D + DV + c0.. (lo) of column i0 + r
-      reinterpret_cast<uint4*>(wt + base)[chunk_of(c0, i0 + r, DV)] = make_uint4(w[0], w[1], w[2], w[3]);
+      if (wt != nullptr)
+        reinterpret_cast<uint4*>(wt + base)[chunk_of(c0, i0 + r, DV)] = make_uint4(w[0], w[1], w[2], w[3]);
       reinterpret_cast<uint4*>(zf)[chunk_of(2 * D + c0, i0 + r, C::ZR)] = make_uint4(h[0], h[1], h[2], h[3]);
       reinterpret_cast<uint4*>(zf)[chunk_of(2 * D + DV + c0, i0 + r, C::ZR)] = make_uint4(l[0], l[1], l[2], l[3]);
     }

@@ -195,15 +195,22 @@ struct StatsBf16 {
 
 // In: uint16_t (bfloat16 inputs) or uint8_t (FP8 e4m3 inputs, converted to bfloat16 as
 // they are written to LDS, so everything after the staging is the same).
-// GRAM = false computes Bm = K^T V alone (no G, no inverse, nothing written to ainv): the
-// backward pass's dW = Q^T dO.
-template <int D, int DV, typename In, bool GRAM = true>
+// MODE kStatsBm computes Bm = K^T V alone (no G, no inverse, nothing written to ainv): the
+// backward pass's dW = Q^T dO.  MODE kStatsBmDq (d = dv = 128, bfloat16) also forms, from
+// the same staged chunks of V = dO, the backward pass's dQ = dO W^T, with
+// W = (X_fwd + X_bwd) / 2 taken from the float32 blocked states xf32 / xb32.
+enum : int { kStatsGram = 0, kStatsBm = 1, kStatsBmDq = 2 };
+template <int D, int DV, typename In, int MODE = kStatsGram>
 __global__ void __launch_bounds__(kThreads, 2)
 stats_bf16_kernel(const In* __restrict__ k, const In* __restrict__ v,
                   const In* __restrict__ tk, const In* __restrict__ tv,
                   float* __restrict__ ainv, float* __restrict__ bm,
-                  int64_t F, int64_t n, int64_t T, float lam) {
+                  int64_t F, int64_t n, int64_t T, float lam,
+                  const float* __restrict__ xf32, const float* __restrict__ xb32, uint16_t* __restrict__ dq) {
   using C = StatsBf16<D, DV>;
+  constexpr bool GRAM = MODE == kStatsGram;
+  constexpr bool DQ = MODE == kStatsBmDq;
+  static_assert(!DQ || (C::DEEP && sizeof(In) == 2), "dQ is formed at d = dv = 128, bfloat16");
   constexpr bool FP8 = sizeof(In) == 1;
   extern __shared__ __align__(16) unsigned char smem[];
   uint16_t* stage = reinterpret_cast<uint16_t*>(smem);
@@ -451,6 +458,49 @@ stats_bf16_kernel(const In* __restrict__ k, const In* __restrict__ v,
         if (wave < 2) acc[2] = mfma32_bf16(a[0], a[2], acc[2]);
       }
     };
+    // dQ = dO W^T (DQ): wave w forms dQ^T rows 32w..32w+31 (key features) for the chunk's 64
+    // tokens on the 32x32x16 MFMA.  Its W operand (rows 32w.., k = value features) stays in
+    // registers for the frame; the dO^T operand is 8 value features of one token, a plain
+    // 16-byte read of the token's staged row.
+    uint4 wq[DQ ? DV / 16 : 1];
+    f32x16 dqa[2] = {f32x16{}, f32x16{}};
+    const bool dq_on = DQ && fi > 0;
+    const auto rq = make_rsrc(dq + (dq_on ? (bh * F + fi - 1) * n * D : 0), dq_on ? uint32_t(ntok * D * 2) : 0u);
+    auto dq_part = [&](int buf, int ks) {  // value-feature blocks 2ks, 2ks+1 of both token halves
+      const uint16_t* rows = stage + buf * C::BUF + D + 8 * (lane >> 5);
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int kb = 2 * ks + u;
+          const uint4 b = *reinterpret_cast<const uint4*>(rows + (32 * tb + (lane & 31)) * C::TROW + 16 * kb);
+          dqa[tb] = mfma32_bf16(wq[kb], b, dqa[tb]);
+        }
+    };
+    // dQ of a finished chunk goes out through this wave's own part of a staging buffer that
+    // every wave has finished reading (its rows 32 (w % 2)..+31, columns of K or V by w / 2:
+    // only this wave's stores of the next chunk write there, later in its program order, and
+    // one wave's LDS accesses complete in order).  Token t of the chunk takes row t % 32,
+    // bytes 64 (t / 32)..+63, so the read-back gives four lanes 64 contiguous bytes of a
+    // token's output row: the global stores are whole 64-byte pieces.
+    auto dq_flush = [&](int buf, int64_t chunk) {
+      uint16_t* fp = stage + buf * C::BUF + 32 * (wave & 1) * C::TROW + (wave >> 1) * D;
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *reinterpret_cast<uint2*>(fp + (lane & 31) * C::TROW + 32 * tb + 8 * g + 4 * (lane >> 5)) =
+              make_uint2(pack_bf16x2(dqa[tb][4 * g], dqa[tb][4 * g + 1]),
+                         pack_bf16x2(dqa[tb][4 * g + 2], dqa[tb][4 * g + 3]));
+        dqa[tb] = f32x16{};
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int t = 16 * j + (lane >> 2), pc = lane & 3;
+        const uint4 x = *reinterpret_cast<const uint4*>(fp + (t & 31) * C::TROW + 32 * (t >> 5) + 8 * pc);
+        buffer_store16<kCacheStreamOut>(rq, uint32_t(((chunk * C::TC + t) * D + 32 * wave + 8 * pc) * 2), x);
+      }
+    };
     // Multiply the chunk in LDS buffer buf while loading chunk ch into r.  The memory
     // queue is usually full, so a load can stall its wave at issue; two loads go out
     // before each k-step, and a stalled issue waits beside the previous k-step's MFMAs
@@ -462,20 +512,51 @@ stats_bf16_kernel(const In* __restrict__ k, const In* __restrict__ v,
         r[2 * ks] = buffer_load16<kCacheNt>(rs, base + uint32_t(2 * ks * 1024));
         r[2 * ks + 1] = buffer_load16<kCacheNt>(rs, base + uint32_t((2 * ks + 1) * 1024));
         kstep_tm(buf, ks);
+        if constexpr (DQ) dq_part(buf, ks);
         __builtin_amdgcn_sched_barrier(0);
       }
     };
     load_deep(0, ra);
     load_deep(1, rn);
+    if (dq_on) {
+      // W^T of the frame into the staging area (rows = value features j, the key features i
+      // along a row, bfloat16, the staging row stride), then every wave's W fragments by the
+      // transposing reads the main loop uses.  A float4 of the blocked states is rows
+      // i0..i0+3 of one column j.
+      const float4* xf4 = reinterpret_cast<const float4*>(xf32 + (bh * F + fi - 1) * int64_t(D) * DV);
+      const float4* xb4 = reinterpret_cast<const float4*>(xb32 + (bh * F + fi - 1) * int64_t(D) * DV);
+#pragma unroll 4
+      for (int m = 0; m < D * DV / 4 / kThreads; ++m) {
+        const int qi = m * kThreads + tid;
+        const float4 a = xf4[qi], b = xb4[qi];
+        const int blk = qi >> 6;
+        const int i0 = (blk % (D / 16)) * 16 + ((qi >> 4) & 3) * 4, j = (blk / (D / 16)) * 16 + (qi & 15);
+        *reinterpret_cast<uint2*>(stage + j * C::TROW + i0) =
+            make_uint2(pack_bf16x2(0.5f * (a.x + b.x), 0.5f * (a.y + b.y)),
+                       pack_bf16x2(0.5f * (a.z + b.z), 0.5f * (a.w + b.w)));
+      }
+      __syncthreads();
+      if constexpr (DQ) {
+#pragma unroll
+        for (int kb = 0; kb < DV / 16; ++kb) wq[kb] = frag(stage + 16 * kb * C::TROW, 32 * wave);
+      }
+      __syncthreads();
+    }
     store_rows(0, ra);
     __syncthreads();
     for (int64_t ch = 0; ch < nchunks; ch += 2) {
       mult_load(0, ch + 2, ra);
       store_rows(1, rn);
       __syncthreads();
+      if constexpr (DQ) {
+        if (dq_on) dq_flush(0, ch);
+      }
       mult_load(1, ch + 3, rn);
       store_rows(0, ra);
       __syncthreads();
+      if constexpr (DQ) {
+        if (dq_on) dq_flush(1, ch + 1);
+      }
     }
   } else {
     Raw r[8];
@@ -728,16 +809,20 @@ hipError_t launch_stats_t(const Problem& p, const void* k, const void* v, const 
       hipLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(kThreads), lds, s,
                          static_cast<const In*>(k), static_cast<const In*>(v),
                          static_cast<const In*>(tk), static_cast<const In*>(tv), p.ainv, p.bm, p.F,
-                         p.n, p.T, p.lam);
+                         p.n, p.T, p.lam, nullptr, nullptr, nullptr);
       return hipGetLastError();
     };
     if (prepare && !p.fp8) {
-      const hipError_t e = launch(stats_bf16_kernel<D, DV, uint16_t, false>, uint16_t{});
+      const hipError_t e = launch(stats_bf16_kernel<D, DV, uint16_t, kStatsBm>, uint16_t{});
       if (e != hipSuccess) return e;
+      if constexpr (D == 128 && DV == 128) {
+        const hipError_t e2 = launch(stats_bf16_kernel<D, DV, uint16_t, kStatsBmDq>, uint16_t{});
+        if (e2 != hipSuccess) return e2;
+      }
     }
     if (p.bm_only) {
       if (p.fp8) return hipErrorInvalidValue;
-      return launch(stats_bf16_kernel<D, DV, uint16_t, false>, uint16_t{});
+      return launch(stats_bf16_kernel<D, DV, uint16_t, kStatsBm>, uint16_t{});
     }
     return p.fp8 ? launch(stats_bf16_kernel<D, DV, uint8_t>, uint8_t{})
                  : launch(stats_bf16_kernel<D, DV, uint16_t>, uint16_t{});
@@ -768,6 +853,17 @@ hipError_t launch_stats(const Problem& p, const void* k, const void* v, const vo
   VDA_CASE(128, 32) VDA_CASE(128, 64) VDA_CASE(128, 128)
 #undef VDA_CASE
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_stats_dq(const Problem& p, const void* q, const void* d_out, const float* xf32,
+                           const float* xb32, void* d_q, hipStream_t s) {
+  if (!(p.d == 128 && p.dv == 128 && p.bf16 && !p.fp8 && p.T == 0)) return hipErrorInvalidValue;
+  const int64_t blocks = p.B * p.H * (p.F + 1);
+  constexpr int lds = StatsBf16<128, 128>::LDS_BYTES;
+  hipLaunchKernelGGL((stats_bf16_kernel<128, 128, uint16_t, kStatsBmDq>), dim3(unsigned(blocks)), dim3(kThreads),
+                     lds, s, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(d_out), nullptr,
+                     nullptr, nullptr, p.bm, p.F, p.n, int64_t(0), p.lam, xf32, xb32, static_cast<uint16_t*>(d_q));
+  return hipGetLastError();
 }
 
 hipError_t prepare_stats(const Problem& p) {

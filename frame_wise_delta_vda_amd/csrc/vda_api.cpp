@@ -301,7 +301,8 @@ BwdLayout bwd_layout(const vda::Problem& p) {
   L.xb = take(BH * F * d * dv * 4);
   L.sf = take(BH * F * d * dv * 4);
   L.sb = take(BH * F * d * dv * 4);
-  L.wt = take(BH * F * dv * d * 2);
+  // W^T for the dQ readout; at d = dv = 128 dQ is formed with dW and needs none
+  L.wt = take(p.d == 128 && p.dv == 128 ? 0 : BH * F * dv * d * 2);
   L.db2 = take(BH * F * 2 * d * dv * 2);
   L.z = take(BH * F * (2 * d + 2 * dv) * d * 2);
   L.db2_text = take(BH * 2 * d * dv * 2);
@@ -394,43 +395,54 @@ vda_status vda_backward(vda_plan_t plan, const void* q, const void* k, const voi
   auto mark = [&](int slot) {
     if (tev != nullptr && e == hipSuccess) e = hipEventRecord(tev[slot], s);
   };
-  // 1. dW_f = Q_f^T dO_f: the statistics stage on (Q, dO), Bm only, with no text (frame 0
-  //    is zero)
-  mark(kEvStatsBegin);
+  // The forward states again, in float32 (the forward pass keeps them in bf16): the scan on
+  // the forward's statistics with float32 state stores.
+  vda::Problem px = p;
+  px.states_f32 = true;
+  px.xf = f32(L.xf);
+  px.xb = f32(L.xb);
+  // dW_f = Q_f^T dO_f: the statistics stage on (Q, dO), Bm only, with no text (frame 0 is zero)
   vda::Problem pw = p;
   pw.T = 0;
   pw.bm_only = true;
   pw.ainv = nullptr;
   pw.bm = f32(L.dw);
-  e = vda::launch_stats(pw, q, d_out, nullptr, nullptr, s);
+  // At d = dv = 128 one pass over (Q, dO) forms dW and dQ = dO W^T (W from the float32
+  // states), so the recomputed states come first; elsewhere dQ is a readout of W^T from the
+  // per-frame kernel.
+  const bool fused_dq = p.d == 128 && p.dv == 128;
+  mark(kEvStatsBegin);
+  if (fused_dq) {
+    e = vda::launch_scan(px, s);
+    if (e == hipSuccess) e = vda::launch_stats_dq(pw, q, d_out, f32(L.xf), f32(L.xb), d_q, s);
+  } else {
+    e = vda::launch_stats(pw, q, d_out, nullptr, nullptr, s);
+  }
   mark(kEvStatsEnd);
-  // 2. the forward states again, in float32 (the forward pass keeps them in bf16), and the
-  //    adjoint chains (twice the adjoints): the scan on (A^{-1} of the forward, dW), float32
-  //    states; then the per-frame terms
+  // the adjoint chains (twice the adjoints): the scan on (A^{-1} of the forward, dW), float32
+  // states; then the per-frame terms
   mark(kEvScanBegin);
-  vda::Problem px = p;
-  px.states_f32 = true;
-  px.xf = f32(L.xf);
-  px.xb = f32(L.xb);
-  if (e == hipSuccess) e = vda::launch_scan(px, s);
+  if (!fused_dq && e == hipSuccess) e = vda::launch_scan(px, s);
   vda::Problem ps = p;
   ps.states_f32 = true;
   ps.bm = f32(L.dw);
   ps.xf = f32(L.sf);
   ps.xb = f32(L.sb);
   if (e == hipSuccess) e = vda::launch_scan(ps, s);
-  vda::BwdProblem b{p, f32(L.xf), f32(L.xb), f32(L.sf), f32(L.sb), u16(L.wt), u16(L.db2), u16(L.z),
-                    u16(L.db2_text), u16(L.z_text)};
+  vda::BwdProblem b{p, f32(L.xf), f32(L.xb), f32(L.sf), f32(L.sb), fused_dq ? nullptr : u16(L.wt), u16(L.db2),
+                    u16(L.z), u16(L.db2_text), u16(L.z_text)};
   if (e == hipSuccess) e = vda::launch_bwd_frames(b, s);
   mark(kEvScanEnd);
-  // 3. the gradient products: dQ = dO W^T, dV = [K K] [dB hi ; lo],
-  //    dK = [K K V V] [M hi ; M lo ; dB^T hi ; dB^T lo]
+  // the gradient products: dQ = dO W^T (unless formed above), dV = [K K] [dB hi ; lo],
+  // dK = [K K V V] [M hi ; M lo ; dB^T hi ; dB^T lo]
   mark(kEvReadBegin);
-  vda::Problem pq = p;
-  pq.d = p.dv;
-  pq.dv = p.d;
-  pq.xf = pq.xb = f32(L.wt);
-  if (e == hipSuccess) e = vda::launch_readout(pq, d_out, d_q, s);
+  if (!fused_dq) {
+    vda::Problem pq = p;
+    pq.d = p.dv;
+    pq.dv = p.d;
+    pq.xf = pq.xb = f32(L.wt);
+    if (e == hipSuccess) e = vda::launch_readout(pq, d_out, d_q, s);
+  }
   if (e == hipSuccess) e = vda::launch_grad_kv(p, k, v, u16(L.z), u16(L.db2), d_k, d_v, s);
   if (p.T > 0) {
     vda::Problem pt = p;

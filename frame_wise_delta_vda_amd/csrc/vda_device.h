@@ -213,6 +213,11 @@ template <int CPOL = kCacheDefault>
 __device__ __forceinline__ void buffer_store16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, uint4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)byte_off, 0, CPOL);
 }
+template <int CPOL = kCacheDefault>
+__device__ __forceinline__ void buffer_store8(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, uint2 v) {
+  typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, v), r, (int)byte_off, 0, CPOL);
+}
 
 // Workgroup index remap so that consecutive logical indices land on one XCD.
 // Hardware deals workgroup id w to XCD w % 8; logical index i = xcd * per + slot.

@@ -31,6 +31,11 @@ struct Problem {
 hipError_t launch_stats(const Problem& p, const void* k, const void* v, const void* tk,
                         const void* tv, hipStream_t stream);
 hipError_t launch_scan(const Problem& p, hipStream_t stream);
+// Backward pass, d = dv = 128: dW_f = Q_f^T dO_f into p.bm (frame 0 zero; p.T must be 0) and,
+// from the same pass over dO, dQ_f = dO_f W_f^T with W_f the mean of the float32 blocked
+// states xf32 / xb32.
+hipError_t launch_stats_dq(const Problem& p, const void* q, const void* d_out, const float* xf32,
+                           const float* xb32, void* d_q, hipStream_t stream);
 hipError_t launch_readout(const Problem& p, const void* q, void* out, hipStream_t stream);
 // Weights of the gated fusion epilogue (bfloat16 [H][dv][dv] matrices, float32 [H][dv] bias).
 struct GateWeights {
