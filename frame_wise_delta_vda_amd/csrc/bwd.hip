@@ -36,6 +36,11 @@ __device__ __forceinline__ void chunk_rc(int q, int& row0, int& col) {
 // bf16 hi / lo of x: hi = rne(x), lo = rne(x - hi)
 __device__ __forceinline__ float lo_part(float x) { return x - bf16_bits_to_f32(f32_to_bf16_bits(x)); }
 
+// Threads of a per-frame workgroup: 8 waves, so the float32 state loads, conversions and
+// stores that dominate a frame have twice the work in flight that 4 waves had at one
+// workgroup per CU (the planes take 139 KB of LDS).
+constexpr int kBwdThreads = 512;
+
 template <int D, int DV>
 struct BwdFrame {
   static constexpr int TR = D + 8;                // bf16 per LDS plane row (row c: value feature c)
@@ -73,7 +78,7 @@ __device__ __forceinline__ void frame_terms(const float* __restrict__ xf, const 
   };
   uint16_t* dbf = db2 + fr * int64_t(2 * D) * DV;
   uint16_t* zf = z + fr * int64_t(C::ZR) * D;
-  for (int u = tid; u < (D / 4) * (DV / 8); u += kThreads) {
+  for (int u = tid; u < (D / 4) * (DV / 8); u += kBwdThreads) {
     const int i0 = 4 * (u % (D / 4)), c0 = 8 * (u / (D / 4));
     float4 xf4[8], xb4[8], sf4[8], sb4[8];
 #pragma unroll
@@ -105,7 +110,7 @@ __device__ __forceinline__ void frame_terms(const float* __restrict__ xf, const 
       reinterpret_cast<uint4*>(zf)[chunk_of(2 * D + DV + c0, i0 + r, C::ZR)] = make_uint4(l[0], l[1], l[2], l[3]);
     }
   }
-  for (int u = tid; u < (D / 8) * DV; u += kThreads) {  // DB2: rows i0..i0+7 of column c, hi and lo
+  for (int u = tid; u < (D / 8) * DV; u += kBwdThreads) {  // DB2: rows i0..i0+7 of column c, hi and lo
     const int i0 = 8 * (u % (D / 8)), c = u / (D / 8);
     const int e0 = blk_index(i0, c, D) / 4, e1 = blk_index(i0 + 4, c, D) / 4;
     const float4 s0 = reinterpret_cast<const float4*>(SB)[e0], t0 = reinterpret_cast<const float4*>(SF)[e0];
@@ -133,7 +138,7 @@ __device__ __forceinline__ void frame_terms(const float* __restrict__ xf, const 
   constexpr int PL = DV * TR;  // bf16 per plane
   uint16_t* pl = reinterpret_cast<uint16_t*>(smem);  // [S hi, S lo, X hi, X lo]
   auto load_planes = [&](const float* M, uint16_t* hi, uint16_t* lo) {
-    for (int g = tid; g < D * DV / 4; g += kThreads) {
+    for (int g = tid; g < D * DV / 4; g += kBwdThreads) {
       const int c15 = g & 15, t = g >> 4, q4 = t & 3, u = t >> 2;
       const int i = (u % (D / 16)) * 16 + q4 * 4, c = (u / (D / 16)) * 16 + c15;
       const float4 x = reinterpret_cast<const float4*>(M)[g];  // rows i..i+3 of column c
@@ -156,7 +161,8 @@ __device__ __forceinline__ void frame_terms(const float* __restrict__ xf, const 
     return make_uint4(xl.x, xl.y, yl.x, yl.y);
   };
   constexpr int NT = D / 32;              // 32 x 32 tiles per side of P
-  constexpr int TPW = NT * NT / 4 > 0 ? NT * NT / 4 : 1;  // tiles per wave
+  constexpr int NW = kBwdThreads / 64;
+  constexpr int TPW = NT * NT / NW > 0 ? NT * NT / NW : 1;  // tiles per wave
   f32x16 acc[TPW];
 #pragma unroll
   for (int t = 0; t < TPW; ++t) acc[t] = f32x16{};
@@ -200,7 +206,7 @@ __device__ __forceinline__ void frame_terms(const float* __restrict__ xf, const 
   __syncthreads();
 
   // 3. Z rows 0..2D-1: M = dA + dA^T = -(P + P^T) / 2, hi then lo
-  for (int qc = tid; qc < C::ZR * D / 8; qc += kThreads) {
+  for (int qc = tid; qc < C::ZR * D / 8; qc += kBwdThreads) {
     int r0, c;
     chunk_rc<C::ZR>(qc, r0, c);
     if (r0 >= 2 * D) continue;
@@ -243,20 +249,21 @@ __device__ __forceinline__ void text_terms(const uint16_t* __restrict__ ainv, co
   const int64_t F1 = F + 1;
   const uint16_t* hi = ainv + bh * F1 * int64_t(2 * D * D);
   const uint16_t* lo = hi + sym_blocks(D) * 256;
-  for (int e = tid; e < D * D; e += kThreads) {
+  for (int e = tid; e < D * D; e += kBwdThreads) {
     const int r = e / D, c = e % D;
     const int rr = (r >> 4) <= (c >> 4) ? r : c, cc = (r >> 4) <= (c >> 4) ? c : r;
     const int idx = sym_index(rr, cc, D);
     LA[r * C::AROW + c] = bf16_bits_to_f32(hi[idx]) + bf16_bits_to_f32(lo[idx]);
   }
   const float* bm0 = bm + bh * F1 * int64_t(D) * DV;
-  for (int e = tid; e < D * DV; e += kThreads) {
+  for (int e = tid; e < D * DV; e += kBwdThreads) {
     const int r = e / DV, c = e % DV;
     LR[r * C::RROW + c] = bm0[blk_index(r, c, D)];
   }
   __syncthreads();
   constexpr int RI = D / 16, RJ = DV / 16;
   const int ti = tid >> 4, tj = tid & 15;
+  const bool comp = tid < 256;  // the 8 x 8 blocks of the products: threads 0..255
   auto solve_product = [&](float (&y)[RI][RJ]) {
 #pragma unroll
     for (int a = 0; a < RI; ++a)
@@ -272,45 +279,47 @@ __device__ __forceinline__ void text_terms(const uint16_t* __restrict__ ainv, co
     }
   };
   float xt[RI][RJ], u0[RI][RJ];
-  solve_product(xt);                       // X_text
+  if (comp) solve_product(xt);             // X_text
   __syncthreads();
   // Gamma = lam (S_bwd_1 + S_fwd_F) / 2 (frame f of a chain at index f - 1)
   const float* s1 = sb + (bh * F + 0) * int64_t(D) * DV;
   const float* sF = sf + (bh * F + (F - 1)) * int64_t(D) * DV;
-  for (int e = tid; e < D * DV; e += kThreads) {
+  for (int e = tid; e < D * DV; e += kBwdThreads) {
     const int r = e / DV, c = e % DV;
     const int idx = blk_index(r, c, D);
     LR[r * C::RROW + c] = 0.5f * lam * (s1[idx] + sF[idx]);
   }
   __syncthreads();
-  solve_product(u0);                       // U_0
+  if (comp) solve_product(u0);             // U_0
   __syncthreads();
+  if (comp) {
 #pragma unroll
-  for (int a = 0; a < RI; ++a)
+    for (int a = 0; a < RI; ++a)
 #pragma unroll
-    for (int b = 0; b < RJ; ++b) {
-      LU[(ti * RI + a) * C::RROW + tj * RJ + b] = u0[a][b];
-      LR[(ti * RI + a) * C::RROW + tj * RJ + b] = xt[a][b];
-    }
+      for (int b = 0; b < RJ; ++b) {
+        LU[(ti * RI + a) * C::RROW + tj * RJ + b] = u0[a][b];
+        LR[(ti * RI + a) * C::RROW + tj * RJ + b] = xt[a][b];
+      }
+  }
   __syncthreads();
   auto put = [&](uint16_t* dst, int r, int c, int R, float x) {  // hi at row r, lo at row r + R
     dst[state_index(r, c, 2 * R)] = uint16_t(f32_to_bf16_bits(x));
     dst[state_index(r + R, c, 2 * R)] = uint16_t(f32_to_bf16_bits(lo_part(x)));
   };
   uint16_t* dbt = db2_text + bh * int64_t(2 * D) * DV;
-  for (int e = tid; e < D * DV; e += kThreads) {
+  for (int e = tid; e < D * DV; e += kBwdThreads) {
     const int r = e / DV, c = e % DV;
     put(dbt, r, c, D, LU[r * C::RROW + c]);
   }
   constexpr int ZR = 2 * D + 2 * DV;
   uint16_t* zt = z_text + bh * int64_t(ZR) * D;
-  for (int e = tid; e < DV * D; e += kThreads) {  // rows 2D + c (hi), 2D + DV + c (lo): U_0^T
+  for (int e = tid; e < DV * D; e += kBwdThreads) {  // rows 2D + c (hi), 2D + DV + c (lo): U_0^T
     const int c = e / D, i = e % D;
     const float x = LU[i * C::RROW + c];
     zt[state_index(2 * D + c, i, ZR)] = uint16_t(f32_to_bf16_bits(x));
     zt[state_index(2 * D + DV + c, i, ZR)] = uint16_t(f32_to_bf16_bits(lo_part(x)));
   }
-  for (int e = tid; e < D * D; e += kThreads) {  // rows i (hi), D + i (lo): M = -(P + P^T)
+  for (int e = tid; e < D * D; e += kBwdThreads) {  // rows i (hi), D + i (lo): M = -(P + P^T)
     const int i = e / D, j = e % D;
     float pij = 0.0f, pji = 0.0f;
     for (int c = 0; c < DV; ++c) {
@@ -326,7 +335,7 @@ __device__ __forceinline__ void text_terms(const uint16_t* __restrict__ ainv, co
 // One launch for both: the text workgroups (one per head) come first in the grid, so they
 // run beside the frame workgroups instead of after them.
 template <int D, int DV>
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(kBwdThreads)
 bwd_frames_kernel(const float* __restrict__ xf, const float* __restrict__ xb,
                   const float* __restrict__ sf, const float* __restrict__ sb,
                   uint16_t* __restrict__ wt, uint16_t* __restrict__ db2, uint16_t* __restrict__ z,
@@ -350,7 +359,7 @@ hipError_t launch_bwd_frames_t(const BwdProblem& b, hipStream_t s, bool prepare)
   const int64_t BH = b.p.B * b.p.H;
   if (BH == 0 || b.p.F == 0) return hipSuccess;
   const int64_t text_blocks = b.p.T > 0 ? BH : 0;
-  hipLaunchKernelGGL(kern, dim3(unsigned(text_blocks + BH * b.p.F)), dim3(kThreads), lds, s, b.xf32, b.xb32,
+  hipLaunchKernelGGL(kern, dim3(unsigned(text_blocks + BH * b.p.F)), dim3(kBwdThreads), lds, s, b.xf32, b.xb32,
                      b.sf, b.sb, b.wt, b.db2, b.z, reinterpret_cast<const uint16_t*>(b.p.ainv), b.p.bm,
                      b.db2_text, b.z_text, b.p.F, b.p.lam, text_blocks);
   return hipGetLastError();
