@@ -413,9 +413,9 @@ vda_status vda_backward(vda_plan_t plan, const void* q, const void* k, const voi
   const bool fused_dq = p.d == 128 && p.dv == 128;
   mark(kEvStatsBegin);
   if (fused_dq) {
-    e = vda::launch_scan(px, s);
+    if (e == hipSuccess) e = vda::launch_scan(px, s);
     if (e == hipSuccess) e = vda::launch_stats_dq(pw, q, d_out, f32(L.xf), f32(L.xb), d_q, s);
-  } else {
+  } else if (e == hipSuccess) {
     e = vda::launch_stats(pw, q, d_out, nullptr, nullptr, s);
   }
   mark(kEvStatsEnd);

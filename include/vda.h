@@ -143,8 +143,9 @@ vda_status vda_forward_gated(vda_plan_t plan, const void* q, const void* k, cons
  * then dB_f = U_f + V_f, dA_f = -(U_f X_fwd_f^T + V_f X_bwd_f^T),
  * dK_f = V_f dB_f^T + K_f (dA_f + dA_f^T), dV_f = K_f dB_f, dQ_f = dO_f W_f^T, and the text
  * gets the same terms from U_0 = A_0^{-1} lam (U_1 + V_F).
- * The call reads the statistics and states that the last vda_forward (or
- * vda_forward_gated) on this plan left in its workspace: run the forward pass first,
+ * The call reads the statistics (the inverses and K^T V of every frame) that the last
+ * vda_forward (or vda_forward_gated) on this plan left in its workspace, and recomputes the
+ * states from them in float32: run the forward pass first,
  * with the same k, v, text_k, text_v, and keep the plan's workspace untouched in between.
  * On a plan whose workspace holds no statistics yet (no forward pass enqueued) the call
  * returns INVALID_VALUE.
@@ -155,8 +156,10 @@ vda_status vda_forward_gated(vda_plan_t plan, const void* q, const void* k, cons
  * make no runtime call but kernel launches and may be captured.  Outputs may not overlap
  * inputs or each other.  With no output element (F or n = 0) every gradient is zero.
  * When timing is enabled (vda_plan_enable_timing) a backward call is recorded as one
- * timed pass whose three spans are the Q^T dO statistics, the adjoint chains with the
- * per-frame terms, and the gradient products.
+ * timed pass with three spans.  At d = dv = 128: the state recompute with one pass over
+ * (Q, dO) that forms Q^T dO and dQ; the adjoint chains with the per-frame terms; dK and dV.
+ * At other widths: Q^T dO; the state recompute, the adjoint chains and the per-frame terms;
+ * dQ, dK and dV.
  * Errors: INVALID_VALUE, MISALIGNED, OUT_OF_MEMORY, DEVICE; NOT_SUPPORTED for float32 and
  * FP8 plans. */
 vda_status vda_backward(vda_plan_t plan, const void* q, const void* k, const void* v,
