@@ -70,6 +70,11 @@ SMALL = [
     ("b_split_frames", dict(d=128, dv=128, n=4000, T=10, F=2, B=1, H=1)),
     ("b_F1", dict(d=64, dv=64, n=333, T=20, F=1, B=1, H=2)),
     ("b_lowrank_lam_small", dict(d=128, dv=128, n=300, T=16, F=6, B=1, H=1, kind="lowrank", lam=0.05)),
+    # at d = dv = 128 dQ is formed in the Q^T dO pass, 64 tokens a chunk: a frame shorter than
+    # one chunk, a one-token frame, one frame
+    ("b_128x128_short", dict(d=128, dv=128, n=37, T=4, F=3, B=1, H=2)),
+    ("b_128x128_n1", dict(d=128, dv=128, n=1, T=2, F=4, B=1, H=1)),
+    ("b_128x128_F1", dict(d=128, dv=128, n=129, T=7, F=1, B=2, H=1)),
 ]
 
 
