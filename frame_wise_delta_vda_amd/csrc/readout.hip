@@ -871,10 +871,10 @@ hipError_t launch_readout_t(const Problem& p, const void* q, void* out, hipStrea
     const ReadGrid gr = readout_grid(frames, (p.n + C::TT - 1) / C::TT, p.num_cus);
     auto launch = [&](auto kern, auto in) {
       using In = decltype(in);
-      hipLaunchKernelGGL(kern, dim3(unsigned(gr.grid)), dim3(kThreads), C::LDS_BYTES, s,
-                         static_cast<const In*>(q), reinterpret_cast<const uint16_t*>(p.xf),
-                         reinterpret_cast<const uint16_t*>(p.xb), static_cast<uint16_t*>(out),
-                         p.n, gr.tpf, gr.splits, gr.tps, gr.head_blocks, gr.tail_splits, gr.tail_tps);
+      launch_kernel(p, kern, dim3(unsigned(gr.grid)), dim3(kThreads), C::LDS_BYTES, s,
+                    static_cast<const In*>(q), reinterpret_cast<const uint16_t*>(p.xf),
+                    reinterpret_cast<const uint16_t*>(p.xb), static_cast<uint16_t*>(out),
+                    p.n, gr.tpf, gr.splits, gr.tps, gr.head_blocks, gr.tail_splits, gr.tail_tps);
     };
     if (p.fp8) launch(readout_bf16_kernel<D, DV, uint8_t>, uint8_t{});
     else launch(readout_bf16_kernel<D, DV, uint16_t>, uint16_t{});
@@ -891,9 +891,9 @@ hipError_t launch_readout_t(const Problem& p, const void* q, void* out, hipStrea
       return lds > 65536 ? hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                hipFuncAttributeMaxDynamicSharedMemorySize, lds)
                          : hipSuccess;
-    hipLaunchKernelGGL(kern, dim3(unsigned(grid)), dim3(kThreads), lds, s,
-                       static_cast<const float*>(q), p.xf, p.xb, static_cast<float*>(out), p.n,
-                       splits, tps);
+    launch_kernel(p, kern, dim3(unsigned(grid)), dim3(kThreads), lds, s,
+                  static_cast<const float*>(q), p.xf, p.xb, static_cast<float*>(out), p.n,
+                  splits, tps);
   }
   return hipGetLastError();
 }
@@ -908,12 +908,12 @@ hipError_t launch_readout_gated_t(const Problem& p, const void* q, const GateWei
   const ReadGrid gr = readout_grid(p.B * p.H * p.F, (p.n + C::TT - 1) / C::TT, p.num_cus);
   auto launch = [&](auto kern, auto in) {
     using In = decltype(in);
-    hipLaunchKernelGGL(kern, dim3(unsigned(gr.grid)), dim3(kThreads), C::LDS_BYTES, s,
-                       static_cast<const In*>(q), reinterpret_cast<const uint16_t*>(p.xf),
-                       reinterpret_cast<const uint16_t*>(p.xb),
-                       static_cast<const uint16_t*>(gw.w_gate), static_cast<const float*>(gw.b_gate),
-                       static_cast<const uint16_t*>(gw.w_out), static_cast<uint16_t*>(out), p.n, p.F,
-                       p.H, gr.tpf, gr.splits, gr.tps, gr.head_blocks, gr.tail_splits, gr.tail_tps);
+    launch_kernel(p, kern, dim3(unsigned(gr.grid)), dim3(kThreads), C::LDS_BYTES, s,
+                  static_cast<const In*>(q), reinterpret_cast<const uint16_t*>(p.xf),
+                  reinterpret_cast<const uint16_t*>(p.xb),
+                  static_cast<const uint16_t*>(gw.w_gate), static_cast<const float*>(gw.b_gate),
+                  static_cast<const uint16_t*>(gw.w_out), static_cast<uint16_t*>(out), p.n, p.F,
+                  p.H, gr.tpf, gr.splits, gr.tps, gr.head_blocks, gr.tail_splits, gr.tail_tps);
   };
   if (p.fp8) launch(readout_gated_kernel<D, DV, uint8_t>, uint8_t{});
   else launch(readout_gated_kernel<D, DV, uint16_t>, uint16_t{});

@@ -394,16 +394,16 @@ hipError_t launch_scan_t(const Problem& p, hipStream_t s, bool prepare) {
                                                         C::LDS_BYTES)
                                   : hipSuccess;
     const int64_t grid = ((nchains + kXcds - 1) / kXcds) * kXcds * C::NCB;
-    hipLaunchKernelGGL(kern, dim3(unsigned(grid)), dim3(C::THREADS), C::LDS_BYTES, s,
-                       reinterpret_cast<const uint16_t*>(p.ainv), p.bm, p.xf, p.xb, nchains, p.F,
-                       p.lam, grid,
-                       p.states_f32 ? kStoreF32 : (p.fp8 && D >= 64) ? kStorePairedBf16 : kStoreBf16);
+    launch_kernel(p, kern, dim3(unsigned(grid)), dim3(C::THREADS), C::LDS_BYTES, s,
+                  reinterpret_cast<const uint16_t*>(p.ainv), p.bm, p.xf, p.xb, nchains, p.F,
+                  p.lam, grid,
+                  p.states_f32 ? kStoreF32 : (p.fp8 && D >= 64) ? kStorePairedBf16 : kStoreBf16);
   } else {
     using C = ScanCfg<D, DV>;
     if (prepare) return hipSuccess;  // static LDS only
     const int64_t grid = ((nchains + kXcds - 1) / kXcds) * kXcds * C::NCB;
-    hipLaunchKernelGGL((scan_kernel<D, DV>), dim3(unsigned(grid)), dim3(kThreads), 0, s, p.ainv,
-                       p.bm, p.xf, p.xb, nchains, p.F, p.lam, grid);
+    launch_kernel(p, scan_kernel<D, DV>, dim3(unsigned(grid)), dim3(kThreads), 0, s, p.ainv,
+                  p.bm, p.xf, p.xb, nchains, p.F, p.lam, grid);
   }
   return hipGetLastError();
 }

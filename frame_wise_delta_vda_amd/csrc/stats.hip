@@ -806,10 +806,11 @@ hipError_t launch_stats_t(const Problem& p, const void* k, const void* v, const 
         return lds > 65536 ? hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize, lds)
                            : hipSuccess;
-      hipLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(kThreads), lds, s,
-                         static_cast<const In*>(k), static_cast<const In*>(v),
-                         static_cast<const In*>(tk), static_cast<const In*>(tv), p.ainv, p.bm, p.F,
-                         p.n, p.T, p.lam, nullptr, nullptr, nullptr);
+      launch_kernel(p, kern, dim3(unsigned(blocks)), dim3(kThreads), lds, s,
+                    static_cast<const In*>(k), static_cast<const In*>(v),
+                    static_cast<const In*>(tk), static_cast<const In*>(tv), p.ainv, p.bm, p.F,
+                    p.n, p.T, p.lam, static_cast<const float*>(nullptr), static_cast<const float*>(nullptr),
+                    static_cast<uint16_t*>(nullptr));
       return hipGetLastError();
     };
     if (prepare && !p.fp8) {
@@ -834,10 +835,10 @@ hipError_t launch_stats_t(const Problem& p, const void* k, const void* v, const 
       return lds > 65536 ? hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                hipFuncAttributeMaxDynamicSharedMemorySize, lds)
                          : hipSuccess;
-    hipLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(kThreads), lds, s,
-                       static_cast<const float*>(k), static_cast<const float*>(v),
-                       static_cast<const float*>(tk), static_cast<const float*>(tv), p.ainv, p.bm,
-                       p.F, p.n, p.T, p.lam);
+    launch_kernel(p, kern, dim3(unsigned(blocks)), dim3(kThreads), lds, s,
+                  static_cast<const float*>(k), static_cast<const float*>(v),
+                  static_cast<const float*>(tk), static_cast<const float*>(tv), p.ainv, p.bm,
+                  p.F, p.n, p.T, p.lam);
   }
   return hipGetLastError();
 }

@@ -260,19 +260,21 @@ vda_status enqueue(vda_plan_t plan, unsigned stages, const void* q, const void* 
   hipEvent_t* tev = nullptr;
   if (stages == VDA_STAGE_ALL && plan->timing_capacity > 0 && plan->timed_calls < plan->timing_capacity)
     tev = plan->timing_events + size_t(plan->timed_calls) * kTimingEvents;
-  auto mark = [&](int slot) {
-    if (tev != nullptr && e == hipSuccess) e = hipEventRecord(tev[slot], s);
+  // each stage is one kernel launch, which records the stage's two events itself
+  auto timed = [&](int begin, int end) {
+    vda::Problem ps = p;
+    if (tev != nullptr) {
+      ps.ev_start = tev[begin];
+      ps.ev_stop = tev[end];
+    }
+    return ps;
   };
-  mark(kEvStatsBegin);
-  if (do_stats) e = vda::launch_stats(p, k, v, text_k, text_v, s);
-  mark(kEvStatsEnd);
-  mark(kEvScanBegin);
-  if (e == hipSuccess && do_scan) e = vda::launch_scan(p, s);
-  mark(kEvScanEnd);
-  mark(kEvReadBegin);
-  if (e == hipSuccess && do_read)
-    e = gate ? vda::launch_readout_gated(p, q, *gate, out, s) : vda::launch_readout(p, q, out, s);
-  mark(kEvReadEnd);
+  if (do_stats) e = vda::launch_stats(timed(kEvStatsBegin, kEvStatsEnd), k, v, text_k, text_v, s);
+  if (e == hipSuccess && do_scan) e = vda::launch_scan(timed(kEvScanBegin, kEvScanEnd), s);
+  if (e == hipSuccess && do_read) {
+    const vda::Problem pr = timed(kEvReadBegin, kEvReadEnd);
+    e = gate ? vda::launch_readout_gated(pr, q, *gate, out, s) : vda::launch_readout(pr, q, out, s);
+  }
   if (tev != nullptr && e == hipSuccess) ++plan->timed_calls;
   if (e != hipSuccess) {
     (void)hipGetLastError();

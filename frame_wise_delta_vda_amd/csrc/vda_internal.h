@@ -1,6 +1,7 @@
 // Internal interface between the C ABI layer (vda_api.cpp) and the HIP kernels.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <cstddef>
 #include <cstdint>
@@ -25,7 +26,20 @@ struct Problem {
   float* bm;        // [BH][F+1][d][dv]
   float* xf;        // [BH][F][d][dv]; bf16 plans: bf16 elements in state_index order
   float* xb;        // [BH][F][d][dv]; likewise
+  // when set, the one kernel a forward stage launches records these around itself, inside its
+  // dispatch (per-stage timing without separate event packets between the kernels)
+  hipEvent_t ev_start = nullptr, ev_stop = nullptr;
 };
+
+// Launch a kernel of a forward stage, with the stage's timing events if the problem carries them.
+template <typename K, typename... Args>
+inline void launch_kernel(const Problem& p, K kern, dim3 grid, dim3 block, uint32_t lds, hipStream_t s,
+                          Args... args) {
+  if (p.ev_start != nullptr)
+    hipExtLaunchKernelGGL(kern, grid, block, lds, s, p.ev_start, p.ev_stop, 0u, args...);
+  else
+    hipLaunchKernelGGL(kern, grid, block, lds, s, args...);
+}
 
 // Each launcher enqueues one stage on `stream` and returns the launch status.
 hipError_t launch_stats(const Problem& p, const void* k, const void* v, const void* tk,

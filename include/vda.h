@@ -168,8 +168,9 @@ vda_status vda_backward(vda_plan_t plan, const void* q, const void* k, const voi
 
 /* Per-stage timing of whole forward passes, for benchmarks.  After
  * vda_plan_enable_timing(plan, capacity) with capacity > 0, each of the next `capacity`
- * vda_forward calls brackets each stage's launch with HIP events on the stream it runs
- * on.  capacity == 0 turns timing off; enabling again discards what was recorded.  The
+ * vda_forward calls times each stage with a pair of HIP events on the stream it runs on,
+ * recorded by the stage's kernel launch itself (hipExtLaunchKernelGGL), so that no event
+ * packet sits between the kernels.  capacity == 0 turns timing off; enabling again discards what was recorded.  The
  * events are created on the current device, which must be the plan's.
  * Errors: INVALID_VALUE (capacity < 0 or > 100000), OUT_OF_MEMORY, DEVICE. */
 vda_status vda_plan_enable_timing(vda_plan_t plan, int capacity);
