@@ -576,17 +576,24 @@ stats_bf16_kernel(const In* __restrict__ k, const In* __restrict__ v,
 
   float* bmo = bm + (bh * F1 + fi) * int64_t(D) * DV;
   if constexpr (D == 128) {
-    // ---- epilogue (d = 128): Bm tiles to the workspace; lam I + G inverted in the
-    // accumulators by the blocked sweep; A^{-1} = -(swept matrix) written out.
+    // ---- epilogue (d = 128): lam I + G inverted in the accumulators by the blocked sweep;
+    // A^{-1} = -(swept matrix), then the Bm tiles (held in their accumulators through the
+    // sweep) written out together: a workgroup's outputs leave in one burst, and each burst of
+    // writes into the other workgroups' read stream costs read bandwidth.
     const int l32 = lane & 31;
-    if (wave < C::NV) {
+    auto store_bm = [&] {
+      if (wave < C::NV) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-          bmo[blk_index(32 * ((wave + i) & 3) + mfma32_row(e, lane), wave * 32 + l32, D)] = acc[3 + i][e];
+          for (int e = 0; e < 16; ++e)
+            bmo[blk_index(32 * ((wave + i) & 3) + mfma32_row(e, lane), wave * 32 + l32, D)] = acc[3 + i][e];
+      }
+    };
+    if constexpr (!GRAM) {
+      store_bm();
+      return;
     }
-    if constexpr (!GRAM) return;
     uint16_t* hi_plane = reinterpret_cast<uint16_t*>(ainv + (bh * F1 + fi) * int64_t(D) * D);
     uint16_t* lo_plane = hi_plane + sym_blocks(D) * 256;
     // G tiles (and the mirror of each off-diagonal one) -> LDS -> G row block in the
@@ -634,6 +641,7 @@ stats_bf16_kernel(const In* __restrict__ k, const In* __restrict__ v,
         *reinterpret_cast<uint2*>(hi_plane + off) = make_uint2(h01, h23);
         *reinterpret_cast<uint2*>(lo_plane + off) = make_uint2(l01, l23);
       }
+    store_bm();
     return;
   }
   // ---- epilogue: Bm tiles to the workspace, G tiles to LDS, then invert lam I + G
