@@ -14,6 +14,10 @@ Profiling helpers (used to produce the committed summaries under profiles/):
                                             calibrating rocprofv3 byte counters
     python bench.py --summarize-stats CSV   kernel_stats.csv -> text summary
     python bench.py --summarize-pmc FETCH_CSV WRITE_CSV COPY_FETCH_CSV COPY_WRITE_CSV
+    python bench.py --summarize-counters CSV  any counter pass -> per-kernel averages
+
+With the CPU leg on (the default), the output of the last timed pass is also compared with
+the oracle on every (b,h) slice the CPU leg computes ("parity" in the JSON line).
 """
 from __future__ import annotations
 
@@ -29,7 +33,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
-BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}  # dense MFMA, vendor figures
 KERNEL_SOURCES = {"stats": "stats.hip", "scan": "scan.hip", "readout": "readout.hip"}
 KERNEL_SYMBOLS = {"stats": "stats_bf16_kernel", "scan": "scan_bf16_kernel", "readout": "readout_bf16_kernel"}
 GATED_READOUT_SYMBOL = "readout_gated_kernel"  # the readout with the gated epilogue (--gated)
@@ -82,34 +86,78 @@ def read_traffic(workload_name):
     return out
 
 
-def cpu_baseline(w, arrays, budget_s=20.0, max_heads=None, gate=None):
+def host_cpu():
+    """(model name, usable cores, BLAS threads to use) of the host this runs on.  The cores are
+    the affinity mask's; where the environment caps the thread count (OMP_NUM_THREADS, set to
+    the per-GPU CPU share on shared boxes) the BLAS pool takes the smaller of the two."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    cores = len(os.sched_getaffinity(0))
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    threads = min(cores, int(cap)) if cap.isdigit() and int(cap) > 0 else cores
+    return model, cores, threads
+
+
+def cpu_baseline(w, arrays, budget_s=20.0, max_heads=None, gate=None, gpu_out=None):
     """Time the float64 oracle on whole (b,h) slices of the same inputs until ~budget_s
-    (with the gated epilogue when gate holds the weights as float64)."""
+    (with the gated epilogue when gate holds the weights as float64).  When gpu_out (the
+    timed GPU output, on the host) is given, every slice the oracle computed is also compared
+    with it: the max per-(b,h,frame) relative Frobenius error is returned with the baseline."""
     import numpy as np
     import threadpoolctl
     import oracle
     import workloads as W
 
-    info = threadpoolctl.threadpool_info()
-    threads = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
+    model, cores, threads = host_cpu()
     heads = [(b, h) for b in range(w.B) for h in range(w.H)][: max_heads or None]
-    spent, done = 0.0, 0
-    for b, h in heads:
-        x = {k: W.storage_to_float64(w, arrays[k][b, h]) for k in W.TENSORS}
-        t0 = time.perf_counter()
-        if gate is None:
-            oracle.vda_forward_head(x["q"], x["k"], x["v"], x["text_k"], x["text_v"], w.lam)
-        else:
-            oracle.vda_forward_gated_head(x["q"], x["k"], x["v"], x["text_k"], x["text_v"], w.lam,
-                                          gate["w_gate"][h], gate["b_gate"][h], gate["w_out"][h])
-        spent += time.perf_counter() - t0
-        done += 1
-        if spent >= budget_s:
-            break
+    spent, done, worst = 0.0, 0, 0.0
+    with threadpoolctl.threadpool_limits(limits=threads, user_api="blas"):
+        for b, h in heads:
+            x = {k: W.storage_to_float64(w, arrays[k][b, h]) for k in W.TENSORS}
+            t0 = time.perf_counter()
+            if gate is None:
+                ref = oracle.vda_forward_head(x["q"], x["k"], x["v"], x["text_k"], x["text_v"], w.lam)
+            else:
+                ref = oracle.vda_forward_gated_head(x["q"], x["k"], x["v"], x["text_k"], x["text_v"], w.lam,
+                                                    gate["w_gate"][h], gate["b_gate"][h], gate["w_out"][h])
+            spent += time.perf_counter() - t0
+            done += 1
+            if gpu_out is not None:
+                got = gpu_out[b, h].float().numpy().astype(np.float64)
+                diff = np.sqrt(np.sum((got - ref) ** 2, axis=(-2, -1)))
+                nrm = np.maximum(np.sqrt(np.sum(ref ** 2, axis=(-2, -1))), 1e-300)
+                worst = max(worst, float(np.max(diff / nrm)))
+            del x, ref
+            if spent >= budget_s:
+                break
     toks = done * w.F * w.n
-    return {"value": toks / spent, "unit": "video tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done} of {w.B * w.H} (b,h) slices of {w.name} ({toks} video tokens), "
-                      f"numpy float64, {spent:.1f} s"}
+    res = {"value": toks / spent, "unit": "video tokens/s", "cores": threads, "kind": "oracle",
+           "sample": f"{done} of {w.B * w.H} (b,h) slices of {w.name} ({toks} video tokens), "
+                     f"numpy float64, {spent:.1f} s",
+           "cpu_model": model, "host_cores": cores, "blas_threads": threads}
+    parity = None
+    if gpu_out is not None:
+        parity = {"max_rel_err": worst, "heads": done, "of_heads": w.B * w.H,
+                  "tol": 1e-4 if w.dtype == "f32" else 1e-2,
+                  "metric": "max over (b,h,frame) of ||O_gpu - O_oracle||_F / ||O_oracle||_F"}
+    return res, parity
+
+
+# Arithmetic of each stage, per input type (the contraction types the kernels use).
+ARITHMETIC = {
+    "f32": {"stats": "fp32 MFMA", "scan": "fp32 MFMA", "readout": "fp32 MFMA"},
+    "bf16": {"stats": "bf16 MFMA, fp32 accumulate; fp32 inverse", "scan": "split-bf16 MFMA (fp32 chain)",
+             "readout": "bf16 MFMA, fp32 accumulate"},
+    "fp8": {"stats": "fp8 e4m3 MFMA at d = dv = 128 (bf16 MFMA at other widths), fp32 accumulate; fp32 inverse",
+            "scan": "split-bf16 MFMA (fp32 chain)", "readout": "bf16 MFMA, fp32 accumulate"},
+}
 
 
 def to_device(w, arrays):
@@ -189,12 +237,21 @@ def run(args):
             entry.update({"alg_bytes": alg[n]["bytes"], "GB/s": round(gbs, 1),
                           "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)})
         entry["TFLOP/s"] = round(alg[n]["flops"] / (ms * 1e-3) / 1e12, 2)
+        # MFMA fraction against the dense peak of the stage's contraction type
+        peak = MFMA_PEAK_TFLOPS["fp8" if (n == "stats" and w.dtype == "fp8" and w.d == 128 and w.dv == 128)
+                                else "f32" if w.dtype == "f32" else "bf16"]
+        entry["mfma_frac"] = round(entry["TFLOP/s"] / peak, 4)
         entry["traffic"] = traffic.get(n)
         kernels[n] = entry
     dom = max(("stats", "readout"), key=lambda n: kern_ms[n])
     ach = kernels[dom]["GB/s"]
+    whole_gbs = w.algorithmic_bytes() / (ms_step * 1e-3) / 1e9
     roofline = {"kernel": dom, "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic.get(dom)}
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic.get(dom),
+                # the whole step (all three kernels and the gaps between them) against the same
+                # peak: the algorithmic bytes of the pass over the wall clock per step
+                "whole_step": {"achieved": round(whole_gbs, 1), "frac": round(whole_gbs / HBM_PEAK_GBS, 4),
+                               "ms": round(ms_step, 4)}}
     value = w.video_tokens / (ms_step * 1e-3)
     result = {
         "metric": "VDA forward video tokens/s at 768p shape; % of HBM/MFMA roofline",
@@ -207,10 +264,11 @@ def run(args):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        # arithmetic type of the path: FP8 inputs are converted to bfloat16 on load
-        "dtype": "f32" if w.dtype == "f32" else "bf16",
+        # arithmetic type of the path: FP8 inputs contract on the FP8 MFMA in the statistics
+        # (d = dv = 128) and are converted to bfloat16 for the readout
+        "dtype": {"f32": "f32", "bf16": "bf16", "fp8": "fp8_e4m3+bf16"}[w.dtype],
         "data": "synthetic",
-        "config": {"workload": w.name, "input_dtype": w.dtype,
+        "config": {"workload": w.name, "input_dtype": w.dtype, "arithmetic": ARITHMETIC[w.dtype],
                    "epilogue": "sigmoid gate and output projection per head" if args.gated else "none", "B": w.B, "H": w.H, "F": w.F, "n": w.n, "d": w.d, "dv": w.dv,
                    "T": w.T, "lambda": w.lam, "video_tokens_per_step": w.video_tokens,
                    "alg_bytes_per_step": w.algorithmic_bytes(),
@@ -219,11 +277,15 @@ def run(args):
         "kernels": kernels,
     }
     plan.close()
+    out_host = None if args.no_cpu_baseline else out.cpu()  # the output of the last timed pass
     del dev, out
     if not args.no_cpu_baseline:
         print(f"[bench] {w.name}: timing the oracle on host cores", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(w, arrays, budget_s=args.cpu_budget,
-                                              gate=W.gate_weights_float64(w, gate) if gate else None)
+        result["cpu_baseline"], result["parity"] = cpu_baseline(
+            w, arrays, budget_s=args.cpu_budget, gate=W.gate_weights_float64(w, gate) if gate else None,
+            gpu_out=out_host)
+        print(f"[bench] {w.name}: parity against the oracle on {result['parity']['heads']} heads: "
+              f"max rel err {result['parity']['max_rel_err']:.3e}", file=sys.stderr, flush=True)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
@@ -333,21 +395,22 @@ def run_backward(args):
     if not args.no_cpu_baseline:
         print(f"[bench] backward {w.name}: timing the oracle on host cores", file=sys.stderr, flush=True)
         import threadpoolctl
-        info = threadpoolctl.threadpool_info()
-        threads = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
+        model, cores, threads = host_cpu()
         spent, done = 0.0, 0
-        for h in range(w.H):
-            x = {kk: W.storage_to_float64(w, arrays[kk][0, h]) for kk in W.TENSORS}
-            dO = W.bf16_bits_to_float32(d_out_bits[0, h]).astype(np.float64)
-            t1 = time.perf_counter()
-            oracle.vda_backward_head(x["q"], x["k"], x["v"], x["text_k"], x["text_v"], w.lam, dO)
-            spent += time.perf_counter() - t1
-            done += 1
-            if spent >= args.cpu_budget:
-                break
+        with threadpoolctl.threadpool_limits(limits=threads, user_api="blas"):
+            for h in range(w.H):
+                x = {kk: W.storage_to_float64(w, arrays[kk][0, h]) for kk in W.TENSORS}
+                dO = W.bf16_bits_to_float32(d_out_bits[0, h]).astype(np.float64)
+                t1 = time.perf_counter()
+                oracle.vda_backward_head(x["q"], x["k"], x["v"], x["text_k"], x["text_v"], w.lam, dO)
+                spent += time.perf_counter() - t1
+                done += 1
+                if spent >= args.cpu_budget:
+                    break
         result["cpu_baseline"] = {"value": done * w.F * w.n / spent, "unit": "video tokens/s", "cores": threads,
                                   "kind": "oracle", "sample": f"{done} of {w.B * w.H} (b,h) slices of {w.name}, "
-                                                              f"numpy float64 backward, {spent:.1f} s"}
+                                                              f"numpy float64 backward, {spent:.1f} s",
+                                  "cpu_model": model, "host_cores": cores, "blas_threads": threads}
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
@@ -411,6 +474,37 @@ def summarize_pmc(args):
               f"write_bytes={wb:.0f} alg_bytes={alg[kern]['bytes']} source={source_hash(kern)}")
 
 
+def summarize_counters(args):
+    """Per-dispatch averages of every counter in a rocprofv3 counter_collection CSV, per VDA
+    kernel, with the derived figures the counters allow: LDS bank-conflict cycles per LDS-active
+    cycle, and MFMA TFLOP/s over the dispatch's own duration under the counter pass."""
+    rows = _rows(args.summarize_counters)
+    acc, dur = {}, {}
+    for r in rows:
+        name = r["Kernel_Name"]
+        if "vda::" not in name:
+            continue
+        acc.setdefault(name, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+        if r.get("Start_Timestamp") and r.get("End_Timestamp"):
+            dur.setdefault(name, {})[r.get("Dispatch_Id", len(dur.get(name, {})))] = \
+                (float(r["End_Timestamp"]) - float(r["Start_Timestamp"])) / 1e3
+    print(f"# rocprofv3 counters per dispatch, {args.workload}{' gated' if args.gated else ''}")
+    print(f"# command: {args.command}")
+    counters = sorted({c for k in acc.values() for c in k})
+    print(f"{'kernel':<58} " + " ".join(f"{c:>22}" for c in counters) + f" {'us':>9} {'derived':>s}")
+    for name, cs in acc.items():
+        avg = {c: sum(v) / len(v) for c, v in cs.items()}
+        us = sum(dur[name].values()) / len(dur[name]) if name in dur else float("nan")
+        derived = []
+        if "SQ_LDS_BANK_CONFLICT" in avg and avg.get("SQ_LDS_IDX_ACTIVE"):
+            derived.append(f"lds_conflict={100 * avg['SQ_LDS_BANK_CONFLICT'] / avg['SQ_LDS_IDX_ACTIVE']:.1f}%")
+        for c in avg:
+            if c.startswith("MfmaFlops") and us == us and us > 0:
+                derived.append(f"{c[9:]}_TFLOP/s={avg[c] / (us * 1e-6) / 1e12:.1f}")
+        print(f"{short_name(name)[:58]:<58} " + " ".join(f"{avg.get(c, float('nan')):>22.4g}" for c in counters)
+              + f" {us:>9.1f} " + " ".join(derived))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -426,6 +520,8 @@ def main():
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--summarize-stats", metavar="CSV")
     ap.add_argument("--summarize-pmc", nargs=4, metavar="CSV")
+    ap.add_argument("--summarize-counters", metavar="CSV",
+                    help="counter_collection.csv -> per-kernel averages of every counter")
     ap.add_argument("--command", default="", help="command line recorded in summaries")
     args = ap.parse_args()
 
@@ -438,6 +534,8 @@ def main():
         return summarize_stats(args)
     if args.summarize_pmc:
         return summarize_pmc(args)
+    if args.summarize_counters:
+        return summarize_counters(args)
     if args.copy_probe:
         return copy_probe(args)
     if args.backward:

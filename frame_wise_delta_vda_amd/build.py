@@ -30,10 +30,13 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False, extra=()) -> str:
-    """Compile every source into libvda.so next to this file; returns its path."""
-    objs = []
+    """Compile every source into libvda.so next to this file; returns its path.  The sources
+    compile in parallel (one hipcc process each), then link."""
+    from concurrent.futures import ThreadPoolExecutor
+
     build_dir = os.path.join(HERE, "_build")
     os.makedirs(build_dir, exist_ok=True)
+    jobs = []
     for src in SOURCES:
         path = os.path.join(CSRC, src)
         obj = os.path.join(build_dir, src + ".o")
@@ -43,10 +46,18 @@ def build(verbose: bool = False, extra=()) -> str:
             cmd[1:1] = ["-x", "hip"]
             cmd += DEVICE_FLAGS
         cmd += list(extra)
+        jobs.append((cmd, obj))
+
+    def compile_one(job):
+        cmd, _ = job
         if verbose:
             print(" ".join(cmd), flush=True)
         subprocess.run(cmd, check=True)
-        objs.append(obj)
+
+    workers = max(1, min(len(jobs), len(os.sched_getaffinity(0))))
+    with ThreadPoolExecutor(workers) as ex:
+        list(ex.map(compile_one, jobs))
+    objs = [obj for _, obj in jobs]
     tmp = LIB + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:

@@ -185,8 +185,8 @@ size_t vda_plan_workspace_bytes(vda_plan_t plan) {
   return plan == nullptr ? 0 : plan->workspace_bytes + plan->bwd_workspace_bytes;
 }
 
-vda_status vda_debug_workspace(vda_plan_t plan, const float** ainv, const float** bm,
-                               const float** x_fwd, const float** x_bwd) {
+vda_status vda_debug_workspace(vda_plan_t plan, const void** ainv, const void** bm,
+                               const void** x_fwd, const void** x_bwd) {
   if (plan == nullptr) return VDA_ERROR_INVALID_VALUE;
   if (ainv) *ainv = plan->p.ainv;
   if (bm) *bm = plan->p.bm;

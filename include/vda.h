@@ -196,6 +196,7 @@ const char* vda_status_string(vda_status s);
 /* Device pointers into the plan's workspace, for checking intermediate results
  * after a synchronised forward pass.  Layouts, with BH = B*H and frame index 0 for
  * the text and 1..F for the frames:
+ * The pointers are untyped: what each buffer holds depends on the plan's dtype, as follows.
  *   ainv  [BH][F+1][d][d]   (lam I + K^T K)^{-1}: float32 row-major for float32 plans.  For
  *                           bfloat16 and FP8 plans each frame's d*d*4 bytes start with two
  *                           bfloat16 planes, hi then lo, with hi + lo = the inverse; the
@@ -209,15 +210,15 @@ const char* vda_status_string(vda_status s);
  * Blocked layout of a d x dv matrix M: element (r, c) is at
  *   (((c/16 * d/16 + r/16) * 4 + (r%16)/4) * 16 + c%16) * 4 + r%4.
  * The states are float32 and blocked for float32 plans.  For the others they are
- * bfloat16 (the pointers then address d*dv bfloat16 per frame, not floats), rounded
+ * bfloat16 (d*dv bfloat16 per frame, in a slot of d*dv*4 bytes per frame), rounded
  * once from the float32 chain, with element (r, c) at
  *   (((c/16 * d/32 + r/32) * 4 + (r%32)/8) * 16 + c%16) * 8 + r%8
  * (the operand order of the readout's MFMA); the chain itself runs in float32.  For FP8
  * plans with d >= 64, r in that formula is the row with bit 3 moved above bits 4-5:
  *   (row & ~0x38) | ((row & 0x08) << 2) | ((row & 0x30) >> 1).
  * The memory stays owned by the plan.  Any output pointer may be NULL. */
-vda_status vda_debug_workspace(vda_plan_t plan, const float** ainv, const float** bm,
-                               const float** x_fwd, const float** x_bwd);
+vda_status vda_debug_workspace(vda_plan_t plan, const void** ainv, const void** bm,
+                               const void** x_fwd, const void** x_bwd);
 
 #ifdef __cplusplus
 }

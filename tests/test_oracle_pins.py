@@ -224,9 +224,36 @@ def pin_backward_torch_autograd(seed=32, lam=0.4, F=4, n=5, d=4, dv=3, T=3):
     return bool(all(np.allclose(gi, t.grad.numpy(), rtol=1e-9, atol=1e-12) for gi, t in zip(g, ts)))
 
 
+def pin_backward_batched(seed=36, lam=0.6, B=2, H=3, F=2, n=3, d=3, dv=2, T=2):
+    """The [B,H] gradient wrapper against central differences of the batched forward op
+    (``vda_forward`` over [B,H,...] arrays, pinned on its own), one random direction per input
+    over the whole batch, and against the one-head gradients of every (b,h) slice.  A slice
+    written to the wrong (b,h), or two slices swapped, fails the directional derivative."""
+    rng = np.random.default_rng(seed)
+    x = {"q": _rand(rng, B, H, F, n, d), "k": _rownorm(_rand(rng, B, H, F, n, d)),
+         "v": _rand(rng, B, H, F, n, dv), "text_k": _rownorm(_rand(rng, B, H, T, d)),
+         "text_v": _rand(rng, B, H, T, dv)}
+    d_out = rng.standard_normal((B, H, F, n, dv))
+    g = oracle.vda_backward(**x, lam=lam, d_out=d_out)
+    ok = len(g) == 5
+    eps = 1e-6
+    for name, gi in zip(("q", "k", "v", "text_k", "text_v"), g):
+        dirn = rng.standard_normal(x[name].shape)
+        lp = np.sum(d_out * oracle.vda_forward(**{**x, name: x[name] + eps * dirn}, lam=lam))
+        lm = np.sum(d_out * oracle.vda_forward(**{**x, name: x[name] - eps * dirn}, lam=lam))
+        fd = (lp - lm) / (2 * eps)
+        ok &= gi.shape == x[name].shape and abs(np.sum(gi * dirn) - fd) <= 1e-6 * max(1.0, abs(fd))
+    for b in range(B):
+        for h in range(H):
+            ref = oracle.vda_backward_head(x["q"][b, h], x["k"][b, h], x["v"][b, h], x["text_k"][b, h],
+                                           x["text_v"][b, h], lam, d_out[b, h])
+            ok &= all(np.array_equal(gi[b, h], r) for gi, r in zip(g, ref))
+    return bool(ok)
+
+
 PINS = [pin_golden, pin_lstsq, lambda: pin_lstsq(seed=4, n=6, d=3, dv=3), pin_delta_rule,
         pin_fixed_point, pin_gate_worked_examples, pin_gate_limits,
-        pin_backward_finite_differences, pin_backward_torch_autograd]
+        pin_backward_finite_differences, pin_backward_torch_autograd, pin_backward_batched]
 
 
 # ---------------------------------------------------------------------------
@@ -392,6 +419,11 @@ def test_backward_matches_torch_autograd():
     assert pin_backward_torch_autograd(seed=34, lam=1.0, F=2, n=1, d=3, dv=3, T=1)
 
 
+def test_batched_backward_wrapper():
+    assert pin_backward_batched()
+    assert pin_backward_batched(seed=37, lam=0.3, B=3, H=2, F=1, n=2, d=2, dv=3, T=1)
+
+
 def test_backward_with_no_text_and_linearity_in_d_out():
     rng = np.random.default_rng(35)
     h = _tiny_head(35, F=3, n=4, d=3, dv=2, T=0)
@@ -544,6 +576,38 @@ def test_backward_mutants_are_caught(name, monkeypatch):
         except Exception:
             results.append(False)
     assert not all(results), f"mutant {name} passes every pin"
+
+
+# mistakes planted in the [B,H] gradient wrapper: one-line edits of its own source
+BATCHED_BACKWARD_MUTANTS = {
+    "slices_to_first_head": ("g[b, h] = r", "g[b, 0] = r"),
+    "heads_reversed": ("g[b, h] = r", "g[b, H - 1 - h] = r"),
+    "d_out_of_other_head": ("                                    d_out[b, h])",
+                            "                                    d_out[b, (h + 1) % H])"),
+    "gradients_rotated": ("for g, r in zip(grads, res):", "for g, r in zip(grads, res[1:] + res[:1]):"),
+}
+
+
+def _batched_backward_mutant(name):
+    import inspect
+    src = inspect.getsource(O.vda_backward)
+    old, new = BATCHED_BACKWARD_MUTANTS[name]
+    assert old in src, name
+    ns = dict(vars(O))
+    exec(src.replace(old, new), ns)
+    return ns["vda_backward"]
+
+
+@pytest.mark.parametrize("name", sorted(BATCHED_BACKWARD_MUTANTS))
+def test_batched_backward_mutants_are_caught(name, monkeypatch):
+    fn = _batched_backward_mutant(name)
+    monkeypatch.setattr(O, "vda_backward", fn)
+    monkeypatch.setattr(oracle, "vda_backward", fn, raising=False)
+    try:
+        ok = pin_backward_batched()
+    except Exception:
+        ok = False
+    assert not ok, f"mutant {name} passes the batched pin"
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
