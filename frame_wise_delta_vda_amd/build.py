@@ -14,7 +14,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libvda.so")
-SOURCES = ["vda_api.cpp", "stats.hip", "scan.hip", "readout.hip", "bwd.hip"]
+SOURCES = ["vda_api.cpp", "stats.hip", "scan.hip", "readout.hip", "bwd.hip", "noalloc.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU ops (v_pk_fma_f32 and friends) are switched off for all device

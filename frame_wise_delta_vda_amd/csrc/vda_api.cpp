@@ -61,31 +61,17 @@ bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
 
 }  // namespace
 
-extern "C" {
+namespace vda {
 
-const char* vda_status_string(vda_status s) {
-  switch (s) {
-    case VDA_SUCCESS: return "VDA_SUCCESS";
-    case VDA_ERROR_INVALID_VALUE: return "VDA_ERROR_INVALID_VALUE";
-    case VDA_ERROR_NOT_SUPPORTED: return "VDA_ERROR_NOT_SUPPORTED";
-    case VDA_ERROR_MISALIGNED: return "VDA_ERROR_MISALIGNED";
-    case VDA_ERROR_OUT_OF_MEMORY: return "VDA_ERROR_OUT_OF_MEMORY";
-    case VDA_ERROR_DEVICE: return "VDA_ERROR_DEVICE";
-  }
-  return "VDA_ERROR_UNKNOWN";
-}
-
-vda_status vda_plan_create(int64_t B, int64_t H, int64_t F, int64_t n, int64_t d, int64_t dv,
-                           int64_t T, float lambda, vda_dtype dtype, vda_plan_t* plan_out) {
-  if (plan_out == nullptr) return VDA_ERROR_INVALID_VALUE;
-  *plan_out = nullptr;
+vda_status make_problem(int64_t B, int64_t H, int64_t F, int64_t n, int64_t d, int64_t dv, int64_t T,
+                        float lambda, vda_dtype dtype, Problem* out, size_t* workspace_bytes) {
   if (B < 0 || H < 0 || F < 0 || n < 0 || T < 0) return VDA_ERROR_INVALID_VALUE;
   if (!(std::isfinite(lambda) && lambda > 0.0f)) return VDA_ERROR_INVALID_VALUE;
   if (dtype != VDA_DTYPE_F32 && dtype != VDA_DTYPE_BF16 && dtype != VDA_DTYPE_FP8_E4M3)
     return VDA_ERROR_NOT_SUPPORTED;
   if (!supported_width(d) || !supported_width(dv)) return VDA_ERROR_NOT_SUPPORTED;
   // a frame (or the text) is addressed with 32-bit byte offsets
-  if (n > vda::kMaxFrameTokens || T > vda::kMaxFrameTokens) return VDA_ERROR_NOT_SUPPORTED;
+  if (n > kMaxFrameTokens || T > kMaxFrameTokens) return VDA_ERROR_NOT_SUPPORTED;
 
   // Every element count the kernels index must fit in int64; grids are 1-D.
   int64_t bh, frames, tok, elems, ws_frames, ws_elems, tmp;
@@ -100,6 +86,63 @@ vda_status vda_plan_create(int64_t B, int64_t H, int64_t F, int64_t n, int64_t d
     return VDA_ERROR_INVALID_VALUE;
   (void)elems;
 
+  Problem p{};
+  p.B = B; p.H = H; p.F = F; p.n = n; p.d = d; p.dv = dv; p.T = T;
+  p.lam = lambda;
+  p.bf16 = (dtype != VDA_DTYPE_F32);  // FP8 inputs run the bfloat16 path after conversion
+  p.fp8 = (dtype == VDA_DTYPE_FP8_E4M3);
+  p.states_f32 = false;
+  p.bm_only = false;
+  p.num_cus = 0;
+  p.ainv = p.bm = p.xf = p.xb = nullptr;
+  const size_t ainv_n = size_t(ws_frames) * d * d;
+  const size_t bm_n = size_t(ws_frames) * d * dv;
+  // states: float32 for float32 plans; bfloat16 (half the bytes) for the others
+  const size_t x_n = size_t(frames) * d * dv / (p.bf16 ? 2 : 1);
+  *workspace_bytes = (ainv_n + bm_n + 2 * x_n) * sizeof(float);
+  *out = p;
+  return VDA_SUCCESS;
+}
+
+void carve_workspace(Problem& p, void* base) {
+  const size_t ws_frames = size_t(p.B) * size_t(p.H) * size_t(p.F + 1);
+  const size_t frames = size_t(p.B) * size_t(p.H) * size_t(p.F);
+  const size_t ainv_n = ws_frames * size_t(p.d) * size_t(p.d);
+  const size_t bm_n = ws_frames * size_t(p.d) * size_t(p.dv);
+  const size_t x_n = frames * size_t(p.d) * size_t(p.dv) / (p.bf16 ? 2 : 1);
+  float* f = static_cast<float*>(base);
+  p.ainv = f;
+  p.bm = p.ainv + ainv_n;
+  p.xf = p.bm + bm_n;
+  p.xb = p.xf + x_n;
+}
+
+}  // namespace vda
+
+extern "C" {
+
+const char* vda_status_string(vda_status s) {
+  switch (s) {
+    case VDA_SUCCESS: return "VDA_SUCCESS";
+    case VDA_ERROR_INVALID_VALUE: return "VDA_ERROR_INVALID_VALUE";
+    case VDA_ERROR_NOT_SUPPORTED: return "VDA_ERROR_NOT_SUPPORTED";
+    case VDA_ERROR_MISALIGNED: return "VDA_ERROR_MISALIGNED";
+    case VDA_ERROR_OUT_OF_MEMORY: return "VDA_ERROR_OUT_OF_MEMORY";
+    case VDA_ERROR_DEVICE: return "VDA_ERROR_DEVICE";
+    case VDA_ERROR_TOO_LARGE: return "VDA_ERROR_TOO_LARGE";
+  }
+  return "VDA_ERROR_UNKNOWN";
+}
+
+vda_status vda_plan_create(int64_t B, int64_t H, int64_t F, int64_t n, int64_t d, int64_t dv,
+                           int64_t T, float lambda, vda_dtype dtype, vda_plan_t* plan_out) {
+  if (plan_out == nullptr) return VDA_ERROR_INVALID_VALUE;
+  *plan_out = nullptr;
+  vda::Problem shape;
+  size_t total = 0;
+  const vda_status st = vda::make_problem(B, H, F, n, d, dv, T, lambda, dtype, &shape, &total);
+  if (st != VDA_SUCCESS) return st;
+
   vda_plan_s* plan = new (std::nothrow) vda_plan_s();
   if (plan == nullptr) return VDA_ERROR_OUT_OF_MEMORY;
   if (hipGetDevice(&plan->device) != hipSuccess) {
@@ -108,7 +151,7 @@ vda_status vda_plan_create(int64_t B, int64_t H, int64_t F, int64_t n, int64_t d
     return VDA_ERROR_DEVICE;
   }
   vda::Problem& p = plan->p;
-  p.num_cus = 0;
+  p = shape;
   if (hipDeviceGetAttribute(&p.num_cus, hipDeviceAttributeMultiprocessorCount, plan->device) !=
           hipSuccess ||
       p.num_cus <= 0) {
@@ -116,21 +159,8 @@ vda_status vda_plan_create(int64_t B, int64_t H, int64_t F, int64_t n, int64_t d
     delete plan;
     return VDA_ERROR_DEVICE;
   }
-  p.B = B; p.H = H; p.F = F; p.n = n; p.d = d; p.dv = dv; p.T = T;
-  p.lam = lambda;
-  p.bf16 = (dtype != VDA_DTYPE_F32);  // FP8 inputs run the bfloat16 path after conversion
-  p.fp8 = (dtype == VDA_DTYPE_FP8_E4M3);
-  p.states_f32 = false;
-  p.bm_only = false;
-  p.ainv = p.bm = p.xf = p.xb = nullptr;
   plan->workspace = nullptr;
   plan->workspace_bytes = 0;
-
-  const size_t ainv_n = size_t(ws_frames) * d * d;
-  const size_t bm_n = size_t(ws_frames) * d * dv;
-  // states: float32 for float32 plans; bfloat16 (half the bytes) for the others
-  const size_t x_n = size_t(frames) * d * dv / (p.bf16 ? 2 : 1);
-  const size_t total = (ainv_n + bm_n + 2 * x_n) * sizeof(float);
   if (total > 0) {
     void* ws = nullptr;
     if (hipMalloc(&ws, total) != hipSuccess || ws == nullptr) {
@@ -140,11 +170,7 @@ vda_status vda_plan_create(int64_t B, int64_t H, int64_t F, int64_t n, int64_t d
     }
     plan->workspace = ws;
     plan->workspace_bytes = total;
-    float* base = static_cast<float*>(ws);
-    p.ainv = base;
-    p.bm = p.ainv + ainv_n;
-    p.xf = p.bm + bm_n;
-    p.xb = p.xf + x_n;
+    vda::carve_workspace(p, ws);
   }
   plan->timing_capacity = 0;
   plan->timed_calls = 0;
@@ -199,13 +225,14 @@ vda_status vda_debug_workspace(vda_plan_t plan, const void** ainv, const void** 
 
 namespace {
 
-// Checks and enqueues the selected stages; gate != nullptr runs the gated readout.
-vda_status enqueue(vda_plan_t plan, unsigned stages, const void* q, const void* k, const void* v,
-                   const void* text_k, const void* text_v, const vda::GateWeights* gate, void* out,
-                   void* stream) {
-  if (plan == nullptr) return VDA_ERROR_INVALID_VALUE;
+}  // namespace
+
+namespace vda {
+
+vda_status enqueue_problem(const Problem& p, int device, unsigned stages, const void* q, const void* k,
+                           const void* v, const void* text_k, const void* text_v, const GateWeights* gate,
+                           void* out, void* stream, hipEvent_t* tev) {
   if (stages == 0 || (stages & ~unsigned(VDA_STAGE_ALL)) != 0) return VDA_ERROR_INVALID_VALUE;
-  const vda::Problem& p = plan->p;
   // No output element: nothing to compute and no pointer is read.
   if (p.B == 0 || p.H == 0 || p.F == 0 || p.n == 0) return VDA_SUCCESS;
   const size_t es = p.fp8 ? 1 : p.bf16 ? 2 : 4;  // input element bytes
@@ -252,14 +279,10 @@ vda_status enqueue(vda_plan_t plan, unsigned stages, const void* q, const void* 
     (void)hipGetLastError();
     return VDA_ERROR_DEVICE;
   }
-  if (dev != plan->device) return VDA_ERROR_INVALID_VALUE;
+  if (dev != device) return VDA_ERROR_INVALID_VALUE;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
-  // timing events of this call (whole passes only), or none
-  hipEvent_t* tev = nullptr;
-  if (stages == VDA_STAGE_ALL && plan->timing_capacity > 0 && plan->timed_calls < plan->timing_capacity)
-    tev = plan->timing_events + size_t(plan->timed_calls) * kTimingEvents;
   // each stage is one kernel launch, which records the stage's two events itself
   auto timed = [&](int begin, int end) {
     vda::Problem ps = p;
@@ -275,12 +298,33 @@ vda_status enqueue(vda_plan_t plan, unsigned stages, const void* q, const void* 
     const vda::Problem pr = timed(kEvReadBegin, kEvReadEnd);
     e = gate ? vda::launch_readout_gated(pr, q, *gate, out, s) : vda::launch_readout(pr, q, out, s);
   }
-  if (tev != nullptr && e == hipSuccess) ++plan->timed_calls;
   if (e != hipSuccess) {
     (void)hipGetLastError();
     return VDA_ERROR_DEVICE;
   }
-  if (do_stats) plan->has_statistics = true;
+  return VDA_SUCCESS;
+}
+
+}  // namespace vda
+
+namespace {
+
+// Checks and enqueues the selected stages of a plan; gate != nullptr runs the gated readout.
+vda_status enqueue(vda_plan_t plan, unsigned stages, const void* q, const void* k, const void* v,
+                   const void* text_k, const void* text_v, const vda::GateWeights* gate, void* out,
+                   void* stream) {
+  if (plan == nullptr) return VDA_ERROR_INVALID_VALUE;
+  // timing events of this call (whole passes only), or none
+  hipEvent_t* tev = nullptr;
+  if (stages == VDA_STAGE_ALL && plan->timing_capacity > 0 && plan->timed_calls < plan->timing_capacity)
+    tev = plan->timing_events + size_t(plan->timed_calls) * kTimingEvents;
+  const vda_status st = vda::enqueue_problem(plan->p, plan->device, stages, q, k, v, text_k, text_v, gate,
+                                             out, stream, tev);
+  if (st != VDA_SUCCESS) return st;
+  const vda::Problem& p = plan->p;
+  if (p.B == 0 || p.H == 0 || p.F == 0 || p.n == 0) return VDA_SUCCESS;  // nothing was enqueued
+  if (tev != nullptr) ++plan->timed_calls;
+  if (stages & VDA_STAGE_STATS) plan->has_statistics = true;
   return VDA_SUCCESS;
 }
 

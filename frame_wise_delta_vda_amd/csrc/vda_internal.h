@@ -6,6 +6,8 @@
 #include <cstddef>
 #include <cstdint>
 
+#include "vda.h"
+
 namespace vda {
 
 // Largest token count of one frame or of the text: a frame's K and V are read through
@@ -40,6 +42,21 @@ inline void launch_kernel(const Problem& p, K kern, dim3 grid, dim3 block, uint3
   else
     hipLaunchKernelGGL(kern, grid, block, lds, s, args...);
 }
+
+// Validates a problem shape (the checks of vda_plan_create) and fills *out with it, no
+// workspace attached; *workspace_bytes is what the forward pass needs (vda_api.cpp).
+vda_status make_problem(int64_t B, int64_t H, int64_t F, int64_t n, int64_t d, int64_t dv, int64_t T,
+                        float lambda, vda_dtype dtype, Problem* out, size_t* workspace_bytes);
+// Points p's workspace buffers (ainv, bm, xf, xb) into the block at base, of the size
+// make_problem reported.
+void carve_workspace(Problem& p, void* base);
+struct GateWeights;
+// Argument checks (pointers, alignment, overlap, current device == device) and the launches of
+// the selected stages of p on `stream`; tev, when not NULL, holds the stages' timing events.
+// A problem with no output element enqueues nothing and returns VDA_SUCCESS.
+vda_status enqueue_problem(const Problem& p, int device, unsigned stages, const void* q, const void* k,
+                           const void* v, const void* text_k, const void* text_v, const GateWeights* gate,
+                           void* out, void* stream, hipEvent_t* tev);
 
 // Each launcher enqueues one stage on `stream` and returns the launch status.
 hipError_t launch_stats(const Problem& p, const void* k, const void* v, const void* tk,

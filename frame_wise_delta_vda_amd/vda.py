@@ -19,9 +19,12 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "vda.h")
 VDA_DTYPE_F32, VDA_DTYPE_BF16, VDA_DTYPE_FP8_E4M3 = 0, 1, 2
 DTYPES = {"f32": VDA_DTYPE_F32, "bf16": VDA_DTYPE_BF16, "fp8": VDA_DTYPE_FP8_E4M3}
 STATUS = {0: "VDA_SUCCESS", 1: "VDA_ERROR_INVALID_VALUE", 2: "VDA_ERROR_NOT_SUPPORTED",
-          3: "VDA_ERROR_MISALIGNED", 4: "VDA_ERROR_OUT_OF_MEMORY", 5: "VDA_ERROR_DEVICE"}
+          3: "VDA_ERROR_MISALIGNED", 4: "VDA_ERROR_OUT_OF_MEMORY", 5: "VDA_ERROR_DEVICE",
+          6: "VDA_ERROR_TOO_LARGE"}
 VDA_SUCCESS, VDA_ERROR_INVALID_VALUE, VDA_ERROR_NOT_SUPPORTED = 0, 1, 2
 VDA_ERROR_MISALIGNED, VDA_ERROR_OUT_OF_MEMORY, VDA_ERROR_DEVICE = 3, 4, 5
+VDA_ERROR_TOO_LARGE = 6
+VDA_NOALLOC_SCRATCH_BYTES = 64 << 20
 VDA_STAGE_STATS, VDA_STAGE_SCAN, VDA_STAGE_READOUT, VDA_STAGE_ALL = 1, 2, 4, 7
 
 
@@ -72,6 +75,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     flp = ctypes.POINTER(ctypes.c_float)
     lib.vda_plan_timings.argtypes = [c_vp, ctypes.POINTER(c_int), flp, flp, flp]
     lib.vda_plan_timings.restype = c_int
+    lib.vda_forward_noalloc.argtypes = [c_i64] * 7 + [ctypes.c_float, c_int] + [c_vp] * 7
+    lib.vda_forward_noalloc.restype = c_int
     if path is None:
         _lib = lib
     return lib
@@ -123,6 +128,15 @@ def vda_plan_create(B, H, F, n, d, dv, T, lam, dtype) -> int:
 def vda_forward(plan, q, k, v, text_k, text_v, out, stream=None):
     _check(load_library().vda_forward(plan, _ptr(q), _ptr(k), _ptr(v), _ptr(text_k), _ptr(text_v),
                                       _ptr(out), _stream(stream)), "vda_forward")
+
+
+def vda_forward_noalloc(B, H, F, n, d, dv, T, lam, dtype, q, k, v, text_k, text_v, out, stream=None):
+    """The forward pass with no plan and no device allocation (include/vda.h)."""
+    if isinstance(dtype, str):
+        dtype = DTYPES[dtype]
+    _check(load_library().vda_forward_noalloc(B, H, F, n, d, dv, T, ctypes.c_float(lam), dtype, _ptr(q), _ptr(k),
+                                              _ptr(v), _ptr(text_k), _ptr(text_v), _ptr(out), _stream(stream)),
+           "vda_forward_noalloc")
 
 
 def vda_forward_gated(plan, q, k, v, text_k, text_v, w_gate, b_gate, w_out, out, stream=None):

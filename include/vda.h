@@ -64,7 +64,9 @@ typedef enum {
   VDA_ERROR_NOT_SUPPORTED = 2,  /* d or dv outside {32, 64, 128}, unknown dtype, n or T too large */
   VDA_ERROR_MISALIGNED = 3,     /* a tensor pointer is not 16-byte aligned */
   VDA_ERROR_OUT_OF_MEMORY = 4,  /* workspace allocation failed */
-  VDA_ERROR_DEVICE = 5          /* a HIP runtime call or kernel launch failed */
+  VDA_ERROR_DEVICE = 5,         /* a HIP runtime call or kernel launch failed */
+  VDA_ERROR_TOO_LARGE = 6       /* vda_forward_noalloc: the problem needs more workspace than
+                                   its fixed scratch (VDA_NOALLOC_SCRATCH_BYTES) holds */
 } vda_status;
 
 /* Pipeline stages of one forward pass, in the order they must run. */
@@ -165,6 +167,30 @@ vda_status vda_forward_gated(vda_plan_t plan, const void* q, const void* k, cons
 vda_status vda_backward(vda_plan_t plan, const void* q, const void* k, const void* v,
                         const void* text_k, const void* text_v, const void* d_out, void* d_q,
                         void* d_k, void* d_v, void* d_text_k, void* d_text_v, void* stream);
+
+/* Bytes of the fixed device scratch of vda_forward_noalloc, per GPU. */
+#define VDA_NOALLOC_SCRATCH_BYTES (64ull << 20)
+
+/* The whole forward pass, as vda_forward computes it, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * It takes the problem shape directly (no plan; arguments as for vda_plan_create) and the
+ * tensors as for vda_forward, and allocates nothing: the pass's workspace (the inverses,
+ * K^T V and the state sequences) lives in a fixed array of VDA_NOALLOC_SCRATCH_BYTES of
+ * device memory that the library holds on every GPU it runs on until the process ends.  The
+ * workspace a problem needs is the one vda_plan_workspace_bytes reports for a plan of the same
+ * shape; a problem that needs more returns VDA_ERROR_TOO_LARGE before anything is enqueued
+ * (at d = dv = 128 in bfloat16 that is about 17.8 MB per head at 90 frames of any n, so three
+ * 768p heads fit).  The first call on a device looks up the array's address on that device and
+ * sets the kernels' attributes there (no allocation); later calls make no runtime call but
+ * kernel launches.  Every call on a GPU uses that GPU's one array: calls that overlap in time on
+ * one GPU (on different streams, or from different threads) race and give undefined results;
+ * calls ordered on one stream are safe.  Results are bitwise those of vda_forward on a plan of
+ * the same shape.  The output is complete when the stream reaches the end of the pass.
+ * Errors: as vda_plan_create and vda_forward (but never OUT_OF_MEMORY), and TOO_LARGE. */
+vda_status vda_forward_noalloc(int64_t B, int64_t H, int64_t F, int64_t n, int64_t d, int64_t dv,
+                               int64_t T, float lambda, vda_dtype dtype, const void* q,
+                               const void* k, const void* v, const void* text_k, const void* text_v,
+                               void* out, void* stream);
 
 /* Per-stage timing of whole forward passes, for benchmarks.  After
  * vda_plan_enable_timing(plan, capacity) with capacity > 0, each of the next `capacity`

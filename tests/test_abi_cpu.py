@@ -20,7 +20,7 @@ def test_every_declared_symbol_is_exported(lib):
                           "vda_backward",
                           "vda_plan_destroy",
                           "vda_plan_workspace_bytes", "vda_status_string", "vda_debug_workspace",
-                          "vda_plan_enable_timing", "vda_plan_timings"}
+                          "vda_plan_enable_timing", "vda_plan_timings", "vda_forward_noalloc"}
     for name in names:
         assert hasattr(lib, name), name
 
@@ -80,3 +80,19 @@ def test_binding_raises_vda_error(lib):
     with pytest.raises(vda.VdaError) as e:
         vda.vda_plan_create(1, 1, 1, 1, 40, 32, 0, 1.0, "bf16")
     assert e.value.status == binding.VDA_ERROR_NOT_SUPPORTED
+
+
+def test_noalloc_rejects_bad_and_oversized_problems_before_any_device_call(lib):
+    # argument errors are those of vda_plan_create; a workspace above the fixed scratch is
+    # TOO_LARGE; none of these touches a device, so they hold on a host with no GPU
+    f = lib.vda_forward_noalloc
+    nul = [None] * 7
+    assert f(1, 1, 1, 1, 48, 32, 0, ctypes.c_float(1.0), 1, *nul) == binding.VDA_ERROR_NOT_SUPPORTED
+    assert f(1, 1, 1, 1, 32, 32, 0, ctypes.c_float(0.0), 1, *nul) == binding.VDA_ERROR_INVALID_VALUE
+    assert f(-1, 1, 1, 1, 32, 32, 0, ctypes.c_float(1.0), 1, *nul) == binding.VDA_ERROR_INVALID_VALUE
+    assert f(2**40, 2**40, 1, 1, 32, 32, 0, ctypes.c_float(1.0), 1, *nul) == binding.VDA_ERROR_INVALID_VALUE
+    # four heads of the 768p shape (bf16, d = dv = 128, 90 frames): 4 x 17.8 MB > 64 MiB
+    assert f(1, 4, 90, 4032, 128, 128, 256, ctypes.c_float(1.0), 1, *nul) == binding.VDA_ERROR_TOO_LARGE
+    # no output element: nothing to do, no pointer read
+    assert f(1, 4, 0, 4032, 128, 128, 256, ctypes.c_float(1.0), 1, *nul) == binding.VDA_SUCCESS
+    assert vda.vda_status_string(binding.VDA_ERROR_TOO_LARGE) == "VDA_ERROR_TOO_LARGE"
