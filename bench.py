@@ -35,7 +35,9 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}  # dense MFMA, vendor figures
 KERNEL_SOURCES = {"stats": "stats.hip", "scan": "scan.hip", "readout": "readout.hip"}
-KERNEL_SYMBOLS = {"stats": "stats_bf16_kernel", "scan": "scan_bf16_kernel", "readout": "readout_bf16_kernel"}
+# kernels of each forward stage (the chunked scan is three launches: local pass, carry, rerun)
+KERNEL_SYMBOLS = {"stats": ("stats_bf16_kernel",), "scan": ("scan_bf16_kernel", "chunk_carry_kernel"),
+                  "readout": ("readout_bf16_kernel",)}
 GATED_READOUT_SYMBOL = "readout_gated_kernel"  # the readout with the gated epilogue (--gated)
 COPY_PROBE_BYTES = 1 << 30
 
@@ -186,6 +188,9 @@ def run(args):
     out = torch.empty(w.shapes()["out"], device="cuda",
                       dtype=torch.float32 if w.dtype == "f32" else torch.bfloat16)
     plan = binding.Plan(w.B, w.H, w.F, w.n, w.d, w.dv, w.T, w.lam, w.dtype)
+    if args.scan_chunk is not None:
+        plan.set_scan_chunk(args.scan_chunk)
+    scan_chunk = plan.scan_chunk if w.dtype != "f32" else 0
     q, k, v, tk, tv = (dev[x] for x in W.TENSORS)
     gate = None
     if args.gated:
@@ -226,7 +231,7 @@ def run(args):
           ", ".join(f"{n} {kern_ms[n]:.3f} ms" for n in names), file=sys.stderr, flush=True)
 
     alg = algorithmic(w, args.gated)
-    prof_name = w.name + ("_gated" if args.gated else "")
+    prof_name = w.name + ("_gated" if args.gated else "") + (f"_scan_chunk{args.scan_chunk}" if args.scan_chunk else "")
     traffic = read_traffic(prof_name)
     kernels = {}
     for n in names:
@@ -269,7 +274,9 @@ def run(args):
         "dtype": {"f32": "f32", "bf16": "bf16", "fp8": "fp8_e4m3+bf16"}[w.dtype],
         "data": "synthetic",
         "config": {"workload": w.name, "input_dtype": w.dtype, "arithmetic": ARITHMETIC[w.dtype],
-                   "epilogue": "sigmoid gate and output projection per head" if args.gated else "none", "B": w.B, "H": w.H, "F": w.F, "n": w.n, "d": w.d, "dv": w.dv,
+                   "epilogue": "sigmoid gate and output projection per head" if args.gated else "none",
+                   "scan": (f"chunked, {scan_chunk} frames per chunk ({-(-w.F // scan_chunk)} chunks)"
+                            if scan_chunk else "serial"), "B": w.B, "H": w.H, "F": w.F, "n": w.n, "d": w.d, "dv": w.dv,
                    "T": w.T, "lambda": w.lam, "video_tokens_per_step": w.video_tokens,
                    "alg_bytes_per_step": w.algorithmic_bytes(),
                    "whole_step_GB/s": round(w.algorithmic_bytes() / (ms_step * 1e-3) / 1e9, 1)},
@@ -445,7 +452,7 @@ def summarize_pmc(args):
     import workloads as W
     fetch_csv, write_csv, cfetch_csv, cwrite_csv = args.summarize_pmc
     w = W.by_name(args.workload)
-    prof_name = w.name + ("_gated" if args.gated else "")
+    prof_name = w.name + ("_gated" if args.gated else "") + (f"_scan_chunk{args.scan_chunk}" if args.scan_chunk else "")
     fetch = _pmc_per_kernel(fetch_csv, "FETCH_SIZE")
     write = _pmc_per_kernel(write_csv, "WRITE_SIZE")
     cf = _pmc_per_kernel(cfetch_csv, "FETCH_SIZE")
@@ -459,17 +466,18 @@ def summarize_pmc(args):
     print(f"# calibration: copy probe '{short_name(copy_name)[:50]}' over {COPY_PROBE_BYTES} B read + "
           f"{COPY_PROBE_BYTES} B written reads FETCH_SIZE {cf[copy_name]:.0f} KiB, WRITE_SIZE "
           f"{cw[copy_name]:.0f} KiB -> scale fetch x{f_scale:.4f}, write x{w_scale:.4f}")
-    for kern, sym in KERNEL_SYMBOLS.items():
+    for kern, syms in KERNEL_SYMBOLS.items():
         if kern == "readout" and args.gated:
-            sym = GATED_READOUT_SYMBOL
-        names = [n for n in fetch if sym in n]
+            syms = (GATED_READOUT_SYMBOL,)
+        names = [n for n in fetch if any(sym in n for sym in syms)]
         if not names:
             continue
-        n = names[0]
-        fb = fetch[n] * 1024.0 * f_scale
-        wb = write.get(n, 0.0) * 1024.0 * w_scale
+        # a stage's bytes per step: the per-dispatch averages of its kernels, summed
+        fb = sum(fetch[n] for n in names) * 1024.0 * f_scale
+        wb = sum(write.get(n, 0.0) for n in names) * 1024.0 * w_scale
         print(f"# {kern}: fetch {fb/1e9:.4f} GB, write {wb/1e9:.4f} GB per launch; algorithmic "
-              f"{alg[kern]['bytes']/1e9:.4f} GB")
+              f"{alg[kern]['bytes']/1e9:.4f} GB" + (f"; kernels: {', '.join(short_name(n) for n in names)}"
+                                                    if len(names) > 1 else ""))
         print(f"traffic kernel={kern} bytes_per_launch={fb + wb:.0f} fetch_bytes={fb:.0f} "
               f"write_bytes={wb:.0f} alg_bytes={alg[kern]['bytes']} source={source_hash(kern)}")
 
@@ -515,6 +523,8 @@ def main():
                     help="time the backward pass (gradients) after one forward pass")
     ap.add_argument("--gated", action="store_true",
                     help="run the pass with the gated fusion epilogue (seeded synthetic weights)")
+    ap.add_argument("--scan-chunk", type=int, default=None,
+                    help="frames per chunk of the chunked scan (0: serial; default: the plan's own choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-probe", action="store_true")

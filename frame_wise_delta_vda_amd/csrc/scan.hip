@@ -186,20 +186,67 @@ struct ScanBf16Cfg {
   static_assert(APIECES % 64 == 0 && THREADS % 64 == 0, "pieces must split into whole waves");
 };
 
-template <int D, int DV>
+// What one launch of the bfloat16 scan kernel runs (chain steps: 0 = the text, 1..F = the
+// frames in the chain's order):
+//   kSegSerial: every chain from step 0 to F, storing every state;
+//   kSegLocal:  the chunked scan's local pass.  A chunk is `len` consecutive chain steps,
+//               chunk 0 being steps 0..len and chunk j >= 1 steps 1 + j len .. (j+1) len.  For
+//               chunks 0..K-2 of every chain it runs the update from a zero state, giving the
+//               chunk's end state C_j (chunk 0: the true end state, stored with every state on
+//               the way), and, for chunks 1..K-2, the chunk's transition P_j = product of
+//               lam Ainv_f over its steps, in step order (the same chain on lam I with no Bm);
+//   kSegRerun:  the chunked scan's last pass: chunks 1..K-1 from their true start states,
+//               storing every state.
+// Chunk summaries (float32): P_j row-major d x d, C_j and the start states blocked d x dv.
+constexpr int kSegSerial = 0, kSegLocal = 1, kSegRerun = 2;
+struct ChunkArgs {
+  int64_t len;      // chain steps per chunk (chunk 0 also holds step 0)
+  int64_t nchunks;  // K >= 2 for the chunked passes
+  float* pc;        // [nchains][K][d*d]  P_j
+  float* cc;        // [nchains][K][d*dv] C_j
+  float* starts;    // [nchains][K][d*dv] true state before chunk j's first step (j >= 1)
+};
+
+template <int D, int DV, int MODE>
 __global__ void __launch_bounds__(4 * D)
 scan_bf16_kernel(const uint16_t* __restrict__ ainv_planes, const float* __restrict__ bm,
                  float* __restrict__ xf, float* __restrict__ xb, int64_t nchains, int64_t F,
-                 float lam, int64_t grid, int store_mode) {
+                 float lam, int64_t grid, int store_mode, ChunkArgs ch) {
   using C = ScanBf16Cfg<D, DV>;
   extern __shared__ __align__(16) unsigned char smem[];
   uint16_t* abuf = reinterpret_cast<uint16_t*>(smem);  // [2][ABUF]: packed Ainv planes of two steps
   uint16_t* rsb = abuf + 2 * C::ABUF;                   // [2][RSB]: R of this step and the next
 
   const int64_t L = xcd_remap(blockIdx.x, grid);
-  const int64_t chain = L / C::NCB;
-  const int cb = int(L % C::NCB);
+  int64_t chain, s_begin = 0, s_end = F, j = 0;
+  int cb;
+  bool transition = false;  // this workgroup runs P_j (no Bm, columns of a d x d product)
+  if constexpr (MODE == kSegSerial) {
+    chain = L / C::NCB;
+    cb = int(L % C::NCB);
+  } else if constexpr (MODE == kSegLocal) {
+    constexpr int G = C::NCB + D / 32;  // C_j's column blocks, then P_j's
+    const int64_t grp = L / G;
+    const int slot = int(L % G);
+    chain = grp / (ch.nchunks - 1);
+    j = grp % (ch.nchunks - 1);
+    transition = slot >= C::NCB;
+    cb = transition ? slot - C::NCB : slot;
+    if (transition && j == 0) return;  // chunk 0 starts from the text state: no P_0
+    s_begin = j == 0 ? 0 : 1 + j * ch.len;
+    s_end = (j + 1) * ch.len < F ? (j + 1) * ch.len : F;
+  } else {
+    const int64_t grp = L / C::NCB;
+    cb = int(L % C::NCB);
+    chain = grp / (ch.nchunks - 1);
+    j = 1 + grp % (ch.nchunks - 1);
+    s_begin = 1 + j * ch.len;
+    s_end = (j + 1) * ch.len < F ? (j + 1) * ch.len : F;
+  }
   if (chain >= nchains) return;
+  // every state of the segment is stored (the serial scan, the rerun, and chunk 0 of the local
+  // pass, whose zero start is the true one); the local pass also keeps its end state
+  const bool store_all = MODE != kSegLocal || (j == 0 && !transition);
   const int64_t bh = chain >> 1;
   const bool backward = chain & 1;
   const int64_t F1 = F + 1;
@@ -277,6 +324,11 @@ scan_bf16_kernel(const uint16_t* __restrict__ ainv_planes, const float* __restri
   uint4 A[C::NSLOT][C::KS][2];
   float4 Bv[C::NSLOT][C::CW];
   auto load_bm = [&](int64_t t, float4 (&bv)[C::CW]) {
+    if (MODE == kSegLocal && transition) {  // a transition adds no Bm
+#pragma unroll
+      for (int cw = 0; cw < C::CW; ++cw) bv[cw] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      return;
+    }
     const float* bsrc = bm_h + frame_at(t + 1) * int64_t(D) * DV;
 #pragma unroll
     for (int cw = 0; cw < C::CW; ++cw)
@@ -299,23 +351,38 @@ scan_bf16_kernel(const uint16_t* __restrict__ ainv_planes, const float* __restri
     *rs_out(buf, cw, 1) = make_uint2(l01, l23);
   };
 
-  // R_0 = lam * 0 + Bm_0
+  // R of the segment's first step: lam X_prev + Bm with X_prev = 0 (the text step, and the local
+  // pass's zero starts), the chunk's true start state (rerun), or lam I for a transition
 #pragma unroll
   for (int cw = 0; cw < C::CW; ++cw) {
-    const float4 b4 = *reinterpret_cast<const float4*>(bm_h + blk_index(row0, c0 + 16 * cw + n, D));
-    write_r(0, cw, b4.x, b4.y, b4.z, b4.w);
+    const int col = c0 + 16 * cw + n;
+    float4 r4;
+    if (MODE == kSegLocal && transition) {
+      r4 = make_float4(row0 == col ? lam : 0.0f, row0 + 1 == col ? lam : 0.0f, row0 + 2 == col ? lam : 0.0f,
+                       row0 + 3 == col ? lam : 0.0f);
+    } else {
+      r4 = *reinterpret_cast<const float4*>(bm_h + frame_at(s_begin) * int64_t(D) * DV + blk_index(row0, col, D));
+      if constexpr (MODE == kSegRerun) {
+        const float4 x4 = *reinterpret_cast<const float4*>(ch.starts + (chain * ch.nchunks + j) * int64_t(D) * DV +
+                                                           blk_index(row0, col, D));
+        r4 = make_float4(__builtin_fmaf(lam, x4.x, r4.x), __builtin_fmaf(lam, x4.y, r4.y),
+                         __builtin_fmaf(lam, x4.z, r4.z), __builtin_fmaf(lam, x4.w, r4.w));
+      }
+    }
+    write_r(0, cw, r4.x, r4.y, r4.z, r4.w);
   }
-  stage_a(0);
+  stage_a(s_begin);
   commit_a(0);
-  stage_a(1);
+  stage_a(s_begin + 1);
   commit_a(1);
-  load_bm(0, Bv[0]);
+  load_bm(s_begin, Bv[0]);
   __syncthreads();
   frags_a(0, A[0]);
 
-  auto step = [&](int64_t s, uint4 (&a)[C::KS][2], float4 (&bv)[C::CW], uint4 (&a_fill)[C::KS][2],
+  // r: the step's index within the segment (its LDS buffers and register slots alternate)
+  auto step = [&](int64_t s, int64_t r, uint4 (&a)[C::KS][2], float4 (&bv)[C::CW], uint4 (&a_fill)[C::KS][2],
                   float4 (&bv_fill)[C::CW]) {
-    const int buf = int(s & 1);
+    const int buf = int(r & 1);
     stage_a(s + 2);  // lands during this step; goes to the LDS buffer that held step s
     load_bm(s + 1, bv_fill);
     // every R fragment of the step in one LDS round trip, then the MFMA chains
@@ -340,7 +407,26 @@ scan_bf16_kernel(const uint16_t* __restrict__ ainv_planes, const float* __restri
       }
       x[cw] = hh + (hl + lh);
     }
-    if (s >= 1) {
+    if constexpr (MODE == kSegLocal) {
+      if (s == s_end) {
+        // the segment's end state, float32: the true start of chunk 1 (chunk 0), C_j, or P_j
+        if (transition) {
+          float* dst = ch.pc + (chain * ch.nchunks + j) * int64_t(D) * D;
+#pragma unroll
+          for (int cw = 0; cw < C::CW; ++cw)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) dst[(row0 + q) * D + c0 + 16 * cw + n] = x[cw][q];
+        } else {
+          float* dst = (j == 0 ? ch.starts + (chain * ch.nchunks + 1) * int64_t(D) * DV
+                               : ch.cc + (chain * ch.nchunks + j) * int64_t(D) * DV);
+#pragma unroll
+          for (int cw = 0; cw < C::CW; ++cw)
+            *reinterpret_cast<float4*>(dst + blk_index(row0, c0 + 16 * cw + n, D)) =
+                make_float4(x[cw][0], x[cw][1], x[cw][2], x[cw][3]);
+        }
+      }
+    }
+    if (store_all && s >= 1) {
       // The states leave the chain only for the readout, which rounds their mean to bf16
       // for its MFMA: they are stored as bf16 in the readout's operand order (state_index),
       // a lane's 4 rows as 8 bytes, and kept out of the caches.
@@ -360,7 +446,7 @@ scan_bf16_kernel(const uint16_t* __restrict__ ainv_planes, const float* __restri
               reinterpret_cast<u32x2*>(dst + state_index(srow0, c0 + 16 * cw + n, D)));
       }
     }
-    if (s < F) {
+    if (s < s_end) {
 #pragma unroll
       for (int cw = 0; cw < C::CW; ++cw)
         write_r(buf ^ 1, cw, __builtin_fmaf(lam, x[cw][0], bv[cw].x), __builtin_fmaf(lam, x[cw][1], bv[cw].y),
@@ -373,13 +459,94 @@ scan_bf16_kernel(const uint16_t* __restrict__ ainv_planes, const float* __restri
     __syncthreads();
   };
 
-  for (int64_t s0 = 0; s0 <= F; s0 += C::NSLOT) {
+  const int64_t nsteps = s_end - s_begin + 1;
+  for (int64_t r0 = 0; r0 < nsteps; r0 += C::NSLOT) {
 #pragma unroll
     for (int u = 0; u < C::NSLOT; ++u) {
-      if (s0 + u > F) break;
-      step(s0 + u, A[u], Bv[u], A[(u + C::NSLOT - 1) % C::NSLOT], Bv[(u + C::NSLOT - 1) % C::NSLOT]);
+      if (r0 + u >= nsteps) break;
+      step(s_begin + r0 + u, r0 + u, A[u], Bv[u], A[(u + C::NSLOT - 1) % C::NSLOT],
+           Bv[(u + C::NSLOT - 1) % C::NSLOT]);
     }
   }
+}
+
+// The chunked scan's carry pass: for every chain, the true start states of chunks 2..K-1 from
+// that of chunk 1, X_{j+1} = P_j X_j + C_j for j = 1..K-2, in float32 on the 16x16x4 float32
+// MFMA.  One workgroup per chain and 16-column slice of X (d/16 waves of 16 rows each); the
+// right operand goes through LDS.
+template <int D, int DV>
+__global__ void __launch_bounds__(kThreads)
+chunk_carry_kernel(ChunkArgs ch, int64_t nchains) {
+  constexpr int RB = D / 16, NW = RB < 4 ? RB : 4, RBW = RB / NW, NCB = DV / 16;
+  __shared__ __align__(16) float rs[D * 16];  // X_j, this workgroup's 16 columns: [row block][g][col][r]
+  const int64_t chain = blockIdx.x / NCB;
+  const int cb = int(blockIdx.x % NCB);
+  if (chain >= nchains) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const bool active = wave < NW;
+  const int c0 = cb * 16;
+  const int64_t K = ch.nchunks;
+  auto rs_at = [&](int jb) -> float* { return rs + ((jb * 4 + g) * 16 + n) * 4; };
+  float* st = ch.starts + chain * K * int64_t(D) * DV;
+  if (active) {
+#pragma unroll
+    for (int i = 0; i < RBW; ++i) {
+      const int row = (wave * RBW + i) * 16 + 4 * g;
+      *reinterpret_cast<float4*>(rs_at(wave * RBW + i)) =
+          *reinterpret_cast<const float4*>(st + 1 * int64_t(D) * DV + blk_index(row, c0 + n, D));
+    }
+  }
+  __syncthreads();
+  for (int64_t jj = 1; jj + 1 < K; ++jj) {
+    f32x4 acc[RBW];
+    if (active) {
+      const float* P = ch.pc + (chain * K + jj) * int64_t(D) * D;
+#pragma unroll
+      for (int i = 0; i < RBW; ++i) acc[i] = f32x4{};
+#pragma unroll
+      for (int jb = 0; jb < RB; ++jb) {
+        const float4 rr = *reinterpret_cast<const float4*>(rs_at(jb));
+#pragma unroll
+        for (int i = 0; i < RBW; ++i) {
+          const int row = (wave * RBW + i) * 16 + n;
+          const float4 a = *reinterpret_cast<const float4*>(P + row * D + 16 * jb + 4 * g);
+          acc[i] = mfma16_f32(a.x, rr.x, acc[i]);
+          acc[i] = mfma16_f32(a.y, rr.y, acc[i]);
+          acc[i] = mfma16_f32(a.z, rr.z, acc[i]);
+          acc[i] = mfma16_f32(a.w, rr.w, acc[i]);
+        }
+      }
+    }
+    __syncthreads();  // every wave has read X_j
+    if (active) {
+      const float* Cj = ch.cc + (chain * K + jj) * int64_t(D) * DV;
+#pragma unroll
+      for (int i = 0; i < RBW; ++i) {
+        const int row = (wave * RBW + i) * 16 + 4 * g;
+        const int idx = blk_index(row, c0 + n, D);
+        const float4 c4 = *reinterpret_cast<const float4*>(Cj + idx);
+        const float4 x4 = make_float4(acc[i][0] + c4.x, acc[i][1] + c4.y, acc[i][2] + c4.z, acc[i][3] + c4.w);
+        *reinterpret_cast<float4*>(st + (jj + 1) * int64_t(D) * DV + idx) = x4;
+        *reinterpret_cast<float4*>(rs_at(wave * RBW + i)) = x4;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// The chunk summaries' place in the plan's chunk workspace: P_j, C_j and the start states,
+// [2BH][K] of each.
+template <int D, int DV>
+ChunkArgs chunk_args(const Problem& p) {
+  const int64_t nchains = 2 * p.B * p.H, K = (p.F + p.scan_chunk - 1) / p.scan_chunk;
+  ChunkArgs ch;
+  ch.len = p.scan_chunk;
+  ch.nchunks = K;
+  ch.pc = p.chunk_ws;
+  ch.cc = ch.pc + nchains * K * int64_t(D) * D;
+  ch.starts = ch.cc + nchains * K * int64_t(D) * DV;
+  return ch;
 }
 
 template <int D, int DV>
@@ -387,17 +554,49 @@ hipError_t launch_scan_t(const Problem& p, hipStream_t s, bool prepare) {
   const int64_t nchains = 2 * p.B * p.H;
   if (p.bf16) {
     using C = ScanBf16Cfg<D, DV>;
-    auto kern = scan_bf16_kernel<D, DV>;
-    if (prepare)
-      return C::LDS_BYTES > 65536 ? hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                                        hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                        C::LDS_BYTES)
-                                  : hipSuccess;
-    const int64_t grid = ((nchains + kXcds - 1) / kXcds) * kXcds * C::NCB;
-    launch_kernel(p, kern, dim3(unsigned(grid)), dim3(C::THREADS), C::LDS_BYTES, s,
-                  reinterpret_cast<const uint16_t*>(p.ainv), p.bm, p.xf, p.xb, nchains, p.F,
-                  p.lam, grid,
-                  p.states_f32 ? kStoreF32 : (p.fp8 && D >= 64) ? kStorePairedBf16 : kStoreBf16);
+    auto kern = scan_bf16_kernel<D, DV, kSegSerial>;
+    auto kern_local = scan_bf16_kernel<D, DV, kSegLocal>;
+    auto kern_rerun = scan_bf16_kernel<D, DV, kSegRerun>;
+    if (prepare) {
+      if (C::LDS_BYTES <= 65536) return hipSuccess;
+      for (const void* k : {reinterpret_cast<const void*>(kern), reinterpret_cast<const void*>(kern_local),
+                            reinterpret_cast<const void*>(kern_rerun)}) {
+        const hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
+        if (e != hipSuccess) return e;
+      }
+      return hipSuccess;
+    }
+    const int store = p.states_f32 ? kStoreF32 : (p.fp8 && D >= 64) ? kStorePairedBf16 : kStoreBf16;
+    const int64_t K = p.scan_chunk > 0 ? (p.F + p.scan_chunk - 1) / p.scan_chunk : 1;
+    const auto planes = reinterpret_cast<const uint16_t*>(p.ainv);
+    if (K < 2 || p.chunk_ws == nullptr) {
+      const int64_t grid = ((nchains + kXcds - 1) / kXcds) * kXcds * C::NCB;
+      launch_kernel(p, kern, dim3(unsigned(grid)), dim3(C::THREADS), C::LDS_BYTES, s, planes, p.bm, p.xf, p.xb,
+                    nchains, p.F, p.lam, grid, store, ChunkArgs{});
+      return hipGetLastError();
+    }
+    // chunked: local pass, carry pass (K > 2), rerun; the stage's timing events go on the
+    // first and the last launch
+    const ChunkArgs ch = chunk_args<D, DV>(p);
+    Problem first = p, mid = p, last = p;
+    first.ev_stop = nullptr;
+    mid.ev_start = mid.ev_stop = nullptr;
+    last.ev_start = nullptr;
+    const int64_t groups = ((nchains * (K - 1) + kXcds - 1) / kXcds) * kXcds;
+    const int64_t grid_local = groups * (C::NCB + D / 32);
+    launch_kernel(first, kern_local, dim3(unsigned(grid_local)), dim3(C::THREADS), C::LDS_BYTES, s, planes, p.bm,
+                  p.xf, p.xb, nchains, p.F, p.lam, grid_local, store, ch);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (K > 2) {
+      launch_kernel(mid, chunk_carry_kernel<D, DV>, dim3(unsigned(nchains * (DV / 16))), dim3(kThreads), 0, s, ch,
+                    nchains);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    const int64_t grid_rerun = groups * C::NCB;
+    launch_kernel(last, kern_rerun, dim3(unsigned(grid_rerun)), dim3(C::THREADS), C::LDS_BYTES, s, planes, p.bm,
+                  p.xf, p.xb, nchains, p.F, p.lam, grid_rerun, store, ch);
   } else {
     using C = ScanCfg<D, DV>;
     if (prepare) return hipSuccess;  // static LDS only

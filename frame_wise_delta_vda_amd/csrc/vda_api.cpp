@@ -25,6 +25,9 @@ struct vda_plan_s {
   // set once a forward pass (whole, or its statistics stage) has been enqueued: the backward
   // pass reads the statistics it leaves in the workspace
   bool has_statistics;
+  // the chunked scan's workspace (vda_plan_set_scan_chunk)
+  void* chunk_workspace;
+  size_t chunk_workspace_bytes;
 };
 
 namespace {
@@ -178,6 +181,8 @@ vda_status vda_plan_create(int64_t B, int64_t H, int64_t F, int64_t n, int64_t d
   plan->bwd_workspace = nullptr;
   plan->bwd_workspace_bytes = 0;
   plan->has_statistics = false;
+  plan->chunk_workspace = nullptr;
+  plan->chunk_workspace_bytes = 0;
   // kernel attributes once, here, so that a forward pass makes no runtime call but launches
   if (vda::prepare_stats(p) != hipSuccess || vda::prepare_scan(p) != hipSuccess ||
       vda::prepare_readout(p) != hipSuccess ||
@@ -186,6 +191,14 @@ vda_status vda_plan_create(int64_t B, int64_t H, int64_t F, int64_t n, int64_t d
     if (plan->workspace != nullptr) (void)hipFree(plan->workspace);
     delete plan;
     return VDA_ERROR_DEVICE;
+  }
+  // the scan the plan runs by default: chunked only where the serial chains leave most of the
+  // GPU idle
+  const vda_status cs = vda_plan_set_scan_chunk(plan, VDA_SCAN_CHUNK_AUTO);
+  if (cs != VDA_SUCCESS) {
+    if (plan->workspace != nullptr) (void)hipFree(plan->workspace);
+    delete plan;
+    return cs;
   }
   *plan_out = plan;
   return VDA_SUCCESS;
@@ -203,12 +216,51 @@ vda_status vda_plan_destroy(vda_plan_t plan) {
   free_timing(plan);
   if (plan->workspace != nullptr) check(hipFree(plan->workspace));
   if (plan->bwd_workspace != nullptr) check(hipFree(plan->bwd_workspace));
+  if (plan->chunk_workspace != nullptr) check(hipFree(plan->chunk_workspace));
   delete plan;
   return st;
 }
 
 size_t vda_plan_workspace_bytes(vda_plan_t plan) {
-  return plan == nullptr ? 0 : plan->workspace_bytes + plan->bwd_workspace_bytes;
+  return plan == nullptr ? 0
+                         : plan->workspace_bytes + plan->bwd_workspace_bytes + plan->chunk_workspace_bytes;
+}
+
+vda_status vda_plan_set_scan_chunk(vda_plan_t plan, int64_t chunk_frames) {
+  if (plan == nullptr || chunk_frames < VDA_SCAN_CHUNK_AUTO) return VDA_ERROR_INVALID_VALUE;
+  vda::Problem& p = plan->p;
+  if (chunk_frames > 0 && !p.bf16) return VDA_ERROR_NOT_SUPPORTED;
+  if (chunk_frames == VDA_SCAN_CHUNK_AUTO) chunk_frames = vda::auto_scan_chunk(p);
+  const size_t bytes = vda::chunk_workspace_bytes(p, chunk_frames);
+  if (plan->chunk_workspace != nullptr) {
+    const hipError_t e = hipFree(plan->chunk_workspace);
+    plan->chunk_workspace = nullptr;
+    plan->chunk_workspace_bytes = 0;
+    p.chunk_ws = nullptr;
+    p.scan_chunk = 0;
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      return VDA_ERROR_DEVICE;
+    }
+  }
+  p.scan_chunk = 0;
+  if (bytes == 0) return VDA_SUCCESS;  // one chunk: the serial scan
+  void* ws = nullptr;
+  if (hipMalloc(&ws, bytes) != hipSuccess || ws == nullptr) {
+    (void)hipGetLastError();
+    return VDA_ERROR_OUT_OF_MEMORY;
+  }
+  plan->chunk_workspace = ws;
+  plan->chunk_workspace_bytes = bytes;
+  p.chunk_ws = static_cast<float*>(ws);
+  p.scan_chunk = chunk_frames;
+  return VDA_SUCCESS;
+}
+
+vda_status vda_plan_get_scan_chunk(vda_plan_t plan, int64_t* chunk_frames) {
+  if (plan == nullptr || chunk_frames == nullptr) return VDA_ERROR_INVALID_VALUE;
+  *chunk_frames = plan->p.scan_chunk;
+  return VDA_SUCCESS;
 }
 
 vda_status vda_debug_workspace(vda_plan_t plan, const void** ainv, const void** bm,
@@ -444,6 +496,7 @@ vda_status vda_backward(vda_plan_t plan, const void* q, const void* k, const voi
   // The forward states again, in float32 (the forward pass keeps them in bf16): the scan on
   // the forward's statistics with float32 state stores.
   vda::Problem px = p;
+  px.scan_chunk = 0;  // the backward pass's chains run serially
   px.states_f32 = true;
   px.xf = f32(L.xf);
   px.xb = f32(L.xb);
@@ -470,6 +523,7 @@ vda_status vda_backward(vda_plan_t plan, const void* q, const void* k, const voi
   mark(kEvScanBegin);
   if (!fused_dq && e == hipSuccess) e = vda::launch_scan(px, s);
   vda::Problem ps = p;
+  ps.scan_chunk = 0;
   ps.states_f32 = true;
   ps.bm = f32(L.dw);
   ps.xf = f32(L.sf);

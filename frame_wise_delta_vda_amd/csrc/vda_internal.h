@@ -28,16 +28,45 @@ struct Problem {
   float* bm;        // [BH][F+1][d][dv]
   float* xf;        // [BH][F][d][dv]; bf16 plans: bf16 elements in state_index order
   float* xb;        // [BH][F][d][dv]; likewise
-  // when set, the one kernel a forward stage launches records these around itself, inside its
-  // dispatch (per-stage timing without separate event packets between the kernels)
+  // bfloat16 path: chain steps per chunk of the chunked scan (0: the serial scan), and its
+  // workspace of chunk summaries (float32, [2BH][K] of d*d + 2*d*dv, K = ceil(F / scan_chunk))
+  int64_t scan_chunk = 0;
+  float* chunk_ws = nullptr;
+  // when set, the kernel a forward stage launches (the first and last of them, for a stage of
+  // several launches) records these around itself, inside its dispatch (per-stage timing
+  // without separate event packets between the kernels)
   hipEvent_t ev_start = nullptr, ev_stop = nullptr;
 };
+
+// Chunk length the plan chooses by itself: the chunked scan only where the serial chains
+// leave most compute units idle (their workgroups fill at most a quarter of them) and are long
+// (at least 48 frames: below that its two extra launches cost about what the shorter chains
+// save), with about as many chunks as fill the compute units in the local pass, at most 8 (the
+// carry pass is serial over the chunks).  0: the serial scan.
+inline int64_t auto_scan_chunk(const Problem& p) {
+  if (!p.bf16 || p.F < 48 || p.num_cus <= 0) return 0;
+  const int64_t nchains = 2 * p.B * p.H;
+  const int64_t serial_wgs = nchains * (p.dv / 32);
+  if (serial_wgs * 4 > p.num_cus) return 0;
+  int64_t k = (p.num_cus + nchains * (p.dv / 32 + p.d / 32) / 2) / (nchains * (p.dv / 32 + p.d / 32)) + 1;
+  const int64_t kmax = p.F / 4 < 8 ? p.F / 4 : 8;
+  k = k < 2 ? 2 : k > kmax ? kmax : k;
+  return (p.F + k - 1) / k;
+}
+
+// Bytes of the chunked scan's workspace for chunks of `chunk` chain steps (0 when the scan is
+// serial: chunk == 0 or a single chunk).
+inline size_t chunk_workspace_bytes(const Problem& p, int64_t chunk) {
+  if (chunk <= 0 || p.F <= chunk) return 0;
+  const size_t K = size_t((p.F + chunk - 1) / chunk);
+  return size_t(2 * p.B * p.H) * K * size_t(p.d * p.d + 2 * p.d * p.dv) * sizeof(float);
+}
 
 // Launch a kernel of a forward stage, with the stage's timing events if the problem carries them.
 template <typename K, typename... Args>
 inline void launch_kernel(const Problem& p, K kern, dim3 grid, dim3 block, uint32_t lds, hipStream_t s,
                           Args... args) {
-  if (p.ev_start != nullptr)
+  if (p.ev_start != nullptr || p.ev_stop != nullptr)
     hipExtLaunchKernelGGL(kern, grid, block, lds, s, p.ev_start, p.ev_stop, 0u, args...);
   else
     hipLaunchKernelGGL(kern, grid, block, lds, s, args...);

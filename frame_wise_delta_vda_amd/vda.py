@@ -25,6 +25,7 @@ VDA_SUCCESS, VDA_ERROR_INVALID_VALUE, VDA_ERROR_NOT_SUPPORTED = 0, 1, 2
 VDA_ERROR_MISALIGNED, VDA_ERROR_OUT_OF_MEMORY, VDA_ERROR_DEVICE = 3, 4, 5
 VDA_ERROR_TOO_LARGE = 6
 VDA_NOALLOC_SCRATCH_BYTES = 64 << 20
+VDA_SCAN_CHUNK_AUTO = -1
 VDA_STAGE_STATS, VDA_STAGE_SCAN, VDA_STAGE_READOUT, VDA_STAGE_ALL = 1, 2, 4, 7
 
 
@@ -77,6 +78,10 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.vda_plan_timings.restype = c_int
     lib.vda_forward_noalloc.argtypes = [c_i64] * 7 + [ctypes.c_float, c_int] + [c_vp] * 7
     lib.vda_forward_noalloc.restype = c_int
+    lib.vda_plan_set_scan_chunk.argtypes = [c_vp, c_i64]
+    lib.vda_plan_set_scan_chunk.restype = c_int
+    lib.vda_plan_get_scan_chunk.argtypes = [c_vp, ctypes.POINTER(c_i64)]
+    lib.vda_plan_get_scan_chunk.restype = c_int
     if path is None:
         _lib = lib
     return lib
@@ -155,6 +160,18 @@ def vda_forward_stages(plan, stages, q, k, v, text_k, text_v, out, stream=None):
     _check(load_library().vda_forward_stages(plan, stages, _ptr(q), _ptr(k), _ptr(v), _ptr(text_k),
                                              _ptr(text_v), _ptr(out), _stream(stream)),
            "vda_forward_stages")
+
+
+def vda_plan_set_scan_chunk(plan, chunk_frames: int):
+    """0: serial scans; > 0: the chunked scan with chunks of that many frames;
+    VDA_SCAN_CHUNK_AUTO: the plan's own choice (include/vda.h)."""
+    _check(load_library().vda_plan_set_scan_chunk(plan, chunk_frames), "vda_plan_set_scan_chunk")
+
+
+def vda_plan_get_scan_chunk(plan) -> int:
+    c = ctypes.c_int64()
+    _check(load_library().vda_plan_get_scan_chunk(plan, ctypes.byref(c)), "vda_plan_get_scan_chunk")
+    return c.value
 
 
 def vda_plan_destroy(plan):
@@ -251,6 +268,14 @@ class Plan:
 
     def debug_workspace(self):
         return vda_debug_workspace(self.handle)
+
+    def set_scan_chunk(self, chunk_frames: int):
+        vda_plan_set_scan_chunk(self.handle, chunk_frames)
+
+    @property
+    def scan_chunk(self) -> int:
+        """Frames per chunk of the chunked scan, 0 for the serial scan."""
+        return vda_plan_get_scan_chunk(self.handle)
 
     def enable_timing(self, capacity: int):
         vda_plan_enable_timing(self.handle, capacity)

@@ -87,10 +87,42 @@ typedef enum {
  *   lambda: the regulariser, finite and > 0, shared by the text and every frame.
  *   dtype: element types of the tensors (vda_dtype).
  * The plan allocates its workspace (hipMalloc, one block) on the current device and
- * keeps it until vda_plan_destroy.  On error *plan_out is set to NULL.
+ * keeps it until vda_plan_destroy.  Its scans start in the automatic mode of
+ * vda_plan_set_scan_chunk (the chunked scan for few heads and many frames, which allocates
+ * its chunk summaries here too).  On error *plan_out is set to NULL.
  * Errors: INVALID_VALUE, NOT_SUPPORTED, OUT_OF_MEMORY, DEVICE. */
 vda_status vda_plan_create(int64_t B, int64_t H, int64_t F, int64_t n, int64_t d, int64_t dv,
                            int64_t T, float lambda, vda_dtype dtype, vda_plan_t* plan_out);
+
+/* Choose how the forward pass runs its state scans (row f1 of the hot path: a chunked
+ * scan over the frames, the composition of the affine step X -> lam A_f^{-1} X + A_f^{-1} B_f
+ * being associative).  chunk_frames == 0 runs each chain serially over its F + 1 steps.
+ * chunk_frames > 0 splits each chain into K = ceil(F / chunk_frames) chunks of that many
+ * frames and runs three passes: every chunk from a zero state, together with its transition
+ * P_j = product of lam A_f^{-1} over its frames, in parallel; the true start of every chunk,
+ * serially over the K chunk ends (X_{j+1} = P_j X_j + C_j, in float32); and every chunk again
+ * from its true start, writing the states.  The result is that of the serial scan up to
+ * rounding (the same bar against the oracle).  It pays where the serial chains leave the GPU
+ * idle -- few heads per GPU, as in a head-sharded share of the problem -- and costs about
+ * three times the scan's work where they do not (measured on one MI355X: 768p with 3 heads,
+ * scan 0.137 -> 0.094 ms; the long clip with 3 heads, 0.533 -> 0.250 ms; the long clip with
+ * 24 heads, 0.745 -> 1.21 ms or more).
+ * chunk_frames == VDA_SCAN_CHUNK_AUTO (the choice every plan starts with) takes the chunked
+ * scan only when the serial chains' workgroups (2*B*H*dv/32 of them) fill at most a quarter of
+ * the GPU's compute units and F >= 48, with K = the number of chunks whose local pass about
+ * fills the compute units (2 <= K <= min(8, F/4)); otherwise the serial scan.
+ * The plan allocates the chunk summaries here (hipMalloc; 2*B*H*K*(d*d + 2*d*dv) floats, none
+ * when the scan is serial) and frees any earlier ones; the forward calls then allocate nothing.
+ * Call it with no pass of the plan in flight.  The backward pass always runs its chains
+ * serially.
+ * Errors: INVALID_VALUE (NULL plan, chunk_frames < VDA_SCAN_CHUNK_AUTO), NOT_SUPPORTED
+ * (chunk_frames > 0 on a float32 plan), OUT_OF_MEMORY, DEVICE. */
+#define VDA_SCAN_CHUNK_AUTO (-1)
+vda_status vda_plan_set_scan_chunk(vda_plan_t plan, int64_t chunk_frames);
+
+/* The chunk length the plan's forward passes use: 0 for the serial scan, else frames per
+ * chunk (the automatic choice resolved).  Errors: INVALID_VALUE (NULL argument). */
+vda_status vda_plan_get_scan_chunk(vda_plan_t plan, int64_t* chunk_frames);
 
 /* Enqueue the whole forward pass on `stream` (a hipStream_t; NULL is the null
  * stream) and return without waiting.  Arguments are checked on the host before
@@ -213,7 +245,8 @@ vda_status vda_plan_timings(vda_plan_t plan, int* calls, float* stats_ms, float*
 vda_status vda_plan_destroy(vda_plan_t plan);
 
 /* Bytes of device workspace the plan holds (0 for NULL): the forward workspace, plus the
- * backward workspace once vda_backward has allocated it. */
+ * backward workspace once vda_backward has allocated it, plus the chunked scan's summaries
+ * (vda_plan_set_scan_chunk). */
 size_t vda_plan_workspace_bytes(vda_plan_t plan);
 
 /* Static, human-readable name of a status code. */

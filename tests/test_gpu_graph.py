@@ -17,6 +17,7 @@ pytestmark = pytest.mark.gpu
     (2, dict(H=2, F=4, n=200, T=9)),                  # bf16 d = dv = 64
     (1, dict(H=2, F=3, n=100, T=16)),                 # fp32 d = dv = 32
     (6, dict(H=2, F=5, n=333, T=20)),                 # FP8 inputs, d = dv = 128
+    (3, dict(H=1, F=50, n=64, T=8)),                  # one head, 50 frames: the chunked scan
 ])
 def test_forward_replays_in_a_graph(idx, over):
     w = W.WORKLOADS[idx].replace(name=f"graph_{idx}", **over)

@@ -269,17 +269,30 @@ def test_intermediates_match_oracle(name, w):
         f"max state error {xerr:.3e}")
 
 
-# Conditioning range of the explicit inverse and the split-bf16 chain: rank-16 keys with 0.05
-# noise at the ill-conditioned workload's frame shape, lam from the workload's 0.1 down.  The
-# smaller lam, the larger the condition number of lam I + K^T K: about 1.7e3 at 0.1, 3.8e3 at
-# 0.03, 5.8e3 at 0.01 and 7.6e3 at 0.001 (the noise floor of K^T K bounds it near 8e3).
-CONDITIONING_LAMBDAS = [0.1, 0.03, 0.01, 0.001]
+# Conditioning range of the explicit inverse and the split-bf16 chain: rank-16 keys at the
+# ill-conditioned workload's frame shape (n = 2016, d = dv = 128), lam from the workload's 0.1
+# down, and less full-rank noise in the keys (the workload's is 0.05) to go further.  The
+# condition number of lam I + K^T K is about 1.7e3 at (0.05, 0.1), 3.8e3 at (0.05, 0.03), 5.8e3
+# at (0.05, 0.01), 7.6e3 at (0.05, 0.001) -- the noise floor of K^T K bounds it near 8e3 -- then
+# 3.9e4 at (0.02, 0.001), 1.0e5 at (0.01, 0.001) and 5.5e5 at (0.005, 1e-4).
+_BEYOND = ("outside the verified conditioning range: the float32 inverse and the split-bf16 chain "
+           "keep the 1e-2 bar up to condition numbers near 1e4 (5.2e-3 at 8.2e3); measured on one "
+           "MI355X at this case: ")
+CONDITIONING = [
+    (0.05, 0.1), (0.05, 0.03), (0.05, 0.01), (0.05, 0.001),
+    pytest.param(0.02, 0.001, marks=pytest.mark.skip(reason=_BEYOND + "condition number 4.3e4, error 2.0e-2")),
+    pytest.param(0.01, 0.001, marks=pytest.mark.skip(reason=_BEYOND + "condition number 1.1e5, error 1.0e-1")),
+    pytest.param(0.005, 1e-4, marks=pytest.mark.skip(reason=_BEYOND + "condition number 5.7e5, error 8.4e-1")),
+]
 
 
-@pytest.mark.parametrize("lam", CONDITIONING_LAMBDAS)
-def test_conditioning_range(lam):
-    w = W.WORKLOADS[5].replace(name=f"lowrank_lam_{lam}", B=1, H=2, F=6, T=64, seed=500, lam=lam)
-    say(f"[gpu] conditioning lam={lam}")
+@pytest.mark.parametrize("noise,lam", CONDITIONING,
+                         ids=["noise0.05_lam0.1", "noise0.05_lam0.03", "noise0.05_lam0.01", "noise0.05_lam0.001",
+                              "noise0.02_lam0.001", "noise0.01_lam0.001", "noise0.005_lam0.0001"])
+def test_conditioning_range(noise, lam):
+    w = W.WORKLOADS[5].replace(name=f"lowrank_noise{noise}_lam{lam}", B=1, H=2, F=6, T=64, seed=500,
+                               lam=lam, noise=noise)
+    say(f"[gpu] conditioning noise={noise} lam={lam}")
     arrays = W.full_storage(w, threads=1)
     out, plan = run_gpu(w, to_device(w, arrays))
     plan.close()
@@ -288,7 +301,7 @@ def test_conditioning_range(lam):
         x = W.head_float64(w, 0, h)
         for f in range(w.F):
             kappa = max(kappa, np.linalg.cond(lam * np.eye(w.d) + x["k"][f].T @ x["k"][f]))
-    say(f"  lam={lam}: max condition number {kappa:.3g}")
+    say(f"  noise={noise} lam={lam}: max condition number {kappa:.3g}")
     _check_heads(w, out, [(0, h) for h in range(w.H)])
 
 

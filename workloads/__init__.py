@@ -17,7 +17,8 @@ with ``seed`` the workload's seed; all draws are float32 in this order:
   text_k ~ N(0,1) [T,d];  text_v ~ N(0,1) [T,dv].
 * low-rank ("ill-conditioned") workloads:  m ~ N(0,1) [dv,d] once per (b,h); then per
   frame f = 0..F-1 in order: u_f ~ N(0,1) [n,r], w_f ~ N(0,1) [r,d], e_f ~ N(0,1) [n,d],
-  z_f ~ N(0,1) [n,dv], with k_f = rownorm(u_f w_f / sqrt(r) + 0.05 e_f) and
+  z_f ~ N(0,1) [n,dv], with k_f = rownorm(u_f w_f / sqrt(r) + s e_f) (s = 0.05 unless a
+  workload states another noise level) and
   v_f = k_f m^T + 0.1 z_f (float32, before any rounding); then q ~ N(0,1) [F,n,d],
   text_k ~ N(0,1) [T,d], text_v ~ N(0,1) [T,dv].
 
@@ -55,6 +56,7 @@ class Workload:
     seed: int
     kind: str = "gaussian"  # "gaussian" or "lowrank"
     rank: int = 16
+    noise: float = 0.05     # low-rank workloads: relative size of the full-rank noise in k
     grid: Optional[tuple] = None  # spatial token grid (rows, cols), informational
 
     @property
@@ -101,6 +103,12 @@ WORKLOADS: Dict[int, Workload] = {
     # the 768p shape with FP8 (e4m3) inputs and a bfloat16 output
     6: Workload("768p_fp8", B=1, H=24, F=90, n=4032, d=128, dv=128, T=256, lam=1.0,
                 dtype="fp8", seed=6, grid=(84, 48)),
+    # one GPU's share of the 768p and long-clip shapes when 8 GPUs split the 24 heads: 3 heads
+    # each, every frame (the shape a head-sharded layout gives each GPU)
+    7: Workload("768p_shard8_bf16", B=1, H=3, F=90, n=4032, d=128, dv=128, T=256, lam=1.0,
+                dtype="bf16", seed=7, grid=(84, 48)),
+    8: Workload("long_clip_shard8_bf16", B=1, H=3, F=360, n=1024, d=128, dv=128, T=256, lam=1.0,
+                dtype="bf16", seed=8, grid=(32, 32)),
 }
 
 
@@ -190,7 +198,7 @@ def head_float32(w: Workload, b: int, h: int) -> Dict[str, np.ndarray]:
             wf = g.standard_normal((w.rank, d), dtype=np.float32)
             e = g.standard_normal((n, d), dtype=np.float32)
             z = g.standard_normal((n, dv), dtype=np.float32)
-            kf = _rownorm((u @ wf) * scale + np.float32(0.05) * e)
+            kf = _rownorm((u @ wf) * scale + np.float32(w.noise) * e)
             k[f] = kf
             v[f] = kf @ m.T + np.float32(0.1) * z
         q = g.standard_normal((F, n, d), dtype=np.float32)
