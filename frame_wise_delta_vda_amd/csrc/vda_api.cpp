@@ -76,9 +76,11 @@ vda_status make_problem(int64_t B, int64_t H, int64_t F, int64_t n, int64_t d, i
   // a frame (or the text) is addressed with 32-bit byte offsets
   if (n > kMaxFrameTokens || T > kMaxFrameTokens) return VDA_ERROR_NOT_SUPPORTED;
 
-  // Every element count the kernels index must fit in int64; grids are 1-D.
-  int64_t bh, frames, tok, elems, ws_frames, ws_elems, tmp;
-  if (!mul_ok(B, H, &bh) || !mul_ok(bh, F + 1, &ws_frames) || !mul_ok(bh, F, &frames) ||
+  // Every element count the kernels index must fit in int64; grids are 1-D.  F + 1 (the frames
+  // with the text) must itself fit.
+  int64_t bh, frames, tok, elems, ws_frames, ws_elems, tmp, f1;
+  if (__builtin_add_overflow(F, int64_t(1), &f1)) return VDA_ERROR_INVALID_VALUE;
+  if (!mul_ok(B, H, &bh) || !mul_ok(bh, f1, &ws_frames) || !mul_ok(bh, F, &frames) ||
       !mul_ok(frames, n, &tok) || !mul_ok(tok, 128, &elems) || !mul_ok(bh, T, &tmp) ||
       !mul_ok(tmp, 128, &tmp))
     return VDA_ERROR_INVALID_VALUE;

@@ -1,8 +1,14 @@
 // Internal interface between the C ABI layer (vda_api.cpp) and the HIP kernels.
 #pragma once
 
+// The kernel sources (HIP language mode) get the launch helper below; the C ABI layer is plain
+// host C++ and needs only the runtime API.
+#if defined(__HIP__)
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
+#else
+#include <hip/hip_runtime_api.h>
+#endif
 #include <cstddef>
 #include <cstdint>
 
@@ -62,6 +68,7 @@ inline size_t chunk_workspace_bytes(const Problem& p, int64_t chunk) {
   return size_t(2 * p.B * p.H) * K * size_t(p.d * p.d + 2 * p.d * p.dv) * sizeof(float);
 }
 
+#if defined(__HIP__)
 // Launch a kernel of a forward stage, with the stage's timing events if the problem carries them.
 template <typename K, typename... Args>
 inline void launch_kernel(const Problem& p, K kern, dim3 grid, dim3 block, uint32_t lds, hipStream_t s,
@@ -71,6 +78,7 @@ inline void launch_kernel(const Problem& p, K kern, dim3 grid, dim3 block, uint3
   else
     hipLaunchKernelGGL(kern, grid, block, lds, s, args...);
 }
+#endif
 
 // Validates a problem shape (the checks of vda_plan_create) and fills *out with it, no
 // workspace attached; *workspace_bytes is what the forward pass needs (vda_api.cpp).
