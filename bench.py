@@ -212,8 +212,21 @@ def run(args):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    # per-stage durations of the timed passes themselves: the library brackets every
-    # launch with HIP events on the stream it runs on
+    names = ["stats", "scan", "readout"]
+    bits = {"stats": binding.VDA_STAGE_STATS, "scan": binding.VDA_STAGE_SCAN, "readout": binding.VDA_STAGE_READOUT}
+    # per-stage breakdown, outside the timed region: K passes with every stage's kernel timed by
+    # the library's HIP events (recorded by each launch itself, on the launch stream)
+    plan.enable_timing(args.steps)
+    for _ in range(args.steps):
+        step()
+    calls, st_ms, sc_ms, rd_ms = plan.timings()
+    if calls != args.steps:
+        raise RuntimeError(f"timed {calls} of {args.steps} passes")
+    kern_ms = {"stats": st_ms, "scan": sc_ms, "readout": rd_ms}
+    dom = max(("stats", "readout"), key=lambda n: kern_ms[n])
+    # the timed region: K whole passes, with only the dominant kernel carrying its events (each
+    # timed stage adds an event pair to a pass), for its live duration
+    plan.set_timed_stages(bits[dom])
     plan.enable_timing(args.steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -222,21 +235,22 @@ def run(args):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
-    names = ["stats", "scan", "readout"]
-    calls, st_ms, sc_ms, rd_ms = plan.timings()
+    calls, *live = plan.timings()
     if calls != args.steps:
         raise RuntimeError(f"timed {calls} of {args.steps} passes")
-    kern_ms = {"stats": st_ms, "scan": sc_ms, "readout": rd_ms}
+    live_ms = dict(zip(names, live))[dom]
     print(f"[bench] {w.name}: {ms_step:.3f} ms/step; " +
-          ", ".join(f"{n} {kern_ms[n]:.3f} ms" for n in names), file=sys.stderr, flush=True)
+          ", ".join(f"{n} {kern_ms[n]:.3f} ms" for n in names) + f"; {dom} in the timed passes {live_ms:.3f} ms",
+          file=sys.stderr, flush=True)
 
     alg = algorithmic(w, args.gated)
     prof_name = w.name + ("_gated" if args.gated else "") + (f"_scan_chunk{args.scan_chunk}" if args.scan_chunk else "")
     traffic = read_traffic(prof_name)
     kernels = {}
+    kern_ms[dom] = live_ms  # the dominant kernel: its duration in the timed passes themselves
     for n in names:
         ms = kern_ms[n]
-        entry = {"ms": round(ms, 4)}
+        entry = {"ms": round(ms, 4), "timed": "live, in the timed passes" if n == dom else "breakdown passes"}
         if alg[n]["bytes"]:
             gbs = alg[n]["bytes"] / (ms * 1e-3) / 1e9
             entry.update({"alg_bytes": alg[n]["bytes"], "GB/s": round(gbs, 1),
@@ -248,7 +262,6 @@ def run(args):
         entry["mfma_frac"] = round(entry["TFLOP/s"] / peak, 4)
         entry["traffic"] = traffic.get(n)
         kernels[n] = entry
-    dom = max(("stats", "readout"), key=lambda n: kern_ms[n])
     ach = kernels[dom]["GB/s"]
     whole_gbs = w.algorithmic_bytes() / (ms_step * 1e-3) / 1e9
     roofline = {"kernel": dom, "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",

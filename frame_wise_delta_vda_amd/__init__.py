@@ -5,7 +5,7 @@ from .vda import (  # noqa: F401
     Plan, VdaError, load_library, declared_functions,
     vda_plan_create, vda_forward, vda_forward_stages, vda_forward_gated, vda_backward,
     vda_plan_destroy, vda_plan_workspace_bytes, vda_status_string, vda_debug_workspace,
-    vda_plan_enable_timing, vda_plan_timings, vda_forward_noalloc, vda_plan_set_scan_chunk, vda_plan_get_scan_chunk, VDA_SCAN_CHUNK_AUTO,
+    vda_plan_enable_timing, vda_plan_timings, vda_plan_set_timed_stages, vda_forward_noalloc, vda_plan_set_scan_chunk, vda_plan_get_scan_chunk, VDA_SCAN_CHUNK_AUTO,
     VDA_DTYPE_F32, VDA_DTYPE_BF16, VDA_DTYPE_FP8_E4M3, DTYPES,
     VDA_STAGE_STATS, VDA_STAGE_SCAN, VDA_STAGE_READOUT, VDA_STAGE_ALL, STATUS,
     VDA_SUCCESS, VDA_ERROR_INVALID_VALUE, VDA_ERROR_NOT_SUPPORTED, VDA_ERROR_MISALIGNED,

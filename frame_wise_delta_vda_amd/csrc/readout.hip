@@ -179,35 +179,37 @@ readout_bf16_kernel(const In* __restrict__ q, const uint16_t* __restrict__ xf,
 // Both products fold into the frame's state: O_f W_o^T = Q_f (W_f W_o^T), so per token the
 // epilogue is two readout products instead of one and O never leaves the registers.
 //  - Per frame the workgroup builds W_f^T = (X_fwd + X_bwd)^T / 2 in LDS (bf16, value
-//    feature rows), then every wave folds its share: W'_g = W_f W_g^T and W'_o = W_f W_o^T
-//    for its half of the output features, on the 16x16x32 MFMA with W_f as the A operand
-//    (transposing LDS reads) and the weight rows as B (16-byte loads).  The fold's A rows
-//    are taken in the order that leaves each lane's accumulators holding exactly the
-//    readout's operand fragments of W'^T (4 input features from each of two row tiles), so
-//    no lane exchange is needed.
-//  - Waves split 2 x 2: wave w takes tokens 16 (w % 2)..+15 of each 32-token tile and output
-//    features (DV / 2)(w / 2)..+DV/2-1, so the two folded matrices fit in the registers the
-//    plain readout uses for W.  Q is loaded as in the plain readout (the two waves of a
-//    token half read the same rows; the second read hits the caches).
-//  - Y goes through a wave-private LDS patch; a store instruction writes whole half rows.
+//    feature rows), then the four waves fold W'_o = W_f W_o^T and W'_g = W_f W_g^T on the
+//    16x16x32 MFMA, each wave a quarter of the output blocks, with W_f as the A operand
+//    (transposing LDS reads) and the weight rows as B (16-byte loads).  The fold's A rows are
+//    taken in the order that leaves each lane's accumulators holding exactly the readout's
+//    operand fragments of W'^T (4 input features from each of two row tiles), and the
+//    fragments go to LDS in fragment order (1 KB per fragment, lane-contiguous).
+//  - Every wave then copies all of W'_o into registers (the plain readout's W budget), and
+//    W'_g stays in LDS, read once per tile, conflict-free.
+//  - Waves split the tokens only, as in the plain readout: wave w takes tokens 16w..16w+15 of
+//    every 64-token tile and all output features, so each Q row is loaded once, two tiles
+//    ahead.
+//  - Y goes through a wave-private LDS patch (in the space W_f^T held during the fold), so
+//    a store instruction writes whole rows.
 template <int D, int DV>
 struct ReadGated {
-  static constexpr int TT = 32;                 // tokens per tile (16 per token half)
+  static constexpr int TT = 64;                 // tokens per tile (16 per wave)
   static constexpr int KS = D / 32;             // readout k-steps (input features)
-  static constexpr int FH = DV / 2;             // output features per wave
-  static constexpr int NBW = FH / 16;           // 16-feature output blocks per wave
+  static constexpr int NBF = DV / 16;           // 16-feature output blocks
   static constexpr int KC = DV / 32;            // fold k-steps (value features)
-  static constexpr int NT = D / 16;             // 16-row tiles of W' (input features)
-  static constexpr int NFR = (DV / 16) * KS;    // state fragments per frame
+  static constexpr int NFR = NBF * KS;          // fragments of one folded matrix (and of a state)
   static constexpr int WTROW = D + 8;           // bf16 per LDS row of W_f^T
   static constexpr int WT_BYTES = DV * WTROW * 2;
-  static constexpr int OWROW = FH + 8;          // bf16 per LDS row of a wave's Y patch
-  static constexpr int OCH = FH / 8;            // 16-byte chunks per half row
-  static constexpr int ORPI = 64 / OCH < 16 ? 64 / OCH : 16;  // rows per store instruction
+  static constexpr int FR_BYTES = NFR * 64 * 16;  // one folded matrix in fragment order
+  static constexpr int OWROW = DV + 8;          // bf16 per LDS row of a wave's Y patch
+  static constexpr int OCH = DV / 8;            // 16-byte chunks per output row
+  static constexpr int ORPI = 64 / OCH;         // output rows per wave store instruction
   static constexpr int OST = 16 / ORPI;         // store instructions per wave per tile
   static constexpr int OW_BYTES = 16 * OWROW * 2;
-  static constexpr int LDS_BYTES = WT_BYTES + 4 * OW_BYTES;
-  static_assert(NBW >= 1 && KC >= 1, "value width must be at least 32");
+  static constexpr int A_BYTES = cmax(WT_BYTES, 4 * OW_BYTES);  // W_f^T, later the Y patches
+  static constexpr int LDS_BYTES = A_BYTES + FR_BYTES + DV * 4;  // + folded W_g + the bias
+  static_assert(KC >= 1 && OST >= 1, "value width must be 32..128");
 };
 
 template <int D, int DV, typename In>
@@ -224,11 +226,11 @@ readout_gated_kernel(const In* __restrict__ q, const uint16_t* __restrict__ xf,
   constexpr int NQL = PAIR ? C::KS / 2 : C::KS;
   using QRaw = typename std::conditional<EB == 1 && !PAIR, uint2, uint4>::type;
   extern __shared__ __align__(16) unsigned char smem[];
-  uint16_t* wt = reinterpret_cast<uint16_t*>(smem);  // W_f^T [DV][WTROW]
+  uint16_t* wt = reinterpret_cast<uint16_t*>(smem);                      // W_f^T [DV][WTROW]
+  uint4* frg = reinterpret_cast<uint4*>(smem + C::A_BYTES);               // [NFR][64] fragments
+  float* bias_s = reinterpret_cast<float*>(smem + C::A_BYTES + C::FR_BYTES);  // [DV]
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int th = wave & 1, fh = wave >> 1;
-  uint16_t* ow = reinterpret_cast<uint16_t*>(smem + C::WT_BYTES + wave * C::OW_BYTES);
   const int c16 = lane & 15, g4 = lane >> 4;
   int64_t frame, t_first, tps;
   if (blockIdx.x < head_blocks) {
@@ -252,7 +254,8 @@ readout_gated_kernel(const In* __restrict__ q, const uint16_t* __restrict__ xf,
   };
 
   // ---- W_f^T = (X_fwd + X_bwd)^T / 2 into LDS: fragment (nb, ks) of the stored states
-  // holds rows 16 nb + lane % 16 of W^T and input features qmap(ks, lane / 16, 0..7)
+  // holds rows 16 nb + lane % 16 of W^T and input features qmap(ks, lane / 16, 0..7); and the
+  // head's gate bias
   {
     const uint4* sf = reinterpret_cast<const uint4*>(xf + frame * int64_t(D) * DV) + lane;
     const uint4* sb = reinterpret_cast<const uint4*>(xb + frame * int64_t(D) * DV) + lane;
@@ -261,75 +264,72 @@ readout_gated_kernel(const In* __restrict__ q, const uint16_t* __restrict__ xf,
       const uint4 m = mean_bf16x8(sf[fr * 64], sb[fr * 64]);
       *reinterpret_cast<uint4*>(wt + (16 * nb + c16) * C::WTROW + qmap(ks, g4, 0)) = m;
     }
+    for (int i = tid; i < DV; i += kThreads) bias_s[i] = b_gate[head * DV + i];
   }
   __syncthreads();
 
-  // ---- fold: wfr[0] = (W_f W_g^T)^T, wfr[1] = (W_f W_o^T)^T fragments of this wave's
-  // output blocks.  Row slot 16t + s of the fold's A operand is input feature
-  // qmap(t / 2, s / 4, 4 (t % 2) + s % 4), so lane (j, g) of accumulator tile t holds the
-  // features of slots 4 (t % 2) .. +3 of k-step t / 2 for lane group g: half a fragment.
-  uint4 wfr[2][C::NBW][C::KS];
-  {
-    // A operand from W_f^T by two transposing reads (ds_read_b64_tr_b16): lane L of a
-    // 16-lane group points at value feature (row) 32 kc + 8 g + L / 4 (+4) and input
-    // features qmap(t / 2, L % 4, 4 (t % 2)) .. +3, and receives 8 consecutive value
-    // features of input feature i(lane % 16).
-    auto fold_a = [&](int t, int kc) -> uint4 {
-      typedef short v4s __attribute__((ext_vector_type(4)));
-      typedef __attribute__((address_space(3))) v4s* lds_v4s;
-      const uint16_t* p = wt + (32 * kc + 8 * g4 + (c16 >> 2)) * C::WTROW + qmap(t >> 1, c16 & 3, 4 * (t & 1));
-      const v4s x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(p));
-      const v4s y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(p + 4 * C::WTROW));
-      const uint2 xl = __builtin_bit_cast(uint2, x), yl = __builtin_bit_cast(uint2, y);
-      return make_uint4(xl.x, xl.y, yl.x, yl.y);
-    };
+  // ---- fold of one weight matrix into the fragment region: fragment (jb, ks) of (W_f Wl^T)^T.
+  // Row slot 16t + s of the fold's A operand is input feature qmap(t / 2, s / 4, 4 (t % 2) + s % 4),
+  // so lane (j, g) of accumulator tile t holds the features of slots 4 (t % 2) .. +3 of k-step
+  // t / 2 for lane group g: half a fragment.  The A operand comes from W_f^T by two transposing
+  // reads (ds_read_b64_tr_b16): lane L of a 16-lane group points at value feature (row)
+  // 32 kc + 8 g + L / 4 (+4) and input features qmap(t / 2, L % 4, 4 (t % 2)) .. +3, and receives
+  // 8 consecutive value features of input feature i(lane % 16).
+  auto fold_a = [&](int t, int kc) -> uint4 {
+    typedef short v4s __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) v4s* lds_v4s;
+    const uint16_t* p = wt + (32 * kc + 8 * g4 + (c16 >> 2)) * C::WTROW + qmap(t >> 1, c16 & 3, 4 * (t & 1));
+    const v4s x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(p));
+    const v4s y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(p + 4 * C::WTROW));
+    const uint2 xl = __builtin_bit_cast(uint2, x), yl = __builtin_bit_cast(uint2, y);
+    return make_uint4(xl.x, xl.y, yl.x, yl.y);
+  };
+  auto fold = [&](const uint16_t* wl) {
+    for (int jb = wave; jb < C::NBF; jb += 4) {  // this wave's output blocks
+      const int j = 16 * jb + c16;               // output feature of this lane
+      uint4 bw[C::KC];
 #pragma unroll
-    for (int mtx = 0; mtx < 2; ++mtx) {
-      const uint16_t* wl = (mtx == 0 ? w_gate : w_out) + head * DV * DV;
+      for (int kc = 0; kc < C::KC; ++kc) bw[kc] = *reinterpret_cast<const uint4*>(wl + j * DV + 32 * kc + 8 * g4);
 #pragma unroll
-      for (int jb = 0; jb < C::NBW; ++jb) {
-        const int j = 16 * (fh * C::NBW + jb) + c16;  // output feature of this lane
-        uint4 bw[C::KC];
+      for (int ks = 0; ks < C::KS; ++ks) {
+        uint32_t wd[4];
 #pragma unroll
-        for (int kc = 0; kc < C::KC; ++kc)
-          bw[kc] = *reinterpret_cast<const uint4*>(wl + j * DV + 32 * kc + 8 * g4);
+        for (int h2 = 0; h2 < 2; ++h2) {
+          f32x4 acc = f32x4{};
 #pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) {
-          uint32_t wd[4];
-#pragma unroll
-          for (int h2 = 0; h2 < 2; ++h2) {
-            f32x4 acc = f32x4{};
-#pragma unroll
-            for (int kc = 0; kc < C::KC; ++kc) acc = mfma16_bf16(fold_a(2 * ks + h2, kc), bw[kc], acc);
-            wd[2 * h2] = pack_bf16x2(acc[0], acc[1]);
-            wd[2 * h2 + 1] = pack_bf16x2(acc[2], acc[3]);
-          }
-          wfr[mtx][jb][ks] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+          for (int kc = 0; kc < C::KC; ++kc) acc = mfma16_bf16(fold_a(2 * ks + h2, kc), bw[kc], acc);
+          wd[2 * h2] = pack_bf16x2(acc[0], acc[1]);
+          wd[2 * h2 + 1] = pack_bf16x2(acc[2], acc[3]);
         }
-        // compiler fence: re-read the A operands for the next block instead of keeping all
-        // of them live across the fold (which would not fit beside wfr)
-        asm volatile("" ::: "memory");
+        frg[(jb * C::KS + ks) * 64 + lane] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
       }
     }
-  }
-  float bias[C::NBW][4];
+  };
+  // W'_o first: every wave keeps all of it in registers
+  fold(w_out + head * DV * DV);
+  __syncthreads();
+  uint4 wo[C::NBF][C::KS];
 #pragma unroll
-  for (int jb = 0; jb < C::NBW; ++jb)
+  for (int jb = 0; jb < C::NBF; ++jb)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) bias[jb][r] = b_gate[head * DV + 16 * (fh * C::NBW + jb) + 4 * g4 + r];
+    for (int ks = 0; ks < C::KS; ++ks) wo[jb][ks] = frg[(jb * C::KS + ks) * 64 + lane];
+  __syncthreads();  // every wave has its copy before W'_g takes the region
+  fold(w_gate + head * DV * DV);
+  __syncthreads();  // W'_g complete; W_f^T no longer needed, its space holds the Y patches
+  uint16_t* ow = reinterpret_cast<uint16_t*>(smem + wave * C::OW_BYTES);
 
   auto wave_rows = [&](int64_t tok0) -> uint32_t {
     const int64_t r = n - tok0;
     return uint32_t(r < 0 ? 0 : (r < 16 ? r : 16));
   };
   auto load_q = [&](int64_t tile, QRaw (&dst)[NQL]) {
-    const int64_t tok0 = tile * C::TT + 16 * th;
+    const int64_t tok0 = tile * C::TT + 16 * wave;
     const auto rs = make_rsrc(q + (frame * n + tok0) * D, wave_rows(tok0) * D * EB);
 #pragma unroll
     for (int i = 0; i < NQL; ++i) {
-      if constexpr (PAIR) dst[i] = buffer_load16(rs, uint32_t(c16 * D + 16 * (g4 + 4 * i)));
-      else if constexpr (EB == 1) dst[i] = buffer_load8(rs, uint32_t(c16 * D + 32 * i + 8 * g4));
-      else dst[i] = buffer_load16(rs, uint32_t((c16 * D + 32 * i + 8 * g4) * 2));
+      if constexpr (PAIR) dst[i] = buffer_load16<kCacheNt>(rs, uint32_t(c16 * D + 16 * (g4 + 4 * i)));
+      else if constexpr (EB == 1) dst[i] = buffer_load8<kCacheNt>(rs, uint32_t(c16 * D + 32 * i + 8 * g4));
+      else dst[i] = buffer_load16<kCacheNt>(rs, uint32_t((c16 * D + 32 * i + 8 * g4) * 2));
     }
   };
   QRaw pfa[NQL], pfb[NQL];
@@ -337,7 +337,7 @@ readout_gated_kernel(const In* __restrict__ q, const uint16_t* __restrict__ xf,
   load_q(t_first + 1 < t_last ? t_first + 1 : t_first, pfb);
 
   auto step = [&](int64_t tile, QRaw (&pf)[NQL]) {
-    const int64_t tok0 = tile * C::TT + 16 * th;
+    const int64_t tok0 = tile * C::TT + 16 * wave;
     uint4 qf[C::KS];
 #pragma unroll
     for (int i = 0; i < NQL; ++i) {
@@ -351,31 +351,43 @@ readout_gated_kernel(const In* __restrict__ q, const uint16_t* __restrict__ xf,
       }
     }
     load_q(tile + 2 < t_last ? tile + 2 : t_last - 1, pf);
-    // Y^T block jb: the lane holds token c16, output features 16 (fh NBW + jb) + 4 g4 + 0..3
+    // Y^T block jb: the lane holds token c16, output features 16 jb + 4 g4 + 0..3; W'_g's
+    // fragments of the next block are read while this one multiplies
+    uint4 gcur[C::KS], gnxt[C::KS];
 #pragma unroll
-    for (int jb = 0; jb < C::NBW; ++jb) {
+    for (int ks = 0; ks < C::KS; ++ks) gcur[ks] = frg[ks * 64 + lane];
+#pragma unroll
+    for (int jb = 0; jb < C::NBF; ++jb) {
+      if (jb + 1 < C::NBF) {
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) gnxt[ks] = frg[((jb + 1) * C::KS + ks) * 64 + lane];
+      }
       f32x4 ga = f32x4{}, pa = f32x4{};
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
-        ga = mfma16_bf16(wfr[0][jb][ks], qf[ks], ga);
-        pa = mfma16_bf16(wfr[1][jb][ks], qf[ks], pa);
+        ga = mfma16_bf16(gcur[ks], qf[ks], ga);
+        pa = mfma16_bf16(wo[jb][ks], qf[ks], pa);
       }
+      const float4 b4 = *reinterpret_cast<const float4*>(bias_s + 16 * jb + 4 * g4);
+      const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
       float y[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        y[r] = pa[r] * __builtin_amdgcn_rcpf(1.0f + __expf(-(ga[r] + bias[jb][r])));
+      for (int r = 0; r < 4; ++r) y[r] = pa[r] * __builtin_amdgcn_rcpf(1.0f + __expf(-(ga[r] + bb[r])));
       *reinterpret_cast<uint2*>(ow + c16 * C::OWROW + 16 * jb + 4 * g4) =
           make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
+      if (jb + 1 < C::NBF) {
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) gcur[ks] = gnxt[ks];
+      }
     }
+    // the patch is private to this wave, whose LDS accesses complete in order
     const auto rs = make_rsrc(out + (frame * n + tok0) * DV, wave_rows(tok0) * DV * 2);
     const int orow = lane / C::OCH, och = lane % C::OCH;
-    if (orow < C::ORPI) {
 #pragma unroll
-      for (int j = 0; j < C::OST; ++j) {
-        const int r = orow + j * C::ORPI;
-        buffer_store16<kCacheStreamOut>(rs, uint32_t(r * DV * 2 + fh * C::FH * 2 + och * 16),
-                                        *reinterpret_cast<const uint4*>(ow + r * C::OWROW + och * 8));
-      }
+    for (int j = 0; j < C::OST; ++j) {
+      const int r = orow + j * C::ORPI;
+      buffer_store16<kCacheStreamOut>(rs, uint32_t(r * DV * 2 + och * 16),
+                                      *reinterpret_cast<const uint4*>(ow + r * C::OWROW + och * 8));
     }
   };
 
@@ -904,7 +916,15 @@ hipError_t launch_readout_gated_t(const Problem& p, const void* q, const GateWei
                                   hipStream_t s, bool prepare) {
   if (!p.bf16) return hipErrorInvalidValue;
   using C = ReadGated<D, DV>;
-  if (prepare) return hipSuccess;  // under 64 KB of LDS: no attribute to set
+  if (prepare) {
+    if (C::LDS_BYTES <= 65536) return hipSuccess;
+    for (const void* k : {reinterpret_cast<const void*>(readout_gated_kernel<D, DV, uint16_t>),
+                          reinterpret_cast<const void*>(readout_gated_kernel<D, DV, uint8_t>)}) {
+      const hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
   const ReadGrid gr = readout_grid(p.B * p.H * p.F, (p.n + C::TT - 1) / C::TT, p.num_cus);
   auto launch = [&](auto kern, auto in) {
     using In = decltype(in);
@@ -979,8 +999,13 @@ hipError_t launch_readout(const Problem& p, const void* q, void* out, hipStream_
 }
 
 hipError_t prepare_readout(const Problem& p) {
-#define VDA_CASE(DD, VV) \
-  if (p.d == DD && p.dv == VV) return launch_readout_t<DD, VV>(p, nullptr, nullptr, nullptr, true);
+  // the plain readout, and for bfloat16 and FP8 plans the gated one (above 64 KB of LDS)
+#define VDA_CASE(DD, VV)                                                                          \
+  if (p.d == DD && p.dv == VV) {                                                                   \
+    const hipError_t e = launch_readout_t<DD, VV>(p, nullptr, nullptr, nullptr, true);            \
+    if (e != hipSuccess || !p.bf16) return e;                                                      \
+    return launch_readout_gated_t<DD, VV>(p, nullptr, GateWeights{nullptr, nullptr, nullptr}, nullptr, nullptr, true); \
+  }
   VDA_CASE(32, 32) VDA_CASE(32, 64) VDA_CASE(32, 128)
   VDA_CASE(64, 32) VDA_CASE(64, 64) VDA_CASE(64, 128)
   VDA_CASE(128, 32) VDA_CASE(128, 64) VDA_CASE(128, 128)

@@ -277,17 +277,21 @@ scan_bf16_kernel(const uint16_t* __restrict__ ainv_planes, const float* __restri
   // 4-element reads of lanes a, a+4, a+8, a+12, so lane i points at row k + i/4 (+4 for
   // the second read) and columns 4(i%4)..+3 of the mirrored block, and receives column
   // i of 4 consecutive rows.
-  uint4 ast[C::APT];
-  auto stage_a = [&](int64_t t) {
+  // The planes travel HBM -> registers -> LDS: the loads of step s + 3 are issued at the start
+  // of step s into one of two register sets, and committed to LDS at the end of step s + 1,
+  // so each load has a whole step to land instead of being waited for in the step that
+  // issued it.
+  uint4 ast0[C::APT], ast1[C::APT];
+  auto stage_a = [&](int64_t t, uint4 (&dst)[C::APT]) {
     const auto rsrc = make_rsrc(ainv_h + frame_at(t) * int64_t(2 * D * D), uint32_t(C::APIECES * 16));
 #pragma unroll
-    for (int i = 0; i < C::APT; ++i) ast[i] = buffer_load16(rsrc, uint32_t((i * C::THREADS + tid) * 16));
+    for (int i = 0; i < C::APT; ++i) dst[i] = buffer_load16(rsrc, uint32_t((i * C::THREADS + tid) * 16));
   };
-  auto commit_a = [&](int b) {
+  auto commit_a = [&](int b, const uint4 (&src)[C::APT]) {
 #pragma unroll
     for (int i = 0; i < C::APT; ++i) {
       const int piece = i * C::THREADS + tid;  // whole waves fall on either side of the end
-      if (piece < C::APIECES) *reinterpret_cast<uint4*>(abuf + b * C::ABUF + piece * 8) = ast[i];
+      if (piece < C::APIECES) *reinterpret_cast<uint4*>(abuf + b * C::ABUF + piece * 8) = src[i];
     }
   };
   auto tr_frag = [&](const uint16_t* blk, int kh) -> uint4 {
@@ -371,19 +375,20 @@ scan_bf16_kernel(const uint16_t* __restrict__ ainv_planes, const float* __restri
     }
     write_r(0, cw, r4.x, r4.y, r4.z, r4.w);
   }
-  stage_a(s_begin);
-  commit_a(0);
-  stage_a(s_begin + 1);
-  commit_a(1);
+  stage_a(s_begin, ast0);
+  commit_a(0, ast0);
+  stage_a(s_begin + 1, ast0);
+  commit_a(1, ast0);
+  stage_a(s_begin + 2, ast0);  // committed at the end of the first step
   load_bm(s_begin, Bv[0]);
   __syncthreads();
   frags_a(0, A[0]);
 
   // r: the step's index within the segment (its LDS buffers and register slots alternate)
   auto step = [&](int64_t s, int64_t r, uint4 (&a)[C::KS][2], float4 (&bv)[C::CW], uint4 (&a_fill)[C::KS][2],
-                  float4 (&bv_fill)[C::CW]) {
+                  float4 (&bv_fill)[C::CW], uint4 (&as_issue)[C::APT], const uint4 (&as_commit)[C::APT]) {
     const int buf = int(r & 1);
-    stage_a(s + 2);  // lands during this step; goes to the LDS buffer that held step s
+    stage_a(s + 3, as_issue);  // committed at the end of the next step
     load_bm(s + 1, bv_fill);
     // every R fragment of the step in one LDS round trip, then the MFMA chains
     uint4 rf[C::CW][C::KS][2];
@@ -453,20 +458,19 @@ scan_bf16_kernel(const uint16_t* __restrict__ ainv_planes, const float* __restri
                 __builtin_fmaf(lam, x[cw][2], bv[cw].z), __builtin_fmaf(lam, x[cw][3], bv[cw].w));
     }
     // next step's fragments (its planes were committed before the last barrier), then the
-    // planes of step s+2 into the buffer whose fragments were taken a step ago
+    // planes of step s+2 (loaded during the last step) into the buffer whose fragments were
+    // taken a step ago
     frags_a(buf ^ 1, a_fill);
-    commit_a(buf);
+    commit_a(buf, as_commit);
     __syncthreads();
   };
 
+  static_assert(C::NSLOT == 2, "the plane registers alternate with the step's parity");
   const int64_t nsteps = s_end - s_begin + 1;
-  for (int64_t r0 = 0; r0 < nsteps; r0 += C::NSLOT) {
-#pragma unroll
-    for (int u = 0; u < C::NSLOT; ++u) {
-      if (r0 + u >= nsteps) break;
-      step(s_begin + r0 + u, r0 + u, A[u], Bv[u], A[(u + C::NSLOT - 1) % C::NSLOT],
-           Bv[(u + C::NSLOT - 1) % C::NSLOT]);
-    }
+  for (int64_t r0 = 0; r0 < nsteps; r0 += 2) {
+    step(s_begin + r0, r0, A[0], Bv[0], A[1], Bv[1], ast1, ast0);
+    if (r0 + 1 >= nsteps) break;
+    step(s_begin + r0 + 1, r0 + 1, A[1], Bv[1], A[0], Bv[0], ast0, ast1);
   }
 }
 

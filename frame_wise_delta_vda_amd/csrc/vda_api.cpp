@@ -18,6 +18,7 @@ struct vda_plan_s {
   // timing_capacity calls; timed_calls counts the calls recorded since the last read.
   int timing_capacity;
   int timed_calls;
+  unsigned timed_stages;  // stages whose kernels record their events (vda_plan_set_timed_stages)
   hipEvent_t* timing_events;
   // backward-pass workspace, allocated by the first vda_backward call
   void* bwd_workspace;
@@ -179,6 +180,7 @@ vda_status vda_plan_create(int64_t B, int64_t H, int64_t F, int64_t n, int64_t d
   }
   plan->timing_capacity = 0;
   plan->timed_calls = 0;
+  plan->timed_stages = VDA_STAGE_ALL;
   plan->timing_events = nullptr;
   plan->bwd_workspace = nullptr;
   plan->bwd_workspace_bytes = 0;
@@ -337,10 +339,11 @@ vda_status enqueue_problem(const Problem& p, int device, unsigned stages, const 
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
-  // each stage is one kernel launch, which records the stage's two events itself
+  // each stage is one kernel launch (the chunked scan: the first and last of its launches),
+  // which records the stage's two events itself; a stage that is not timed has none
   auto timed = [&](int begin, int end) {
     vda::Problem ps = p;
-    if (tev != nullptr) {
+    if (tev != nullptr && tev[begin] != nullptr) {
       ps.ev_start = tev[begin];
       ps.ev_stop = tev[end];
     }
@@ -368,10 +371,19 @@ vda_status enqueue(vda_plan_t plan, unsigned stages, const void* q, const void* 
                    const void* text_k, const void* text_v, const vda::GateWeights* gate, void* out,
                    void* stream) {
   if (plan == nullptr) return VDA_ERROR_INVALID_VALUE;
-  // timing events of this call (whole passes only), or none
+  // timing events of this call (whole passes only, the timed stages' slots), or none
   hipEvent_t* tev = nullptr;
-  if (stages == VDA_STAGE_ALL && plan->timing_capacity > 0 && plan->timed_calls < plan->timing_capacity)
-    tev = plan->timing_events + size_t(plan->timed_calls) * kTimingEvents;
+  hipEvent_t slots[kTimingEvents] = {};
+  if (stages == VDA_STAGE_ALL && plan->timing_capacity > 0 && plan->timed_calls < plan->timing_capacity) {
+    hipEvent_t* ev = plan->timing_events + size_t(plan->timed_calls) * kTimingEvents;
+    const unsigned bits[3] = {VDA_STAGE_STATS, VDA_STAGE_SCAN, VDA_STAGE_READOUT};
+    for (int i = 0; i < 3; ++i)
+      if (plan->timed_stages & bits[i]) {
+        slots[2 * i] = ev[2 * i];
+        slots[2 * i + 1] = ev[2 * i + 1];
+      }
+    tev = slots;
+  }
   const vda_status st = vda::enqueue_problem(plan->p, plan->device, stages, q, k, v, text_k, text_v, gate,
                                              out, stream, tev);
   if (st != VDA_SUCCESS) return st;
@@ -492,8 +504,11 @@ vda_status vda_backward(vda_plan_t plan, const void* q, const void* k, const voi
   hipEvent_t* tev = nullptr;
   if (plan->timing_capacity > 0 && plan->timed_calls < plan->timing_capacity)
     tev = plan->timing_events + size_t(plan->timed_calls) * kTimingEvents;
+  const unsigned slot_stage[kTimingEvents] = {VDA_STAGE_STATS, VDA_STAGE_STATS, VDA_STAGE_SCAN, VDA_STAGE_SCAN,
+                                              VDA_STAGE_READOUT, VDA_STAGE_READOUT};
   auto mark = [&](int slot) {
-    if (tev != nullptr && e == hipSuccess) e = hipEventRecord(tev[slot], s);
+    if (tev != nullptr && e == hipSuccess && (plan->timed_stages & slot_stage[slot]))
+      e = hipEventRecord(tev[slot], s);
   };
   // The forward states again, in float32 (the forward pass keeps them in bf16): the scan on
   // the forward's statistics with float32 state stores.
@@ -602,6 +617,13 @@ vda_status vda_plan_enable_timing(vda_plan_t plan, int capacity) {
   return VDA_SUCCESS;
 }
 
+vda_status vda_plan_set_timed_stages(vda_plan_t plan, unsigned stages) {
+  if (plan == nullptr || (stages & ~unsigned(VDA_STAGE_ALL)) != 0) return VDA_ERROR_INVALID_VALUE;
+  if (plan->timed_calls != 0) return VDA_ERROR_INVALID_VALUE;  // read the recorded calls first
+  plan->timed_stages = stages;
+  return VDA_SUCCESS;
+}
+
 vda_status vda_plan_timings(vda_plan_t plan, int* calls, float* stats_ms, float* scan_ms,
                             float* readout_ms) {
   if (plan == nullptr || calls == nullptr) return VDA_ERROR_INVALID_VALUE;
@@ -612,7 +634,9 @@ vda_status vda_plan_timings(vda_plan_t plan, int* calls, float* stats_ms, float*
     const int spans[3][3] = {{kEvStatsBegin, kEvStatsEnd, 0},
                              {kEvScanBegin, kEvScanEnd, 1},
                              {kEvReadBegin, kEvReadEnd, 2}};
+    const unsigned bits[3] = {VDA_STAGE_STATS, VDA_STAGE_SCAN, VDA_STAGE_READOUT};
     for (const auto& sp : spans) {
+      if (!(plan->timed_stages & bits[sp[2]])) continue;  // not timed: reported as 0
       float ms = 0.0f;
       if (hipEventSynchronize(ev[sp[1]]) != hipSuccess ||
           hipEventElapsedTime(&ms, ev[sp[0]], ev[sp[1]]) != hipSuccess) {

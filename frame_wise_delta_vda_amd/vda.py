@@ -82,6 +82,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.vda_plan_set_scan_chunk.restype = c_int
     lib.vda_plan_get_scan_chunk.argtypes = [c_vp, ctypes.POINTER(c_i64)]
     lib.vda_plan_get_scan_chunk.restype = c_int
+    lib.vda_plan_set_timed_stages.argtypes = [c_vp, ctypes.c_uint]
+    lib.vda_plan_set_timed_stages.restype = c_int
     if path is None:
         _lib = lib
     return lib
@@ -194,6 +196,10 @@ def vda_plan_enable_timing(plan, capacity: int):
     _check(load_library().vda_plan_enable_timing(plan, capacity), "vda_plan_enable_timing")
 
 
+def vda_plan_set_timed_stages(plan, stages: int):
+    _check(load_library().vda_plan_set_timed_stages(plan, stages), "vda_plan_set_timed_stages")
+
+
 def vda_plan_timings(plan):
     """(calls, stats_ms, scan_ms, readout_ms) of the timed whole passes since the last read."""
     calls = ctypes.c_int()
@@ -279,6 +285,9 @@ class Plan:
 
     def enable_timing(self, capacity: int):
         vda_plan_enable_timing(self.handle, capacity)
+
+    def set_timed_stages(self, stages: int):
+        vda_plan_set_timed_stages(self.handle, stages)
 
     def timings(self):
         return vda_plan_timings(self.handle)

@@ -239,6 +239,13 @@ vda_status vda_forward_noalloc(int64_t B, int64_t H, int64_t F, int64_t n, int64
  * Errors: INVALID_VALUE (capacity < 0 or > 100000), OUT_OF_MEMORY, DEVICE. */
 vda_status vda_plan_enable_timing(vda_plan_t plan, int capacity);
 
+/* Which stages' kernels record their events in timed calls (a bitwise OR of vda_stage; the
+ * default is VDA_STAGE_ALL).  Each timed stage adds a pair of events to a pass; a benchmark that
+ * needs one stage's live duration can time that stage alone.  Stages not timed are reported as
+ * 0 ms by vda_plan_timings.  Errors: INVALID_VALUE (NULL plan, bits outside VDA_STAGE_ALL, or
+ * timed calls recorded and not yet read). */
+vda_status vda_plan_set_timed_stages(vda_plan_t plan, unsigned stages);
+
 /* Waits for the timed calls recorded since timing was enabled or last read, and returns
  * their number in *calls and the mean duration in milliseconds of each stage launch
  * (statistics, scan, readout).  Any of the float pointers may be NULL.  Resets the count.

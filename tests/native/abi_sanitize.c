@@ -87,6 +87,7 @@ int main(void) {
   int calls = 0;
   expect("timings NULL", vda_plan_timings(NULL, &calls, NULL, NULL, NULL), VDA_ERROR_INVALID_VALUE);
   expect("set chunk NULL", vda_plan_set_scan_chunk(NULL, 8), VDA_ERROR_INVALID_VALUE);
+  expect("timed stages NULL", vda_plan_set_timed_stages(NULL, 4), VDA_ERROR_INVALID_VALUE);
   int64_t chunk = 0;
   expect("get chunk NULL", vda_plan_get_scan_chunk(NULL, &chunk), VDA_ERROR_INVALID_VALUE);
 

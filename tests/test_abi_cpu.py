@@ -21,7 +21,7 @@ def test_every_declared_symbol_is_exported(lib):
                           "vda_plan_destroy",
                           "vda_plan_workspace_bytes", "vda_status_string", "vda_debug_workspace",
                           "vda_plan_enable_timing", "vda_plan_timings", "vda_forward_noalloc",
-                          "vda_plan_set_scan_chunk", "vda_plan_get_scan_chunk"}
+                          "vda_plan_set_scan_chunk", "vda_plan_get_scan_chunk", "vda_plan_set_timed_stages"}
     for name in names:
         assert hasattr(lib, name), name
 
@@ -75,6 +75,7 @@ def test_null_handles(lib):
     assert lib.vda_plan_set_scan_chunk(None, 8) == binding.VDA_ERROR_INVALID_VALUE
     c = ctypes.c_int64()
     assert lib.vda_plan_get_scan_chunk(None, ctypes.byref(c)) == binding.VDA_ERROR_INVALID_VALUE
+    assert lib.vda_plan_set_timed_stages(None, 4) == binding.VDA_ERROR_INVALID_VALUE
     calls = ctypes.c_int()
     assert lib.vda_plan_timings(None, ctypes.byref(calls), None, None, None) == \
         binding.VDA_ERROR_INVALID_VALUE
