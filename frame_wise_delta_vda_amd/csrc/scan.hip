@@ -383,6 +383,7 @@ scan_bf16_kernel(const uint16_t* __restrict__ ainv_planes, const float* __restri
   load_bm(s_begin, Bv[0]);
   __syncthreads();
   frags_a(0, A[0]);
+  __syncthreads();  // every wave has its first fragments before the first step overwrites buffer 0
 
   // r: the step's index within the segment (its LDS buffers and register slots alternate)
   auto step = [&](int64_t s, int64_t r, uint4 (&a)[C::KS][2], float4 (&bv)[C::CW], uint4 (&a_fill)[C::KS][2],
@@ -390,7 +391,10 @@ scan_bf16_kernel(const uint16_t* __restrict__ ainv_planes, const float* __restri
     const int buf = int(r & 1);
     stage_a(s + 3, as_issue);  // committed at the end of the next step
     load_bm(s + 1, bv_fill);
-    // every R fragment of the step in one LDS round trip, then the MFMA chains
+    // every R fragment of the step in one LDS round trip; then, so that their LDS traffic
+    // overlaps the MFMA chains, the next step's fragments (its planes were committed before the
+    // last barrier) and the planes of step s+2 (loaded during the last step) into the buffer
+    // whose fragments were taken before the last barrier
     uint4 rf[C::CW][C::KS][2];
 #pragma unroll
     for (int cw = 0; cw < C::CW; ++cw)
@@ -399,6 +403,8 @@ scan_bf16_kernel(const uint16_t* __restrict__ ainv_planes, const float* __restri
         rf[cw][ks][0] = *rs_frag(buf, cw, 0, ks);
         rf[cw][ks][1] = *rs_frag(buf, cw, 1, ks);
       }
+    frags_a(buf ^ 1, a_fill);
+    commit_a(buf, as_commit);
     __builtin_amdgcn_sched_barrier(0);
     f32x4 x[C::CW];
 #pragma unroll
@@ -457,11 +463,6 @@ scan_bf16_kernel(const uint16_t* __restrict__ ainv_planes, const float* __restri
         write_r(buf ^ 1, cw, __builtin_fmaf(lam, x[cw][0], bv[cw].x), __builtin_fmaf(lam, x[cw][1], bv[cw].y),
                 __builtin_fmaf(lam, x[cw][2], bv[cw].z), __builtin_fmaf(lam, x[cw][3], bv[cw].w));
     }
-    // next step's fragments (its planes were committed before the last barrier), then the
-    // planes of step s+2 (loaded during the last step) into the buffer whose fragments were
-    // taken a step ago
-    frags_a(buf ^ 1, a_fill);
-    commit_a(buf, as_commit);
     __syncthreads();
   };
 
