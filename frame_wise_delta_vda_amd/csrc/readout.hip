@@ -19,11 +19,14 @@ namespace {
 // bfloat16 path.  One workgroup per frame (or per equal part of a frame when there
 // are too few frames to fill the chip), so W is formed once per frame and the
 // workgroups that run together stream neighbouring frames.  Wave w of a workgroup
-// takes tokens 16w..16w+15 of every 64-token tile and works alone -- there is no
-// workgroup barrier at all:
-//  - at the start each wave forms all of its W^T operand fragments in registers from
-//    the two bf16 states, which the scan stores in exactly that operand order
-//    (state_index): one 16-byte load per state and fragment, mean in fp32, one rounding;
+// takes tokens 16w..16w+15 of every 64-token tile and, after one barrier at the start,
+// works alone:
+//  - at the start the four waves form the W^T operand fragments from the two bf16
+//    states, which the scan stores in exactly that operand order (state_index), a
+//    quarter each (one 16-byte load per state and fragment, mean in fp32, one
+//    rounding) into LDS; after the barrier every wave takes all of them into registers.
+//    Each state byte crosses into the compute unit once per workgroup, not once per
+//    wave (a quarter of the traffic, 1-2% of the readout at d = dv = 128);
 //  - the wave's Q rows are loaded straight into MFMA operands (lane: token l%16, eight
 //    consecutive features), two tiles ahead;
 //  - O^T = W^T Q^T goes through a wave-private LDS patch so the stores are whole rows
@@ -46,7 +49,9 @@ struct ReadBf16 {
   static constexpr int ORPI = 64 / OCH;         // output rows per wave store instruction
   static constexpr int OST = 16 / ORPI;         // store instructions per wave per tile
   static constexpr int OW_BYTES = 16 * OWROW * 2;  // per wave
-  static constexpr int LDS_BYTES = 4 * OW_BYTES;
+  static constexpr int NFR = NBF * KS;           // W^T fragments of a frame
+  static constexpr int WF_BYTES = NFR * 64 * 16;  // formed once per workgroup, shared through LDS
+  static constexpr int LDS_BYTES = 4 * OW_BYTES + WF_BYTES;
   static_assert(OST >= 1, "value width too large for one wave store pass");
 };
 
@@ -105,28 +110,21 @@ readout_bf16_kernel(const In* __restrict__ q, const uint16_t* __restrict__ xf,
   load_q(t_first + 1 < t_last ? t_first + 1 : t_first, pfb);
 
   // W = (X_fwd + X_bwd) / 2 of the frame, rounded once to bf16; fragment (nb, ks) of
-  // both states is the 1 KB at ((nb * KS + ks) * 64 + lane) * 8.  Two output blocks at a
-  // time, so the loads in flight stay within the registers.
+  // both states is the 1 KB at ((nb * KS + ks) * 64 + lane) * 8, and in LDS.  The early
+  // return above is the same for the whole workgroup, so every wave reaches the barrier.
   uint4 wfr[C::NBF][C::KS];  // W^T fragments: rows = output features, k = input features
   {
+    // each wave forms a quarter of the fragments into LDS (fragment order), then every wave
+    // takes all of them
+    uint4* wsm = reinterpret_cast<uint4*>(smem + 4 * C::OW_BYTES);
     const uint4* sf = reinterpret_cast<const uint4*>(xf + frame * int64_t(D) * DV) + lane;
     const uint4* sb = reinterpret_cast<const uint4*>(xb + frame * int64_t(D) * DV) + lane;
-    constexpr int NG = C::NBF >= 2 ? 2 : 1;
+    for (int fr = wave; fr < C::NFR; fr += 4) wsm[fr * 64 + lane] = mean_bf16x8(sf[fr * 64], sb[fr * 64]);
+    __syncthreads();
 #pragma unroll
-    for (int nb0 = 0; nb0 < C::NBF; nb0 += NG) {
-      uint4 a[NG][C::KS], b[NG][C::KS];
+    for (int nb = 0; nb < C::NBF; ++nb)
 #pragma unroll
-      for (int i = 0; i < NG; ++i)
-#pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) {
-          a[i][ks] = sf[((nb0 + i) * C::KS + ks) * 64];
-          b[i][ks] = sb[((nb0 + i) * C::KS + ks) * 64];
-        }
-#pragma unroll
-      for (int i = 0; i < NG; ++i)
-#pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) wfr[nb0 + i][ks] = mean_bf16x8(a[i][ks], b[i][ks]);
-    }
+      for (int ks = 0; ks < C::KS; ++ks) wfr[nb][ks] = wsm[(nb * C::KS + ks) * 64 + lane];
   }
 
   auto step = [&](int64_t tile, QRaw (&pf)[NQL]) {
