@@ -581,21 +581,30 @@ stats_bf16_kernel(const In* __restrict__ k, const In* __restrict__ v,
     // sweep) written out together: a workgroup's outputs leave in one burst, and each burst of
     // writes into the other workgroups' read stream costs read bandwidth.
     const int l32 = lane & 31;
+    // accumulator registers 4m..4m+3 of a lane are rows 4j..4j+3 of one column, which the
+    // blocked layout keeps as 4 consecutive floats: one 16-byte store each, and a store
+    // instruction writes two whole 512-byte pieces
     auto store_bm = [&] {
       if (wave < C::NV) {
+        const auto rs = make_rsrc(bmo, uint32_t(D * DV * 4));
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int e = 0; e < 16; ++e)
-            bmo[blk_index(32 * ((wave + i) & 3) + mfma32_row(e, lane), wave * 32 + l32, D)] = acc[3 + i][e];
+          for (int m = 0; m < 4; ++m) {
+            const f32x16& a = acc[3 + i];
+            const int off = blk_index(32 * ((wave + i) & 3) + mfma32_row(4 * m, lane), wave * 32 + l32, D);
+            buffer_store16<kCacheSc1>(rs, uint32_t(off * 4),
+                                      make_uint4(__float_as_uint(a[4 * m]), __float_as_uint(a[4 * m + 1]),
+                                                 __float_as_uint(a[4 * m + 2]), __float_as_uint(a[4 * m + 3])));
+          }
       }
     };
     if constexpr (!GRAM) {
       store_bm();
       return;
     }
+    // the frame's A^{-1} as two bf16 planes, hi then lo, each sym_blocks(D) 16 x 16 blocks
     uint16_t* hi_plane = reinterpret_cast<uint16_t*>(ainv + (bh * F1 + fi) * int64_t(D) * D);
-    uint16_t* lo_plane = hi_plane + sym_blocks(D) * 256;
     // G tiles (and the mirror of each off-diagonal one) -> LDS -> G row block in the
     // accumulator layout the sweep works on
     float* gsm = reinterpret_cast<float*>(smem);
@@ -626,21 +635,42 @@ stats_bf16_kernel(const In* __restrict__ k, const In* __restrict__ v,
     static_assert(6 * 16 * kPbs * 4 <= C::MAIN_BYTES, "sweep buffers exceed the staging area");
     sweep_neg_inverse_128(t, reinterpret_cast<float*>(smem), wave, lane);
     // A^{-1} is symmetric: lane l's column j of tile c is row j of A^{-1}, and its
-    // registers 4q..4q+3 are 4 consecutive columns of that row (8 bytes per plane).  Only
-    // the 16 x 16 blocks on and above the diagonal are stored (sym_index).
+    // registers 4q..4q+3 are columns 32 wave + 8q + 4h .. +3 of that row (h = lane / 32).
+    // Only the 16 x 16 blocks on and above the diagonal are stored (sym_index).  Lanes l and
+    // l + 32 trade a quarter-row so that each holds 8 consecutive columns (h = 0: columns
+    // 0..7 of a 16-column block, h = 1: 8..15): a store instruction then writes each plane's
+    // rows whole, two 512-byte blocks.
+    {
+      const auto rs = make_rsrc(hi_plane, uint32_t(2 * sym_blocks(D) * 256 * 2));
+      const int h = lane >> 5;
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
+      for (int c = 0; c < 4; ++c)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int row = 32 * c + l32, col = 32 * wave + 8 * q + 4 * (lane >> 5);
-        if ((row >> 4) > (col >> 4)) continue;
-        uint32_t h01, l01, h23, l23;
-        split_bf16x2(-t[c][4 * q + 0], -t[c][4 * q + 1], h01, l01);
-        split_bf16x2(-t[c][4 * q + 2], -t[c][4 * q + 3], h23, l23);
-        const int off = sym_index(row, col, D);
-        *reinterpret_cast<uint2*>(hi_plane + off) = make_uint2(h01, h23);
-        *reinterpret_cast<uint2*>(lo_plane + off) = make_uint2(l01, l23);
-      }
+        for (int qp = 0; qp < 2; ++qp) {
+          uint32_t hw[2][2], lw[2][2];  // [j][word]: columns 16 qp + 8 j + 4 h .. +3
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const int q = 2 * qp + j;
+            split_bf16x2(-t[c][4 * q + 0], -t[c][4 * q + 1], hw[j][0], lw[j][0]);
+            split_bf16x2(-t[c][4 * q + 2], -t[c][4 * q + 3], hw[j][1], lw[j][1]);
+          }
+          // h = 0 gives its columns 8..11 and takes the partner's 4..7; h = 1 gives 4..7 and
+          // takes 8..11
+          uint32_t rh[2], rl[2];
+#pragma unroll
+          for (int w2 = 0; w2 < 2; ++w2) {
+            rh[w2] = uint32_t(__shfl_xor(int(h ? hw[0][w2] : hw[1][w2]), 32));
+            rl[w2] = uint32_t(__shfl_xor(int(h ? lw[0][w2] : lw[1][w2]), 32));
+          }
+          const int row = 32 * c + l32, col = 32 * wave + 16 * qp + 8 * h;
+          if ((row >> 4) > (col >> 4)) continue;
+          const uint4 vh = h ? make_uint4(rh[0], rh[1], hw[1][0], hw[1][1]) : make_uint4(hw[0][0], hw[0][1], rh[0], rh[1]);
+          const uint4 vl = h ? make_uint4(rl[0], rl[1], lw[1][0], lw[1][1]) : make_uint4(lw[0][0], lw[0][1], rl[0], rl[1]);
+          const int off = sym_index(row, col, D);
+          buffer_store16<kCacheSc1>(rs, uint32_t(off * 2), vh);
+          buffer_store16<kCacheSc1>(rs, uint32_t((off + sym_blocks(D) * 256) * 2), vl);
+        }
+    }
     store_bm();
     return;
   }
