@@ -511,6 +511,9 @@ def summarize_counters(args):
                 (float(r["End_Timestamp"]) - float(r["Start_Timestamp"])) / 1e3
     print(f"# rocprofv3 counters per dispatch, {args.workload}{' gated' if args.gated else ''}")
     print(f"# command: {args.command}")
+    if args.workload.endswith("fp8") and any(c.startswith("MfmaFlops") for k in acc.values() for c in k):
+        print("# the statistics kernel's G and Bm run on the FP8 MFMA here, which neither MfmaFlopsBF16 nor "
+              "MfmaFlopsF32 counts (its F32 figure is the inverse's updates); MfmaUtil counts every MFMA type")
     counters = sorted({c for k in acc.values() for c in k})
     print(f"{'kernel':<58} " + " ".join(f"{c:>22}" for c in counters) + f" {'us':>9} {'derived':>s}")
     for name, cs in acc.items():
