@@ -75,16 +75,47 @@ def test_gated_small_shapes_parity(name, over):
     plan.close()
 
 
+def _check_every_head(w, out, g, arrays, threads=8):
+    """Every (b,h) slice of a full-size gated output against the oracle, from the stored inputs
+    (no regeneration); slices run on a thread pool with one BLAS thread each."""
+    import threadpoolctl
+    from concurrent.futures import ThreadPoolExecutor
+
+    g64 = W.gate_weights_float64(w, g)
+
+    def one(bh):
+        b, h = bh
+        x = {k: W.storage_to_float64(w, arrays[k][b, h]) for k in W.TENSORS}
+        ref = oracle.vda_forward_gated_head(x["q"], x["k"], x["v"], x["text_k"], x["text_v"], w.lam,
+                                            g64["w_gate"][h], g64["b_gate"][h], g64["w_out"][h])
+        got = out[b, h].float().cpu().numpy().astype(np.float64)
+        return bh, float(frame_errors(got, ref).max()), bool(np.all(np.isfinite(got)))
+
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    with threadpoolctl.threadpool_limits(limits=1, user_api="blas"), ThreadPoolExecutor(threads) as ex:
+        res = list(ex.map(one, heads))
+    worst_bh, worst, _ = max(res, key=lambda r: r[1])
+    say(f"  gated {w.name} B={w.B} H={w.H} F={w.F} n={w.n}: max rel err {worst:.3e} at (b,h)={worst_bh} "
+        f"over all {len(heads)} heads")
+    assert all(r[2] for r in res)
+    assert worst <= TOL[w.dtype], (worst, worst_bh)
+
+
 @pytest.mark.parametrize("idx", [3, 6])
-def test_gated_full_size_sampled_parity(idx):
+def test_gated_full_size_every_head_parity(idx):
+    """The gated pass at 768p (bfloat16 and FP8 inputs) in the launch configuration the
+    benchmark times; the oracle recomputes every (b,h) slice and every frame of it."""
     w = W.WORKLOADS[idx]
-    say(f"[gpu] gated full-size {w.name}")
+    say(f"[gpu] gated full-size {w.name}: generating inputs")
     g = W.gate_weights(w)
-    dev = to_device(w, W.full_storage(w))
+    arrays = W.full_storage(w)
+    dev = to_device(w, arrays)
+    say(f"[gpu] gated full-size {w.name}: running")
     out, plan = _run_gated(w, dev, _gate_to_device(g))
     del dev
-    _check(w, out, g, [(0, 0), (0, w.H // 2), (0, w.H - 1)])
     plan.close()
+    say(f"[gpu] gated full-size {w.name}: oracle on every head")
+    _check_every_head(w, out, g, arrays)
 
 
 def test_open_gate_with_identity_projection_is_the_plain_output():
