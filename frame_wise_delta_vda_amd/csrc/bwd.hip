@@ -69,62 +69,74 @@ __device__ __forceinline__ void frame_terms(const float* __restrict__ xf, const 
   const float* SB = sb + base;
   const int tid = threadIdx.x;
 
-  // 1. element-wise outputs straight from the (cached) inputs.  In the blocked layout four
-  //    consecutive rows of a column are one float4, so outputs that run along a row (WT and
-  //    the dB^T rows of Z: 8 consecutive value features of one input feature) are made for
-  //    4 rows x 8 columns at a time, and those that run down a column (DB2) 8 rows at a time.
+  // 1. element-wise outputs straight from the inputs, each adjoint state read once.  In the
+  //    blocked layout four consecutive rows of a column are one float4; a thread takes 4 rows x
+  //    8 columns and writes, from the same registers, the outputs that run along a row (WT and
+  //    the dB^T rows of Z: 8 consecutive value features of one input feature, 16 bytes) and its
+  //    half of those that run down a column (DB2: 8 consecutive rows of a column, 8 bytes of
+  //    the 16).  The forward states are read here only for WT (widths other than d = dv = 128).
   auto chunk_of = [](int row0, int col, int R) -> int {  // inverse of chunk_rc for an R-row state
     return (((col >> 4) * (R / 32) + (row0 >> 5)) * 4 + ((row0 & 31) >> 3)) * 16 + (col & 15);
   };
   uint16_t* dbf = db2 + fr * int64_t(2 * D) * DV;
   uint16_t* zf = z + fr * int64_t(C::ZR) * D;
+  const bool want_wt = wt != nullptr;
   for (int u = tid; u < (D / 4) * (DV / 8); u += kBwdThreads) {
     const int i0 = 4 * (u % (D / 4)), c0 = 8 * (u / (D / 4));
     float4 xf4[8], xb4[8], sf4[8], sb4[8];
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
       const int e = blk_index(i0, c0 + m, D) / 4;
-      xf4[m] = reinterpret_cast<const float4*>(XF)[e];
-      xb4[m] = reinterpret_cast<const float4*>(XB)[e];
       sf4[m] = reinterpret_cast<const float4*>(SF)[e];
       sb4[m] = reinterpret_cast<const float4*>(SB)[e];
     }
+    if (want_wt) {
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const int e = blk_index(i0, c0 + m, D) / 4;
+        xf4[m] = reinterpret_cast<const float4*>(XF)[e];
+        xb4[m] = reinterpret_cast<const float4*>(XB)[e];
+      }
+    }
     auto comp = [](const float4& a, int r) { return r == 0 ? a.x : r == 1 ? a.y : r == 2 ? a.z : a.w; };
+    float db[4][8];  // dB = (S_bwd + S_fwd) / 2 at rows i0 + r, columns c0 + m
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int m = 0; m < 8; ++m) db[r][m] = 0.5f * (comp(sb4[m], r) + comp(sf4[m], r));
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      uint32_t w[4], h[4], l[4];
+      uint32_t h[4], l[4];
 #pragma unroll
       for (int m = 0; m < 8; m += 2) {
-        w[m / 2] = pack_bf16x2(0.5f * (comp(xf4[m], r) + comp(xb4[m], r)),
-                               0.5f * (comp(xf4[m + 1], r) + comp(xb4[m + 1], r)));
-        const float a = 0.5f * (comp(sb4[m], r) + comp(sf4[m], r));
-        const float b = 0.5f * (comp(sb4[m + 1], r) + comp(sf4[m + 1], r));
-        h[m / 2] = pack_bf16x2(a, b);
-        l[m / 2] = pack_bf16x2(lo_part(a), lo_part(b));
+        h[m / 2] = pack_bf16x2(db[r][m], db[r][m + 1]);
+        l[m / 2] = pack_bf16x2(lo_part(db[r][m]), lo_part(db[r][m + 1]));
       }
-      // WT: rows c0.. (value features) of column i0 + r; Z rows 2D + c0.. (dB^T hi) and
-      // 2D + DV + c0.. (lo) of column i0 + r
-      if (wt != nullptr)
-        reinterpret_cast<uint4*>(wt + base)[chunk_of(c0, i0 + r, DV)] = make_uint4(w[0], w[1], w[2], w[3]);
+      // Z rows 2D + c0.. (dB^T hi) and 2D + DV + c0.. (lo) of column i0 + r
       reinterpret_cast<uint4*>(zf)[chunk_of(2 * D + c0, i0 + r, C::ZR)] = make_uint4(h[0], h[1], h[2], h[3]);
       reinterpret_cast<uint4*>(zf)[chunk_of(2 * D + DV + c0, i0 + r, C::ZR)] = make_uint4(l[0], l[1], l[2], l[3]);
-    }
-  }
-  for (int u = tid; u < (D / 8) * DV; u += kBwdThreads) {  // DB2: rows i0..i0+7 of column c, hi and lo
-    const int i0 = 8 * (u % (D / 8)), c = u / (D / 8);
-    const int e0 = blk_index(i0, c, D) / 4, e1 = blk_index(i0 + 4, c, D) / 4;
-    const float4 s0 = reinterpret_cast<const float4*>(SB)[e0], t0 = reinterpret_cast<const float4*>(SF)[e0];
-    const float4 s1 = reinterpret_cast<const float4*>(SB)[e1], t1 = reinterpret_cast<const float4*>(SF)[e1];
-    const float v[8] = {0.5f * (s0.x + t0.x), 0.5f * (s0.y + t0.y), 0.5f * (s0.z + t0.z), 0.5f * (s0.w + t0.w),
-                        0.5f * (s1.x + t1.x), 0.5f * (s1.y + t1.y), 0.5f * (s1.z + t1.z), 0.5f * (s1.w + t1.w)};
-    uint32_t h[4], l[4];
+      if (want_wt) {
+        uint32_t w[4];
 #pragma unroll
-    for (int m = 0; m < 8; m += 2) {
-      h[m / 2] = pack_bf16x2(v[m], v[m + 1]);
-      l[m / 2] = pack_bf16x2(lo_part(v[m]), lo_part(v[m + 1]));
+        for (int m = 0; m < 8; m += 2)
+          w[m / 2] = pack_bf16x2(0.5f * (comp(xf4[m], r) + comp(xb4[m], r)),
+                                 0.5f * (comp(xf4[m + 1], r) + comp(xb4[m + 1], r)));
+        // WT: rows c0.. (value features) of column i0 + r
+        reinterpret_cast<uint4*>(wt + base)[chunk_of(c0, i0 + r, DV)] = make_uint4(w[0], w[1], w[2], w[3]);
+      }
     }
-    reinterpret_cast<uint4*>(dbf)[chunk_of(i0, c, 2 * D)] = make_uint4(h[0], h[1], h[2], h[3]);
-    reinterpret_cast<uint4*>(dbf)[chunk_of(D + i0, c, 2 * D)] = make_uint4(l[0], l[1], l[2], l[3]);
+    // DB2 rows (i0 & ~7) .. +7 of column c0 + m, hi then lo: this thread's 4 rows are the
+    // first or the second 8 bytes of each chunk
+    const int half = (i0 >> 2) & 1;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const int c = c0 + m;
+      const uint2 hv = make_uint2(pack_bf16x2(db[0][m], db[1][m]), pack_bf16x2(db[2][m], db[3][m]));
+      const uint2 lv = make_uint2(pack_bf16x2(lo_part(db[0][m]), lo_part(db[1][m])),
+                                  pack_bf16x2(lo_part(db[2][m]), lo_part(db[3][m])));
+      reinterpret_cast<uint2*>(dbf)[2 * chunk_of(i0 & ~7, c, 2 * D) + half] = hv;
+      reinterpret_cast<uint2*>(dbf)[2 * chunk_of(D + (i0 & ~7), c, 2 * D) + half] = lv;
+    }
   }
 
   // 2. P = S_bwd X_fwd^T + S_fwd X_bwd^T (D x D) on the 32x32x16 bf16 MFMA with split
