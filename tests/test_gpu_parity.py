@@ -142,6 +142,43 @@ def test_readout_last_round_in_parts():
     plan.close()
 
 
+def test_longest_frame_sampled_parity():
+    """One frame of the most tokens the header allows, n = 2^24 - 256, at d = dv = 128: the
+    statistics kernel's frame-wide K and V descriptors then span 2^32 - 65536 bytes.  The
+    oracle computes the frame's state from all of its tokens; the output is compared on
+    sampled rows (both ends, the rows where K and V byte offsets cross 2^31, and 2048 seeded
+    random rows) by the relative Frobenius error over those rows."""
+    n = 16776960
+    w = W.WORKLOADS[3].replace(name="longest_frame", B=1, H=1, F=1, n=n, T=0, seed=901)
+    say(f"[gpu] longest frame n={n}: generating inputs")
+    arrays = W.full_storage(w)
+    dev = to_device(w, arrays)
+    dev["text_k"] = dev["text_v"] = None
+    say("[gpu] longest frame: running")
+    out, plan = run_gpu(w, dev)
+    plan.close()
+    del dev
+    rng = np.random.default_rng(901)
+    half = (1 << 31) // (2 * w.d)  # first token whose K row starts at byte 2^31
+    rows = np.unique(np.concatenate([np.arange(256), np.arange(half - 64, half + 64), np.arange(n - 300, n),
+                                     rng.integers(0, n, 2048)]))
+    got = out[0, 0, 0][torch.from_numpy(rows).cuda()].float().cpu().numpy().astype(np.float64)
+    del out
+    torch.cuda.empty_cache()
+    say("[gpu] longest frame: oracle")
+    k64 = W.storage_to_float64(w, arrays["k"][0, 0])
+    v64 = W.storage_to_float64(w, arrays["v"][0, 0])
+    empty_k, empty_v = np.zeros((0, w.d)), np.zeros((0, w.dv))
+    _, x_fwd, x_bwd = oracle.head_states(k64, v64, empty_k, empty_v, w.lam)
+    del k64, v64
+    q_rows = W.storage_to_float64(w, arrays["q"][0, 0, 0][rows])[None]
+    ref = oracle.readout(q_rows, x_fwd, x_bwd)[0]
+    err = float(np.sqrt(np.sum((got - ref) ** 2)) / np.sqrt(np.sum(ref ** 2)))
+    say(f"  longest frame: rel err {err:.3e} over {len(rows)} sampled rows")
+    assert np.all(np.isfinite(got))
+    assert err <= TOL[w.dtype], err
+
+
 def fetch_intermediates(w, plan):
     """The plan's workspace after a synchronised forward pass, as float64 row-major arrays:
     ainv [BH,F+1,d,d], bm [BH,F+1,d,dv], xf, xb [BH,F,d,dv] (layouts in include/vda.h)."""
