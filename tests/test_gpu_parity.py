@@ -179,6 +179,25 @@ def test_longest_frame_sampled_parity():
     assert err <= TOL[w.dtype], err
 
 
+@pytest.mark.parametrize("chunk", [0, binding.VDA_SCAN_CHUNK_AUTO])
+def test_long_chain_every_frame_parity(chunk):
+    """4000 frames of 37 tokens (a ragged part of one 64-token chunk) per head: chains of
+    4001 steps, run serially and with the automatic choice (chunked for so few heads), every
+    frame against the oracle.  The state must neither drift nor lose accuracy with the
+    length of the chain."""
+    w = W.WORKLOADS[3].replace(name="long_chain", B=1, H=2, F=4000, n=37, T=16, seed=902)
+    say(f"[gpu] long chain F={w.F}, scan chunk {chunk}")
+    dev = to_device(w, W.full_storage(w))
+    plan = binding.Plan(w.B, w.H, w.F, w.n, w.d, w.dv, w.T, w.lam, w.dtype)
+    plan.set_scan_chunk(chunk)
+    say(f"  scan chunk frames chosen: {plan.scan_chunk}")
+    if chunk != 0:
+        assert plan.scan_chunk > 0
+    out, _ = run_gpu(w, dev, plan=plan)
+    plan.close()
+    _check_heads(w, out, [(0, 0), (0, 1)])
+
+
 def fetch_intermediates(w, plan):
     """The plan's workspace after a synchronised forward pass, as float64 row-major arrays:
     ainv [BH,F+1,d,d], bm [BH,F+1,d,dv], xf, xb [BH,F,d,dv] (layouts in include/vda.h)."""
