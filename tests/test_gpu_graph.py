@@ -108,3 +108,51 @@ def test_gated_forward_and_backward_replay_in_graphs():
             assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"replay {i}"
     del graph
     plan.close()
+
+
+def test_noalloc_forward_replays_in_a_graph():
+    """vda_forward_noalloc, the entry point for callers that cannot allocate, launches kernels
+    only once its device is set up (on its first call): captured in a graph, every replay
+    equals vda_forward on a plan running the same serial scan, also after the inputs change
+    in place."""
+    w = W.WORKLOADS[3].replace(name="graph_noalloc", H=2, F=5, n=333, T=20, seed=41)
+    say("[gpu] graph replay noalloc")
+    dev = to_device(w, W.full_storage(w, threads=1))
+    plan = binding.Plan(w.B, w.H, w.F, w.n, w.d, w.dv, w.T, w.lam, w.dtype)
+    plan.set_scan_chunk(0)
+    eager, _ = run_gpu(w, dev, plan=plan)
+    out = torch.empty_like(eager)
+
+    def call():
+        binding.vda_forward_noalloc(w.B, w.H, w.F, w.n, w.d, w.dv, w.T, w.lam, w.dtype, dev["q"], dev["k"],
+                                    dev["v"], dev["text_k"], dev["text_v"], out)
+
+    call()  # sets the device up outside the capture
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), eager.view(torch.int16))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for i in range(3):
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {i}"
+    dev["v"].mul_(-0.5)
+    dev["q"].mul_(2.0)
+    ref2, _ = run_gpu(w, dev, plan=plan)
+    ref2 = ref2.clone()
+    for i in range(2):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref2.view(torch.int16)), f"replay after update {i}"
+    del g
+    plan.close()
