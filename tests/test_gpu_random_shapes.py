@@ -54,3 +54,52 @@ def test_random_shape_parity(w, chunk):
     out, _ = run_gpu(w, dev, plan=plan)
     plan.close()
     _check_heads(w, out, [(b, h) for b in range(w.B) for h in range(w.H)])
+
+
+def _epilogue_cases(count, seed, dtypes):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(count):
+        dtype = dtypes[int(rng.integers(len(dtypes)))]
+        d, dv = int(rng.choice([32, 64, 128])), int(rng.choice([32, 64, 128]))
+        w = W.WORKLOADS[2].replace(
+            name=f"rand_{seed}_{i:02d}", B=int(rng.integers(1, 3)), H=int(rng.integers(1, 3)),
+            F=int(rng.choice([1, 2, 3, 5, 8])), n=int(rng.choice([1, 31, 64, 65, 129, 200, 333])), d=d, dv=dv,
+            T=int(rng.choice([0, 1, 7, 64])), lam=float(rng.choice([0.1, 0.5, 1.0, 2.0])), dtype=dtype,
+            kind="lowrank" if rng.random() < 0.3 else "gaussian", seed=5000 + seed + i)
+        cases.append(w)
+    return cases
+
+
+GATED = _epilogue_cases(24, 11, ["bf16", "bf16", "fp8"])
+
+
+@pytest.mark.parametrize("w", GATED, ids=[w.name for w in GATED])
+def test_random_shape_gated_parity(w):
+    from test_gpu_gated import _check, _gate_to_device, _run_gated
+    say(f"[gpu] gated {w.name}: {w.dtype} B={w.B} H={w.H} F={w.F} n={w.n} d={w.d} dv={w.dv} T={w.T} "
+        f"lam={w.lam} {w.kind}")
+    g = W.gate_weights(w)
+    dev = to_device(w, W.full_storage(w, threads=1))
+    if w.T == 0:
+        dev["text_k"] = dev["text_v"] = None
+    out, plan = _run_gated(w, dev, _gate_to_device(g))
+    plan.close()
+    _check(w, out, g, [(b, h) for b in range(w.B) for h in range(w.H)])
+
+
+BACKWARD = _epilogue_cases(24, 12, ["bf16"])
+
+
+@pytest.mark.parametrize("w", BACKWARD, ids=[w.name for w in BACKWARD])
+def test_random_shape_backward_parity(w):
+    from test_gpu_backward import _bf16, _check, _d_out, _run_backward
+    say(f"[gpu] backward {w.name}: B={w.B} H={w.H} F={w.F} n={w.n} d={w.d} dv={w.dv} T={w.T} "
+        f"lam={w.lam} {w.kind}")
+    dev = to_device(w, W.full_storage(w, threads=1))
+    if w.T == 0:
+        dev["text_k"] = dev["text_v"] = None
+    dO = _d_out(w)
+    grads, plan = _run_backward(w, dev, _bf16(dO))
+    plan.close()
+    _check(w, grads, dO, [(b, h) for b in range(w.B) for h in range(w.H)])
