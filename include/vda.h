@@ -222,8 +222,10 @@ vda_status vda_backward(vda_plan_t plan, const void* q, const void* k, const voi
  * sets the kernels' attributes there (no allocation); later calls make no runtime call but
  * kernel launches.  Every call on a GPU uses that GPU's one array: calls that overlap in time on
  * one GPU (on different streams, or from different threads) race and give undefined results;
- * calls ordered on one stream are safe.  Results are bitwise those of vda_forward on a plan of
- * the same shape.  The output is complete when the stream reaches the end of the pass.
+ * calls ordered on one stream are safe.  The scans run serially, so results are bitwise those of
+ * vda_forward on a plan of the same shape running the serial scan (vda_plan_set_scan_chunk 0;
+ * a plan in the automatic mode that chose the chunked scan agrees up to rounding).  The output
+ * is complete when the stream reaches the end of the pass.
  * Errors: as vda_plan_create and vda_forward (but never OUT_OF_MEMORY), and TOO_LARGE. */
 vda_status vda_forward_noalloc(int64_t B, int64_t H, int64_t F, int64_t n, int64_t d, int64_t dv,
                                int64_t T, float lambda, vda_dtype dtype, const void* q,
